@@ -1,0 +1,305 @@
+/*
+ * moe.h -- C ABI of libmoe: a routed-expert MoE layer whose experts run
+ * straight from affine group-quantised int4/int8 weights on AMD gfx950.
+ *
+ * Page abbreviations in the citations:
+ *   [xix]    xix.ai, "Swiftlet Packs 80B Qwen Into Mac With 4.3GB Memory;
+ *            iPhone 17 to Run 35B Natively" (Korean; xix.ai/ru has the same
+ *            text in Russian).
+ *   [ttj]    ttj.kr article on Swiftlet, the MoE streaming runtime for Apple
+ *            devices.
+ *   [digest] paper-digest.app, "Swiftlet: Mac에서 80B Qwen을 4.3GB RAM으로,
+ *            iPhone에서 35B를 돌리는 런타임".
+ *   [lens]   agentlenshq.com, "Swiftletは低RAM使用量でMacとiPhone上で35Bおよび
+ *            80B Qwenモデルを可能にする".
+ *
+ * Conventions for every call:
+ *   - Returns int32_t status: MOE_OK (0) or a negative MOE_E_* code; the
+ *     message of the last failure on the calling thread is moe_last_error().
+ *     No C++ exception crosses this boundary.
+ *   - Device work is enqueued on the caller's stream and the call returns
+ *     without synchronising, except where a call says otherwise.  A kernel
+ *     fault surfaces at the next synchronising HIP call as MOE_E_HIP.
+ *   - bf16 values travel as uint16_t bit patterns.  Matrices are row-major.
+ *   - Pointers named "device" are caller-owned device memory; the library
+ *     keeps non-owning views of weights until the object that uses them is
+ *     destroyed.  Stores, pools, layers and stacks own their own memory.
+ *   - Objects are single-host-thread: calls on one object must not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_E_INVAL = -1,          /* bad argument (shape, null pointer, k > E ...) */
+  MOE_E_NOMEM = -2,          /* host or device allocation failed */
+  MOE_E_HIP = -3,            /* a HIP runtime call failed */
+  MOE_E_RANGE = -4,          /* layer or expert index out of range */
+  MOE_E_POOL_EXHAUSTED = -5, /* every slot is pinned; nothing can be evicted */
+  MOE_E_BUSY = -6            /* the slot is pinned by an in-flight acquire */
+};
+
+#define MOE_MAX_TOPK 16      /* largest k the router supports */
+#define MOE_MAX_DECODE_T 8   /* tokens per call on the per-token (GEMV) path */
+
+/* Last failure message on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Quantised expert format.
+ *
+ * One expert is three matrices W[out, in]: gate [inter, hidden], up [inter,
+ * hidden] and down [hidden, inter] (SwiGLU).  Each is affine group-quantised
+ * in the MLX convention the pages name ([xix] lineage paragraph: MLX-style
+ * int4/int8 group quantisation; [lens] "TurboFieldfareとの関係"):
+ *   W[r, c] = s[r, c/group] * q[r, c] + b[r, c/group],
+ * q unsigned in [0, 2^bits), packed 32/bits fields per uint32 word with
+ * field c of a row at bit bits*(c mod 32/bits) of word c/(32/bits); s and b
+ * bf16.  group is 64; bits is 4 or 8.
+ *
+ * Blob: one expert in one contiguous fixed-size record, so fetching an
+ * expert is one copy ([xix] how-it-works paragraph: experts repacked into
+ * fixed-stride blobs so one read is one fetch).  Sections, each 256-byte
+ * aligned, in this order: gate.q, up.q, down.q, gate.sb, up.sb, down.sb.
+ * An "sb" section holds one uint32 per (row, group): scale bits in the low
+ * half, bias bits in the high half.  stride = bytes rounded up to 4096;
+ * blob (l, e) of a layered store sits at byte (l*E + e) * stride (64-bit).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_qshape {
+  int32_t hidden;   /* H: input of gate/up, output of down; multiple of group */
+  int32_t inter;    /* I: expert intermediate size; multiple of group */
+  int32_t group;    /* must be 64 */
+  int32_t bits;     /* 4 or 8 */
+} moe_qshape;
+
+typedef struct moe_blob_layout {
+  int64_t q_off[3];     /* byte offsets of gate/up/down packed words */
+  int64_t sb_off[3];    /* byte offsets of gate/up/down (scale, bias) words */
+  int64_t q_bytes[3];
+  int64_t sb_bytes[3];
+  int64_t bytes;        /* end of the last section */
+  int64_t stride;       /* bytes rounded up to 4096 */
+} moe_blob_layout;
+
+/* One matrix in canonical host form: q words [out, in*bits/32], s and b
+ * bf16 bits [out, in/group]. */
+typedef struct moe_qmatrix_host {
+  const uint32_t* q;
+  const uint16_t* s;
+  const uint16_t* b;
+} moe_qmatrix_host;
+
+/* Section offsets and stride of one expert blob.  MOE_E_INVAL on a shape
+ * the kernels do not support. */
+int32_t moe_blob_layout_get(const moe_qshape* shape, moe_blob_layout* out);
+
+/* Write one expert (gate, up, down in canonical form) into a host blob of
+ * layout.stride bytes; padding bytes are zeroed.  Host only, synchronous. */
+int32_t moe_blob_pack(const moe_qshape* shape, const moe_qmatrix_host* gate,
+                      const moe_qmatrix_host* up, const moe_qmatrix_host* down,
+                      void* blob_host);
+
+/* ------------------------------------------------------------------------
+ * Router: logits, softmax, top-k, renormalise ([xix] how-it-works
+ * paragraph: each layer sends a token to 10 of 512 experts (80B) or 8 of
+ * 256 (35B); [lens] "エキスパートストリーミングの仕組み").
+ *
+ *   logits[t, e] = sum_h x[t, h] * Wr[e, h] + rb[e]      (f32 accumulation)
+ *   idx[t, :]    = the k largest logits, ordered by (logit desc, index asc)
+ *   w[t, j]      = softmax over all E, renormalised over the chosen k
+ *                = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *   sigma[t]     = 1 / (1 + exp(-(wsg . x_t)))           (shared-expert gate)
+ *
+ * x: device bf16 [T, H]; Wr: device f32 [E, H]; rb: device f32 [E] or
+ * NULL (zero bias); wsg: device f32 [H] or NULL (then sigma is not written).
+ * idx: device int32 [T, k]; w: device f32 [T, k]; sigma: device f32 [T] or
+ * NULL; logits: device f32 [T, E], required -- written, and used as the
+ * kernels' scratch.  MOE_E_INVAL if k < 1, k > E, k > MOE_MAX_TOPK,
+ * E > 1024, H not a positive multiple of 256, or T < 0 (T = 0 is a no-op).
+ * ---------------------------------------------------------------------- */
+int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
+                       const float* rb, int32_t E, int32_t k, const float* wsg,
+                       int32_t* idx, float* w, float* sigma, float* logits,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dequantise one matrix of a device blob (test hook for the bit-exact
+ * dequant check).  which: 0 gate, 1 up, 2 down.  out_f32: device f32
+ * [out, in] with s*q + b computed in f32 (exact for the supported value
+ * ranges); out_bf16: device bf16 [out, in] (round to nearest even of the
+ * f32 value) or NULL.
+ * ---------------------------------------------------------------------- */
+int32_t moe_dequant(const void* blob, const moe_qshape* shape, int32_t which,
+                    float* out_f32, uint16_t* out_bf16, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One SwiGLU expert on T tokens, accumulated:
+ *   h = bf16(silu(Wg x) * (Wu x)),   y_accum[t] += coef[t] * (Wd h)
+ * x: device bf16 [T, H]; blob: device expert blob; coef: device f32 [T];
+ * y_accum: device f32 [T, H] (read and written).  1 <= T <= MOE_MAX_DECODE_T.
+ * Uses stream-ordered scratch (hipMallocAsync) for h.
+ * ---------------------------------------------------------------------- */
+int32_t moe_expert_forward(const uint16_t* x, int32_t T, const moe_qshape* shape,
+                           const void* blob, const float* coef, float* y_accum,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Fixed-stride expert store in pinned host memory: L*E blobs of `stride`
+ * bytes ([xix] how-it-works paragraph: fixed-stride blobs in a .qpack
+ * container, one read per expert; [xix] lineage paragraph: 64-bit offsets
+ * for multi-gigabyte shards).  Allocated with hipHostMalloc; MOE_E_NOMEM if
+ * pinning fails.  stride must be a positive multiple of 4096.
+ * ---------------------------------------------------------------------- */
+typedef struct expert_store expert_store;
+
+int32_t expert_store_create(int32_t layers, int32_t experts, int64_t stride,
+                            expert_store** out);
+/* Copy n <= stride bytes into blob (l, e) (host memcpy). */
+int32_t expert_store_write(expert_store* store, int32_t layer, int32_t expert,
+                           const void* blob, int64_t n);
+/* Host address of blob (l, e). */
+int32_t expert_store_host_ptr(const expert_store* store, int32_t layer,
+                              int32_t expert, void** ptr);
+int32_t expert_store_destroy(expert_store* store);
+
+/* ------------------------------------------------------------------------
+ * Bounded HBM slot pool over a store ([xix] how-it-works paragraph:
+ * popular experts cached in a bounded pool with LFU plus recency eviction;
+ * [lens] "エキスパートストリーミングの仕組み").
+ *
+ * Policy: each access advances a tick; a hit adds one to the slot's use
+ * count and stamps the tick.  A miss takes the lowest-numbered free slot,
+ * else evicts the unpinned resident slot with the smallest (use count, last
+ * tick, layer, expert), and is filled by exactly one hipMemcpyAsync of
+ * `stride` bytes from the store on the pool's own copy stream.  That copy
+ * waits for the evicted slot's last reader (write-after-read) and the
+ * compute stream waits for the copy (read-after-write) -- [lens]
+ * "TurboFieldfareとの関係": explicit hazard management.  The policy decides
+ * hits only; results never depend on it.
+ * ---------------------------------------------------------------------- */
+typedef struct slotpool slotpool;
+
+typedef struct slotpool_stats {
+  int64_t hits;
+  int64_t misses;
+  int64_t evictions;
+  int64_t bytes_h2d;
+} slotpool_stats;
+
+/* capacity: number of slots (>= 1); device: HIP device ordinal.  Allocates
+ * capacity * stride bytes of device memory and a copy stream. */
+int32_t slotpool_create(const expert_store* store, int64_t capacity,
+                        int32_t device, slotpool** out);
+/* Make experts[0..n) of `layer` resident and pin them.  slot_ptrs (out, n
+ * entries): device addresses of the blobs.  was_miss (out, nullable).
+ * `compute` is made to wait for every copy this call enqueued.  The experts
+ * must be distinct.  MOE_E_POOL_EXHAUSTED if a miss finds every slot
+ * pinned (experts admitted earlier in the call stay resident, unpinned). */
+int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts,
+                         int32_t n, hipStream_t compute, const void** slot_ptrs,
+                         uint8_t* was_miss);
+/* Unpin; records on `compute` the event a later refill of these slots
+ * waits for. */
+int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts,
+                         int32_t n, hipStream_t compute);
+/* Drop (layer, expert) if resident.  MOE_E_BUSY if pinned. */
+int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert);
+/* Drop every resident expert (next accesses all miss); MOE_E_BUSY if any
+ * slot is pinned.  Counters are kept. */
+int32_t slotpool_flush(slotpool* pool);
+int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out);
+/* Slot index of (layer, expert), or -1 if not resident (test hook). */
+int32_t slotpool_slot_of(const slotpool* pool, int32_t layer, int32_t expert,
+                         int32_t* slot);
+/* Synchronises the copy stream, then frees. */
+int32_t slotpool_destroy(slotpool* pool);
+
+/* ------------------------------------------------------------------------
+ * MoE layer ([xix] how-it-works paragraph; [lens]
+ * "エキスパートストリーミングの仕組み"): route, run the k chosen SwiGLU
+ * experts from quantised weights, add the sigmoid-gated shared expert,
+ * combine:  y[t] = sum_j w[t,j] * E_idx[t,j](x_t) + sigma_t * S(x_t),
+ * summed in j order then the shared term, f32.  y_bf16 = RNE(y_f32).
+ * ---------------------------------------------------------------------- */
+typedef struct moe_layer_cfg {
+  int32_t hidden;        /* H, multiple of 256, <= 2048 */
+  int32_t experts;       /* E <= 1024 */
+  int32_t top_k;         /* k <= MOE_MAX_TOPK */
+  int32_t inter;         /* I of routed experts */
+  int32_t shared_inter;  /* I of the shared expert */
+  int32_t group;         /* 64 */
+  int32_t bits;          /* 4 or 8 */
+  int32_t layer_index;   /* l: routed blob (l, e) of resident_base / pool */
+} moe_layer_cfg;
+
+typedef struct moe_layer moe_layer;
+
+/* Wr f32 [E,H], rb f32 [E] (nullable), wsg f32 [H], shared_blob: device
+ * blob of shape (H, shared_inter).  Exactly one of resident_base (device
+ * base of the L*E routed blobs, blob (l,e) at (l*E+e)*stride) and pool is
+ * non-NULL.  Allocates the layer's device workspace. */
+int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr,
+                         const float* rb, const void* shared_blob,
+                         const float* wsg, const void* resident_base,
+                         slotpool* pool, moe_layer** out);
+
+/* x: device bf16 [T, H].  y_bf16: device bf16 [T, H] (required); y_f32:
+ * device f32 [T, H] or NULL; idx_out: device int32 [T, k] or NULL; w_out:
+ * device f32 [T, k] or NULL.  1 <= T <= MOE_MAX_DECODE_T takes the
+ * per-token GEMV path; larger T takes the sorted grouped-GEMM path
+ * (MOE_E_INVAL until that path is built).  With a pool, the call copies the
+ * chosen expert ids to the host and waits for them (one sync per call). */
+int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T,
+                          uint16_t* y_bf16, float* y_f32, int32_t* idx_out,
+                          float* w_out, hipStream_t stream);
+int32_t moe_layer_destroy(moe_layer* layer);
+
+/* ------------------------------------------------------------------------
+ * Stack of MoE layers run one after another on the same tokens.  Layer
+ * l > 0 takes x_l = bf16(y_{l-1} / sqrt(mean(y_{l-1}^2) + 1e-6)) (f32), a
+ * weightless stand-in for the residual and norm layers between the pages'
+ * MoE layers, fused into layer l's router.  All layers share H and top_k.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_stack moe_stack;
+
+int32_t moe_stack_create(moe_layer* const* layers, int32_t n_layers,
+                         moe_stack** out);
+/* x0: device bf16 [T, H].  Optional exports (NULL to skip): x_layers bf16
+ * [L, T, H] (each layer's input), y_layers f32 [L, T, H], idx [L, T, k],
+ * w [L, T, k].  y_last: device bf16 [T, H] (required).  1 <= T <=
+ * MOE_MAX_DECODE_T. */
+int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T,
+                          uint16_t* x_layers, float* y_layers, int32_t* idx,
+                          float* w, uint16_t* y_last, hipStream_t stream);
+int32_t moe_stack_destroy(moe_stack* stack);
+
+/* ------------------------------------------------------------------------
+ * Profiling hook: per-launch kernel durations from HIP events.  While a
+ * timer is attached (one per process), every launch of its kernel by a layer
+ * or stack forward is bracketed by two events recorded on the launch's
+ * stream, up to `capacity` launches.  Not thread-safe; for benchmarks.
+ * ---------------------------------------------------------------------- */
+enum { MOE_KERNEL_ROUTE = 0, MOE_KERNEL_GATE_UP = 1, MOE_KERNEL_DOWN = 2 };
+
+typedef struct moe_timer moe_timer;
+
+int32_t moe_timer_create(int32_t kernel, int32_t capacity, moe_timer** out);
+/* Attach (timer) or detach (NULL). */
+int32_t moe_timer_attach(moe_timer* timer);
+/* Waits for the recorded events; ms (out, capacity entries): duration of
+ * each recorded launch in milliseconds; n (out): how many.  Resets the
+ * count. */
+int32_t moe_timer_read(moe_timer* timer, float* ms, int32_t* n);
+int32_t moe_timer_destroy(moe_timer* timer);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

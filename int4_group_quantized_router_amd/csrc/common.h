@@ -1,0 +1,51 @@
+// Host-side helpers shared by every translation unit of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Records a formatted message for moe_last_error() and returns `code`.
+int32_t fail(int32_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Fills `out`; false (with the error set) if the shape is unsupported.
+bool blob_layout(const moe_qshape& s, moe_blob_layout* out);
+
+// Device-side copy of the few layout numbers the kernels need.
+struct QLayout {
+  int64_t q_off[3];
+  int64_t sb_off[3];
+  int64_t stride;
+};
+
+inline QLayout to_qlayout(const moe_blob_layout& l) {
+  QLayout q;
+  for (int i = 0; i < 3; ++i) {
+    q.q_off[i] = l.q_off[i];
+    q.sb_off[i] = l.sb_off[i];
+  }
+  q.stride = l.stride;
+  return q;
+}
+
+}  // namespace moe
+
+#define MOE_HIP_TRY(expr)                                                        \
+  do {                                                                           \
+    hipError_t moe_err_ = (expr);                                                \
+    if (moe_err_ != hipSuccess)                                                  \
+      return ::moe::fail(MOE_E_HIP, "%s failed: %s (%s:%d)", #expr,              \
+                         hipGetErrorString(moe_err_), __FILE__, __LINE__);       \
+  } while (0)
+
+#define MOE_REQUIRE(cond, ...)                                                   \
+  do {                                                                           \
+    if (!(cond)) return ::moe::fail(MOE_E_INVAL, __VA_ARGS__);                   \
+  } while (0)

@@ -1,0 +1,78 @@
+// Internal launch interface between the host objects and the HIP kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxSlots = MOE_MAX_DECODE_T * MOE_MAX_TOPK;  // distinct routed experts per call
+constexpr int kJmapStride = MOE_MAX_DECODE_T;              // jmap row length
+
+// Router (GEMV + fused softmax/top-k) arguments.
+struct RouteArgs {
+  const uint16_t* x;      // bf16 [T,H] input, or NULL when y_prev is given
+  const float* y_prev;    // f32 [T,H]: input is bf16(y_prev / rms(y_prev)), or NULL
+  uint16_t* x_out;        // bf16 [T,H] copy of the input actually used (block 0), or NULL
+  const float* Wr;        // f32 [E,H]
+  const float* rb;        // f32 [E] or NULL
+  const float* wsg;       // f32 [H] or NULL
+  int T, H, E, k;
+  float* logits;          // f32 [T,E]
+  unsigned* counter;      // ticket for the fused top-k (0 at launch), or NULL
+  int32_t* idx;           // [T,k]
+  float* w;               // [T,k]
+  float* sigma;           // [T]: wsg . x from the GEMV, then sigmoid of it; NULL
+                          // (with wsg NULL) to skip the shared gate
+  // distinct-expert list for the expert kernels (NULL to skip)
+  int32_t* n_slots;       // [1]
+  int32_t* slot_expert;   // [T*k]
+  int8_t* jmap;           // [T*k][kJmapStride]: j of token t in slot s, or -1
+};
+
+// Kernels whose LDS (dynamic `bytes` plus up to 8 KiB static) may exceed
+// 64 KiB opt in to more dynamic LDS (gfx950 has 160 KiB per workgroup).
+template <typename Kernel>
+inline hipError_t allow_lds(Kernel kernel, size_t bytes) {
+  if (bytes + 8192 <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_topk_only(const RouteArgs& a, hipStream_t s);  // logits already written
+
+struct SlotPtrs {
+  const uint8_t* p[kMaxSlots];
+};
+
+// Decode (T <= 8) expert kernels.
+struct DecodeArgs {
+  const uint16_t* x;          // bf16 [T,H] layer input
+  int T, H, I, Is, k, bits;
+  int n_slot_max;             // routed slots in the grid (T*k, or 0)
+  const uint8_t* routed_base; // device address of blob (l, 0), or NULL (pool mode)
+  int64_t stride;             // routed blob stride
+  QLayout lr, ls;             // routed / shared section offsets
+  const uint8_t* shared_blob; // or NULL
+  const int32_t* n_slots;     // device [1]
+  const int32_t* slot_expert; // device [n_slot_max]
+  const int8_t* jmap;         // device [n_slot_max][kJmapStride]
+  SlotPtrs pool;              // blob address per slot when routed_base is NULL
+  uint16_t* h;                // bf16 [T][k+1][hI], down-kernel order
+  int hI;                     // max(I, Is)
+  const float* w;             // [T,k] routing weights
+  const float* gate;          // [T] shared-expert scale (sigma, or coef)
+  float* y_f32;               // [T,H] or NULL
+  uint16_t* y_bf16;           // [T,H] or NULL
+  int accumulate;             // y = y_f32_in + ... (y_f32 required)
+};
+
+hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_down(const DecodeArgs& a, hipStream_t s);
+bool decode_shape_supported(int H, int I, int Is, int bits);
+
+hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols,
+                          int bits, int which, float* out_f32, uint16_t* out_bf16,
+                          hipStream_t s);
+
+}  // namespace moe

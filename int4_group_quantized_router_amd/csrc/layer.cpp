@@ -1,0 +1,478 @@
+// MoE layer and stack objects, and the standalone router / expert / dequant
+// entry points.  Host code only: argument checks, workspace, launches.
+//
+// The layer follows the pages' statement of the model's MoE layer ([xix]
+// how-it-works paragraph; [lens] "エキスパートストリーミングの仕組み"): the
+// router, the shared experts and the dense core stay resident; routed experts
+// are read from wherever they live -- all resident in HBM, or a bounded slot
+// pool filled from a host store.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+struct moe_layer {
+  moe_layer_cfg cfg;
+  const float* Wr;
+  const float* rb;
+  const float* wsg;
+  const uint8_t* shared_blob;
+  const uint8_t* resident_base;
+  slotpool* pool;
+  moe_blob_layout lay_r, lay_s;
+  int device;
+  // device workspace, one allocation
+  void* ws;
+  float* logits;
+  int32_t* idx;
+  float* w;
+  float* sigma;
+  unsigned* counter;
+  int32_t* slots;       // [0] = n_slots, [1..] = slot_expert
+  int8_t* jmap;
+  uint16_t* x_cur;
+  uint16_t* h;
+  float* y;
+  int hI;
+  // pinned host mirror of `slots` for the pool path
+  int32_t* host_slots;
+};
+
+struct moe_stack {
+  std::vector<moe_layer*> layers;
+};
+
+struct moe_timer {
+  int32_t kernel;
+  int32_t capacity;
+  int32_t count;
+  std::vector<hipEvent_t> start, stop;
+};
+
+static moe_timer* g_timer = nullptr;
+
+namespace moe {
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int max_lds_per_block(int device) {
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, device) != hipSuccess)
+    return 65536;
+  return v;
+}
+
+size_t down_lds_bytes(int T, int k, int hI, int bits) {
+  const int epc = 128 / bits;
+  return (size_t)T * (k + 1) * hI * 2 + (size_t)T * (k + 1) * (hI / epc) * 4 +
+         (size_t)T * (k + 1) * 8 * 4;
+}
+
+int32_t check_layer_cfg(const moe_layer_cfg& c) {
+  MOE_REQUIRE(c.group == 64, "group must be 64 (got %d)", c.group);
+  MOE_REQUIRE(c.bits == 4 || c.bits == 8, "bits must be 4 or 8 (got %d)", c.bits);
+  MOE_REQUIRE(c.hidden > 0 && c.hidden % 256 == 0 && c.hidden <= 2048,
+              "hidden must be a multiple of 256 in [256, 2048] (got %d)", c.hidden);
+  MOE_REQUIRE(c.experts >= 1 && c.experts <= 1024, "experts must be in [1, 1024] (got %d)",
+              c.experts);
+  MOE_REQUIRE(c.top_k >= 1 && c.top_k <= MOE_MAX_TOPK && c.top_k <= c.experts,
+              "top_k must be in [1, min(E, %d)] (got %d)", MOE_MAX_TOPK, c.top_k);
+  MOE_REQUIRE(decode_shape_supported(c.hidden, c.inter, c.shared_inter, c.bits),
+              "unsupported expert shape H=%d I=%d Is=%d bits=%d", c.hidden, c.inter,
+              c.shared_inter, c.bits);
+  MOE_REQUIRE(c.layer_index >= 0, "layer_index must be >= 0");
+  return MOE_OK;
+}
+
+void timer_mark(int kernel, bool begin, hipStream_t stream) {
+  moe_timer* t = g_timer;
+  if (!t || t->kernel != kernel || t->count >= t->capacity) return;
+  if (begin) {
+    (void)hipEventRecord(t->start[t->count], stream);
+  } else {
+    (void)hipEventRecord(t->stop[t->count], stream);
+    t->count += 1;
+  }
+}
+
+// One forward of a layer on T <= 8 tokens.  Input is either x (bf16) or
+// y_prev (f32 output of the previous layer, rescaled in the router).
+int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uint16_t* x_export,
+                       int T, uint16_t* y_bf16, float* y_f32, int32_t* idx_out, float* w_out,
+                       hipStream_t stream) {
+  const moe_layer_cfg& c = L->cfg;
+  RouteArgs r{};
+  r.x = y_prev ? nullptr : x;
+  r.y_prev = y_prev;
+  r.x_out = y_prev ? (x_export ? x_export : L->x_cur) : x_export;
+  r.Wr = L->Wr;
+  r.rb = L->rb;
+  r.wsg = L->wsg;
+  r.T = T;
+  r.H = c.hidden;
+  r.E = c.experts;
+  r.k = c.top_k;
+  r.logits = L->logits;
+  r.counter = L->counter;
+  r.idx = idx_out ? idx_out : L->idx;
+  r.w = w_out ? w_out : L->w;
+  r.sigma = L->sigma;
+  r.n_slots = L->slots;
+  r.slot_expert = L->slots + 1;
+  r.jmap = L->jmap;
+  timer_mark(MOE_KERNEL_ROUTE, true, stream);
+  MOE_HIP_TRY(launch_route(r, stream));
+  timer_mark(MOE_KERNEL_ROUTE, false, stream);
+
+  DecodeArgs d{};
+  d.x = y_prev ? r.x_out : x;
+  d.T = T;
+  d.H = c.hidden;
+  d.I = c.inter;
+  d.Is = c.shared_inter;
+  d.k = c.top_k;
+  d.bits = c.bits;
+  d.n_slot_max = T * c.top_k;
+  d.stride = L->lay_r.stride;
+  d.lr = to_qlayout(L->lay_r);
+  d.ls = to_qlayout(L->lay_s);
+  d.shared_blob = L->shared_blob;
+  d.n_slots = L->slots;
+  d.slot_expert = L->slots + 1;
+  d.jmap = L->jmap;
+  d.h = L->h;
+  d.hI = L->hI;
+  d.w = r.w;
+  d.gate = L->sigma;
+  d.y_f32 = y_f32;
+  d.y_bf16 = y_bf16;
+  d.accumulate = 0;
+
+  std::vector<int32_t> experts;
+  if (L->pool) {
+    // The chosen experts are needed on the host to run the pool policy.
+    MOE_HIP_TRY(hipMemcpyAsync(L->host_slots, L->slots, sizeof(int32_t) * (1 + T * c.top_k),
+                               hipMemcpyDeviceToHost, stream));
+    MOE_HIP_TRY(hipStreamSynchronize(stream));
+    const int n = L->host_slots[0];
+    if (n < 0 || n > T * c.top_k) return fail(MOE_E_HIP, "router produced %d slots", n);
+    experts.assign(L->host_slots + 1, L->host_slots + 1 + n);
+    const void* ptrs[kMaxSlots];
+    int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, nullptr);
+    if (st != MOE_OK) return st;
+    d.routed_base = nullptr;
+    for (int i = 0; i < n; ++i) d.pool.p[i] = static_cast<const uint8_t*>(ptrs[i]);
+  } else {
+    d.routed_base = L->resident_base + (int64_t)c.layer_index * c.experts * L->lay_r.stride;
+  }
+  timer_mark(MOE_KERNEL_GATE_UP, true, stream);
+  hipError_t e1 = launch_gate_up(d, stream);
+  timer_mark(MOE_KERNEL_GATE_UP, false, stream);
+  timer_mark(MOE_KERNEL_DOWN, true, stream);
+  hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream) : e1;
+  timer_mark(MOE_KERNEL_DOWN, false, stream);
+  if (L->pool) {
+    int32_t st = slotpool_release(L->pool, c.layer_index, experts.data(), (int)experts.size(), stream);
+    if (st != MOE_OK) return st;
+  }
+  MOE_HIP_TRY(e2);
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr, const float* rb,
+                       int32_t E, int32_t k, const float* wsg, int32_t* idx, float* w,
+                       float* sigma, float* logits, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(x && Wr && idx && w && logits, "null argument");
+  MOE_REQUIRE(H > 0 && H % 256 == 0 && H <= 4096, "H must be a multiple of 256 in [256, 4096]");
+  MOE_REQUIRE(E >= 1 && E <= 1024, "E must be in [1, 1024]");
+  MOE_REQUIRE(k >= 1 && k <= E && k <= MOE_MAX_TOPK, "k must be in [1, min(E, %d)]",
+              MOE_MAX_TOPK);
+  RouteArgs r{};
+  r.x = x;
+  r.Wr = Wr;
+  r.rb = rb;
+  r.wsg = sigma ? wsg : nullptr;
+  r.T = T;
+  r.H = H;
+  r.E = E;
+  r.k = k;
+  r.logits = logits;
+  r.idx = idx;
+  r.w = w;
+  r.sigma = sigma;
+  MOE_HIP_TRY(launch_route(r, stream));
+  MOE_HIP_TRY(launch_topk_only(r, stream));
+  return MOE_OK;
+}
+
+int32_t moe_dequant(const void* blob, const moe_qshape* shape, int32_t which, float* out_f32,
+                    uint16_t* out_bf16, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(blob && shape && out_f32, "null argument");
+  MOE_REQUIRE(which >= 0 && which <= 2, "which must be 0, 1 or 2");
+  moe_blob_layout lay;
+  if (!blob_layout(*shape, &lay)) return MOE_E_INVAL;
+  const int rows = which == 2 ? shape->hidden : shape->inter;
+  const int cols = which == 2 ? shape->inter : shape->hidden;
+  MOE_HIP_TRY(launch_dequant(static_cast<const uint8_t*>(blob), to_qlayout(lay), rows, cols,
+                             shape->bits, which, out_f32, out_bf16, stream));
+  return MOE_OK;
+}
+
+int32_t moe_expert_forward(const uint16_t* x, int32_t T, const moe_qshape* shape, const void* blob,
+                           const float* coef, float* y_accum, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(x && shape && blob && coef && y_accum, "null argument");
+  MOE_REQUIRE(T >= 1 && T <= MOE_MAX_DECODE_T, "T must be in [1, %d]", MOE_MAX_DECODE_T);
+  moe_blob_layout lay;
+  if (!blob_layout(*shape, &lay)) return MOE_E_INVAL;
+  MOE_REQUIRE(shape->hidden % 256 == 0 && shape->hidden <= 2048 &&
+                  decode_shape_supported(shape->hidden, shape->inter, shape->inter, shape->bits),
+              "unsupported expert shape H=%d I=%d bits=%d", shape->hidden, shape->inter,
+              shape->bits);
+  int dev = 0;
+  MOE_HIP_TRY(hipGetDevice(&dev));
+  MOE_REQUIRE(down_lds_bytes(T, 0, shape->inter, shape->bits) <= (size_t)max_lds_per_block(dev),
+              "intermediate size too large for LDS");
+  uint16_t* h = nullptr;
+  const size_t hbytes = align256((size_t)T * shape->inter * 2);
+  MOE_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&h), hbytes, stream));
+  DecodeArgs d{};
+  d.x = x;
+  d.T = T;
+  d.H = shape->hidden;
+  d.I = shape->inter;
+  d.Is = shape->inter;
+  d.k = 0;
+  d.bits = shape->bits;
+  d.n_slot_max = 0;
+  d.ls = to_qlayout(lay);
+  d.lr = d.ls;
+  d.shared_blob = static_cast<const uint8_t*>(blob);
+  d.h = h;
+  d.hI = shape->inter;
+  d.gate = coef;
+  d.y_f32 = y_accum;
+  d.accumulate = 1;
+  hipError_t e1 = launch_gate_up(d, stream);
+  hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream) : e1;
+  hipError_t e3 = hipFreeAsync(h, stream);
+  MOE_HIP_TRY(e2);
+  MOE_HIP_TRY(e3);
+  return MOE_OK;
+}
+
+int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float* rb,
+                         const void* shared_blob, const float* wsg, const void* resident_base,
+                         slotpool* pool, moe_layer** out) {
+  clear_error();
+  MOE_REQUIRE(cfg && Wr && shared_blob && wsg && out, "null argument");
+  MOE_REQUIRE((resident_base != nullptr) != (pool != nullptr),
+              "exactly one of resident_base and pool must be given");
+  int32_t st = check_layer_cfg(*cfg);
+  if (st != MOE_OK) return st;
+  moe_qshape sr{cfg->hidden, cfg->inter, cfg->group, cfg->bits};
+  moe_qshape ss{cfg->hidden, cfg->shared_inter, cfg->group, cfg->bits};
+  moe_layer* L = new (std::nothrow) moe_layer{};
+  if (!L) return fail(MOE_E_NOMEM, "host allocation failed");
+  L->cfg = *cfg;
+  blob_layout(sr, &L->lay_r);
+  blob_layout(ss, &L->lay_s);
+  L->Wr = Wr;
+  L->rb = rb;
+  L->wsg = wsg;
+  L->shared_blob = static_cast<const uint8_t*>(shared_blob);
+  L->resident_base = static_cast<const uint8_t*>(resident_base);
+  L->pool = pool;
+  L->hI = std::max(cfg->inter, cfg->shared_inter);
+  hipError_t he = hipGetDevice(&L->device);
+  if (he != hipSuccess) {
+    delete L;
+    return fail(MOE_E_HIP, "hipGetDevice: %s", hipGetErrorString(he));
+  }
+  if (down_lds_bytes(MOE_MAX_DECODE_T, cfg->top_k, L->hI, cfg->bits) >
+      (size_t)max_lds_per_block(L->device)) {
+    delete L;
+    return fail(MOE_E_INVAL, "top_k x intermediate too large for the down kernel's LDS");
+  }
+  const int T = MOE_MAX_DECODE_T, E = cfg->experts, k = cfg->top_k, H = cfg->hidden;
+  const size_t sizes[] = {
+      (size_t)T * E * 4,                 // logits
+      (size_t)T * k * 4,                 // idx
+      (size_t)T * k * 4,                 // w
+      (size_t)T * 4,                     // sigma
+      4,                                 // counter
+      (size_t)(1 + T * k) * 4,           // slots
+      (size_t)T * k * kJmapStride,       // jmap
+      (size_t)T * H * 2,                 // x_cur
+      (size_t)T * (k + 1) * L->hI * 2,   // h
+      (size_t)T * H * 4,                 // y
+  };
+  size_t total = 0;
+  for (size_t s : sizes) total += align256(s);
+  he = hipMalloc(&L->ws, total);
+  if (he != hipSuccess) {
+    delete L;
+    return fail(MOE_E_NOMEM, "workspace hipMalloc(%zu): %s", total, hipGetErrorString(he));
+  }
+  uint8_t* p = static_cast<uint8_t*>(L->ws);
+  void* parts[10];
+  for (int i = 0; i < 10; ++i) {
+    parts[i] = p;
+    p += align256(sizes[i]);
+  }
+  L->logits = static_cast<float*>(parts[0]);
+  L->idx = static_cast<int32_t*>(parts[1]);
+  L->w = static_cast<float*>(parts[2]);
+  L->sigma = static_cast<float*>(parts[3]);
+  L->counter = static_cast<unsigned*>(parts[4]);
+  L->slots = static_cast<int32_t*>(parts[5]);
+  L->jmap = static_cast<int8_t*>(parts[6]);
+  L->x_cur = static_cast<uint16_t*>(parts[7]);
+  L->h = static_cast<uint16_t*>(parts[8]);
+  L->y = static_cast<float*>(parts[9]);
+  he = hipMemset(L->ws, 0, total);
+  if (he == hipSuccess && pool)
+    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (1 + T * k) * sizeof(int32_t),
+                       hipHostMallocDefault);
+  if (he == hipSuccess) he = hipDeviceSynchronize();
+  if (he != hipSuccess) {
+    (void)hipFree(L->ws);
+    delete L;
+    return fail(MOE_E_HIP, "layer setup: %s", hipGetErrorString(he));
+  }
+  *out = L;
+  return MOE_OK;
+}
+
+int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y_bf16,
+                          float* y_f32, int32_t* idx_out, float* w_out, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(layer && x && y_bf16, "null argument");
+  MOE_REQUIRE(T >= 1, "T must be >= 1");
+  MOE_REQUIRE(T <= MOE_MAX_DECODE_T, "T = %d: the many-token path is not available", T);
+  return forward_decode(layer, x, nullptr, nullptr, T, y_bf16, y_f32 ? y_f32 : layer->y, idx_out,
+                        w_out, stream);
+}
+
+int32_t moe_layer_destroy(moe_layer* layer) {
+  clear_error();
+  if (!layer) return MOE_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (layer->ws) (void)hipFree(layer->ws);
+  if (layer->host_slots) (void)hipHostFree(layer->host_slots);
+  delete layer;
+  if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int32_t moe_stack_create(moe_layer* const* layers, int32_t n_layers, moe_stack** out) {
+  clear_error();
+  MOE_REQUIRE(layers && out && n_layers >= 1, "bad argument");
+  for (int i = 0; i < n_layers; ++i) {
+    MOE_REQUIRE(layers[i], "layer %d is NULL", i);
+    MOE_REQUIRE(layers[i]->cfg.hidden == layers[0]->cfg.hidden &&
+                    layers[i]->cfg.top_k == layers[0]->cfg.top_k,
+                "all layers of a stack must share hidden size and top_k");
+  }
+  moe_stack* s = new (std::nothrow) moe_stack{};
+  if (!s) return fail(MOE_E_NOMEM, "host allocation failed");
+  s->layers.assign(layers, layers + n_layers);
+  *out = s;
+  return MOE_OK;
+}
+
+int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint16_t* x_layers,
+                          float* y_layers, int32_t* idx, float* w, uint16_t* y_last,
+                          hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(stack && x0 && y_last, "null argument");
+  MOE_REQUIRE(T >= 1 && T <= MOE_MAX_DECODE_T, "T must be in [1, %d]", MOE_MAX_DECODE_T);
+  const int n = (int)stack->layers.size();
+  const int H = stack->layers[0]->cfg.hidden, k = stack->layers[0]->cfg.top_k;
+  const float* prev = nullptr;
+  for (int l = 0; l < n; ++l) {
+    moe_layer* L = stack->layers[l];
+    float* yout = y_layers ? y_layers + (size_t)l * T * H : L->y;
+    int32_t st = forward_decode(L, l == 0 ? x0 : nullptr, prev,
+                                x_layers ? x_layers + (size_t)l * T * H : nullptr, T,
+                                l == n - 1 ? y_last : nullptr, yout,
+                                idx ? idx + (size_t)l * T * k : nullptr,
+                                w ? w + (size_t)l * T * k : nullptr, stream);
+    if (st != MOE_OK) return st;
+    prev = yout;
+  }
+  return MOE_OK;
+}
+
+int32_t moe_stack_destroy(moe_stack* stack) {
+  delete stack;
+  return MOE_OK;
+}
+
+int32_t moe_timer_create(int32_t kernel, int32_t capacity, moe_timer** out) {
+  clear_error();
+  MOE_REQUIRE(out && capacity >= 1 && kernel >= MOE_KERNEL_ROUTE && kernel <= MOE_KERNEL_DOWN,
+              "bad argument");
+  moe_timer* t = new (std::nothrow) moe_timer{};
+  if (!t) return fail(MOE_E_NOMEM, "host allocation failed");
+  t->kernel = kernel;
+  t->capacity = capacity;
+  t->start.assign(capacity, nullptr);
+  t->stop.assign(capacity, nullptr);
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&t->start[i]);
+    if (e == hipSuccess) e = hipEventCreate(&t->stop[i]);
+    if (e != hipSuccess) {
+      moe_timer_destroy(t);
+      return fail(MOE_E_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  }
+  *out = t;
+  return MOE_OK;
+}
+
+int32_t moe_timer_attach(moe_timer* timer) {
+  clear_error();
+  g_timer = timer;
+  return MOE_OK;
+}
+
+int32_t moe_timer_read(moe_timer* timer, float* ms, int32_t* n) {
+  clear_error();
+  MOE_REQUIRE(timer && ms && n, "null argument");
+  for (int i = 0; i < timer->count; ++i) {
+    MOE_HIP_TRY(hipEventSynchronize(timer->stop[i]));
+    MOE_HIP_TRY(hipEventElapsedTime(&ms[i], timer->start[i], timer->stop[i]));
+  }
+  *n = timer->count;
+  timer->count = 0;
+  return MOE_OK;
+}
+
+int32_t moe_timer_destroy(moe_timer* timer) {
+  clear_error();
+  if (!timer) return MOE_OK;
+  if (g_timer == timer) g_timer = nullptr;
+  for (hipEvent_t e : timer->start)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : timer->stop)
+    if (e) (void)hipEventDestroy(e);
+  delete timer;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,321 @@
+// Router: logits GEMV, then softmax / top-k / renormalise.
+//
+// Each layer sends a token to k of E routed experts (10 of 512 in the 80B
+// model, 8 of 256 in the 35B model) -- [xix] how-it-works paragraph; [lens]
+// "エキスパートストリーミングの仕組み".  The router stays resident and
+// unquantised in f32 (the pages list routers among the dense weights kept in
+// memory).
+//
+// Kernel shape (decode, T <= 8 tokens):
+//   * the layer input is staged once per workgroup in LDS as f32; for layer
+//     l > 0 of a stack it is bf16(y_{l-1} / rms(y_{l-1})), computed here;
+//   * one 64-lane wave streams half a row of Wr (or all of it for H < 512)
+//     with 16-byte loads and keeps all T token sums in registers, so Wr is
+//     read exactly once per call;
+//   * the last workgroup to finish (device-scope ticket) reads the E logits
+//     back and runs the top-k on one wave per token: k rounds of a
+//     lane-local best + a 6-step butterfly arg-max.  Selection compares
+//     logits (softmax is monotone); ties go to the lower expert index.
+//   * the same workgroup builds the list of distinct experts of the call
+//     (first appearance order) and, per distinct expert, which slot j each
+//     token gave it -- the expert kernels read every chosen expert once.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+using namespace dev;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ void stage_input(const RouteArgs& a, float* xs, float* red, int T) {
+  const int tid = threadIdx.x;
+  const int H = a.H;
+  if (a.y_prev) {
+    for (int t = 0; t < T; ++t) {
+      const float* y = a.y_prev + (size_t)t * H;
+      float s = 0.f;
+      for (int i = tid; i < H; i += kThreads) s = fmaf(y[i], y[i], s);
+      s = group_sum(s, kWave);
+      __syncthreads();
+      if ((tid & 63) == 0) red[tid >> 6] = s;
+      __syncthreads();
+      const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+      const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+      for (int i = tid; i < H; i += kThreads) {
+        const uint32_t b = f32_to_bf16(y[i] * r);
+        xs[t * H + i] = bf16_to_f32(b);
+        if (blockIdx.x == 0 && a.x_out) a.x_out[(size_t)t * H + i] = (uint16_t)b;
+      }
+    }
+  } else {
+    for (int i = tid; i < T * H; i += kThreads) {
+      const uint16_t b = a.x[i];
+      xs[i] = bf16_to_f32(b);
+      if (blockIdx.x == 0 && a.x_out) a.x_out[i] = b;
+    }
+  }
+}
+
+// Top-k of tokens [t0, t1) with one wave per token; selections go to LDS.
+template <int VPL>
+__device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int E = a.E, k = a.k;
+  for (int t = t0 + wave; t < t1; t += kWaves) {
+    const float* lg = a.logits + (size_t)t * E;
+    float v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + kWave * i;
+      v[i] = e < E ? lg[e] : -INFINITY;
+    }
+    uint32_t taken = 0;
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        const bool free_ = e < E && !((taken >> i) & 1u);
+        if (free_ && (v[i] > bv || (v[i] == bv && e < bi))) {
+          bv = v[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      if (lane == 0) {
+        s_sel[(t - t0) * k + j] = bi;
+        s_val[(t - t0) * k + j] = bv;
+      }
+    }
+  }
+}
+
+// Renormalised weights over the chosen k (= softmax over the chosen
+// logits: the full-softmax denominator cancels) and the shared gate.
+__device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_sel,
+                              const float* s_val) {
+  const int k = a.k;
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += kThreads) {
+    const int r = t - t0;
+    const float m = s_val[r * k];
+    float ex[MOE_MAX_TOPK];
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        ex[j] = expf(s_val[r * k + j] - m);
+        sum += ex[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        a.w[(size_t)t * k + j] = ex[j] / sum;
+        a.idx[(size_t)t * k + j] = s_sel[r * k + j];
+      }
+    }
+    if (a.sigma && a.wsg) a.sigma[t] = 1.0f / (1.0f + expf(-a.sigma[t]));
+  }
+}
+
+// Distinct experts of the call in first-appearance order (token-major).
+__device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, int* s_slot) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = a.T * a.k, k = a.k;
+  for (int e = threadIdx.x; e < a.E; e += kThreads) s_first[e] = 0x7fffffff;
+  for (int i = threadIdx.x; i < n * kJmapStride; i += kThreads) a.jmap[i] = -1;
+  __syncthreads();
+  for (int p = threadIdx.x; p < n; p += kThreads) atomicMin(&s_first[s_sel[p]], p);
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+    for (int p0 = 0; p0 < n; p0 += kWave) {
+      const int p = p0 + lane;
+      const bool first = p < n && s_first[s_sel[p]] == p;
+      const unsigned long long b = __ballot(first);
+      if (p < n) s_slot[p] = first ? base + __popcll(b & ((1ull << lane) - 1ull)) : -1;
+      base += __popcll(b);
+    }
+    if (lane == 0) *a.n_slots = base;
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < n; p += kThreads) {
+    const int e = s_sel[p];
+    const int slot = s_slot[s_first[e]];
+    a.jmap[slot * kJmapStride + p / k] = (int8_t)(p % k);
+    if (s_first[e] == p) a.slot_expert[slot] = e;
+  }
+}
+
+// GEMV over Wr (and wsg as row E) for up to NT tokens: blockIdx.y selects a
+// tile of NT tokens.  With a ticket counter the last block runs the top-k.
+template <int NT, int VPL>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  extern __shared__ __align__(16) float xs[];  // [NT][H]
+  __shared__ float red[kWaves];
+  __shared__ float halves[kWaves][NT];
+  __shared__ int s_last;
+
+  const int t0 = blockIdx.y * NT;
+  const int T = min(NT, a.T - t0);
+  RouteArgs b = a;
+  if (a.x) b.x = a.x + (size_t)t0 * a.H;
+  if (a.y_prev) b.y_prev = a.y_prev + (size_t)t0 * a.H;
+  if (a.x_out) b.x_out = a.x_out + (size_t)t0 * a.H;
+  stage_input(b, xs, red, T);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = a.H, E = a.E;
+  const int rows = E + (a.wsg && a.sigma ? 1 : 0);
+  const int wpr = (H % 512 == 0) ? 2 : 1;
+  const int item = blockIdx.x * kWaves + wave;
+  const int row = item / wpr, part = item % wpr;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+  if (row < rows) {
+    const float* wr = row < E ? a.Wr + (size_t)row * H : a.wsg;
+    const int span = H / wpr, c0 = part * span;
+    for (int c = c0 + lane * 4; c < c0 + span; c += 4 * kWave) {
+      const float4 wv = *reinterpret_cast<const float4*>(wr + c);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < T) {
+          const float4 xv = *reinterpret_cast<const float4*>(xs + t * H + c);
+          float s = acc[t];
+          s = fmaf(wv.x, xv.x, s);
+          s = fmaf(wv.y, xv.y, s);
+          s = fmaf(wv.z, xv.z, s);
+          s = fmaf(wv.w, xv.w, s);
+          acc[t] = s;
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = group_sum(acc[t], kWave);
+  }
+  float out[NT];
+  if (wpr == 2) {
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) halves[wave][t] = acc[t];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[t] = halves[wave & ~1][t] + halves[wave | 1][t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[t] = acc[t];
+  }
+  if (row < rows && part == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T && lane == t) {
+        if (row < E)
+          a.logits[(size_t)(t0 + t) * E + row] = out[t] + (a.rb ? a.rb[row] : 0.f);
+        else
+          a.sigma[t0 + t] = out[t];
+      }
+    }
+  }
+
+  if (!a.counter) return;
+  // Last block: every other block's logits are visible after the ticket.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (atomicAdd(a.counter, 1u) == gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (threadIdx.x == 0) *a.counter = 0u;
+
+  __shared__ int s_sel[NT * MOE_MAX_TOPK];
+  __shared__ float s_val[NT * MOE_MAX_TOPK];
+  __shared__ int s_slot[NT * MOE_MAX_TOPK];
+  __shared__ int s_first[1024];
+  topk_tokens<VPL>(a, 0, a.T, s_sel, s_val);
+  __syncthreads();
+  write_weights(a, 0, a.T, s_sel, s_val);
+  if (a.n_slots) build_slots(a, s_sel, s_first, s_slot);
+}
+
+// Top-k alone over logits written by an earlier launch: 4 tokens per block.
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void topk_kernel(RouteArgs a) {
+  __shared__ int s_sel[kWaves * MOE_MAX_TOPK];
+  __shared__ float s_val[kWaves * MOE_MAX_TOPK];
+  const int t0 = blockIdx.x * kWaves;
+  const int t1 = min(a.T, t0 + kWaves);
+  topk_tokens<VPL>(a, t0, t1, s_sel, s_val);
+  __syncthreads();
+  write_weights(a, t0, t1, s_sel, s_val);
+}
+
+template <int NT>
+hipError_t launch_route_nt(const RouteArgs& a, hipStream_t s, bool fused) {
+  const int rows = a.E + (a.wsg && a.sigma ? 1 : 0);
+  const int wpr = (a.H % 512 == 0) ? 2 : 1;
+  dim3 grid((rows * wpr + kWaves - 1) / kWaves, fused ? 1 : (a.T + NT - 1) / NT);
+  const size_t lds = (size_t)NT * a.H * sizeof(float);
+  RouteArgs b = a;
+  if (!fused) {
+    b.counter = nullptr;
+  }
+  const int vpl = (a.E + 63) / 64;
+#define MOE_ROUTE_CASE(V)                                                           \
+  if (vpl <= V) {                                                                   \
+    hipError_t e = allow_lds(route_kernel<NT, V>, lds);                             \
+    if (e != hipSuccess) return e;                                                  \
+    hipLaunchKernelGGL((route_kernel<NT, V>), grid, dim3(kThreads), lds, s, b);     \
+    return hipGetLastError();                                                       \
+  }
+  MOE_ROUTE_CASE(1)
+  MOE_ROUTE_CASE(2)
+  MOE_ROUTE_CASE(4)
+  MOE_ROUTE_CASE(8)
+  MOE_ROUTE_CASE(16)
+#undef MOE_ROUTE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.T <= 1) return launch_route_nt<1>(a, s, a.counter != nullptr);
+  if (a.T <= MOE_MAX_DECODE_T) return launch_route_nt<MOE_MAX_DECODE_T>(a, s, a.counter != nullptr);
+  // Many tokens: GEMV over token tiles only; the top-k runs as its own launch.
+  return launch_route_nt<MOE_MAX_DECODE_T>(a, s, false);
+}
+
+hipError_t launch_topk_only(const RouteArgs& a, hipStream_t s) {
+  dim3 grid((a.T + kWaves - 1) / kWaves);
+  const int vpl = (a.E + 63) / 64;
+#define MOE_TOPK_CASE(V)                                                         \
+  if (vpl <= V) {                                                                \
+    hipLaunchKernelGGL((topk_kernel<V>), grid, dim3(kThreads), 0, s, a);         \
+    return hipGetLastError();                                                    \
+  }
+  MOE_TOPK_CASE(1)
+  MOE_TOPK_CASE(2)
+  MOE_TOPK_CASE(4)
+  MOE_TOPK_CASE(8)
+  MOE_TOPK_CASE(16)
+#undef MOE_TOPK_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

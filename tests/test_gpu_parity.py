@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Dequantisation and routing decisions exact; layer
+outputs within 2e-3 max-norm relative error on the f32 result; bf16 output
+= round-to-nearest-even of the f32 output."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, token_x, tokens_x
+from oracle import moe_oracle as O
+
+from harness import (REL_TOL, DeviceModel, check_bf16_of_f32, check_routing, oracle_layer,
+                     rel_err)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def _x(torch, cfg, t0, n):
+    return torch.from_numpy(tokens_x(cfg, t0, n).view(np.int16)).cuda()
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _device_bytes(addr, n):
+    """Copy n bytes at a raw device address to the host (HIP runtime call)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    out = np.empty(n, np.uint8)
+    assert hip.hipMemcpy(out.ctypes.data, addr, n, 2) == 0  # hipMemcpyDeviceToHost
+    return out
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("name,H,I", [("tiny", 256, 64), ("decode35b", 2048, 512),
+                                      ("decode80b_int8", 2048, 512), ("decode80b_int8", 256, 128)])
+def test_dequant_bit_exact(torch, name, H, I):
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd.weights import upload_blob
+    cfg = CONFIGS[name].replace(hidden=H, inter=I)
+    _print("dequant", name, H, I)
+    arr = expert_arrays(cfg, 0, 11)
+    blob = upload_blob(H, I, cfg.bits, arr)
+    for which, mat in enumerate(("gate", "up", "down")):
+        f32, b16 = m.moe_dequant(blob, H, I, cfg.bits, which)
+        torch.cuda.synchronize()
+        W = O.dequantize(*arr[mat], bits=cfg.bits, group=64)
+        assert np.array_equal(f32.cpu().numpy().astype(np.float64), W)
+        assert np.array_equal(b16.cpu().numpy().view(np.uint16), O.bf16_bits(O.round_bf16(W)))
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 8), ("decode35b", 1), ("decode35b", 8),
+                                    ("stream80b", 1), ("stream80b", 5), ("stream80b", 37),
+                                    ("prefill80b", 300)])
+def test_route_topk(torch, name, T):
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS[name]
+    _print("route", name, T)
+    decided = 0
+    for layer in (0, 1):
+        Wr, rb, wsg = router_arrays(cfg, layer)
+        xb = tokens_x(cfg, 100 * layer, T)
+        out = m.moe_route_topk(torch.from_numpy(xb.view(np.int16)).cuda(),
+                               torch.from_numpy(Wr).cuda(), torch.from_numpy(rb).cuda(),
+                               cfg.top_k, wsg=torch.from_numpy(wsg).cuda())
+        torch.cuda.synchronize()
+        idx, w = out["idx"].cpu().numpy(), out["w"].cpu().numpy()
+        lg, sg = out["logits"].cpu().numpy(), out["sigma"].cpu().numpy()
+        for t in range(T):
+            x = O.bf16_to_f64(xb[t])
+            decided += check_routing(idx[t], lg[t], x, Wr, rb, cfg.top_k, w[t])
+            s_ref = O.sigmoid(np.dot(wsg.astype(np.float64), x))
+            assert abs(sg[t] - s_ref) <= 1e-6
+    assert decided >= 0.9 * 2 * T
+
+
+def test_route_edge_cases(torch):
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["tiny"]
+    Wr, rb, wsg = router_arrays(cfg, 0)
+    dWr, dwsg = torch.from_numpy(Wr).cuda(), torch.from_numpy(wsg).cuda()
+    # x = 0 and no bias: all logits tie -> experts 0..k-1, equal weights, sigma 1/2
+    x0 = torch.zeros((3, cfg.hidden), dtype=torch.int16, device="cuda")
+    for k in (1, 2, 16):
+        out = m.moe_route_topk(x0, dWr, None, k, wsg=dwsg)
+        torch.cuda.synchronize()
+        assert (out["idx"].cpu().numpy() == np.arange(k)).all()
+        assert np.allclose(out["w"].cpu().numpy(), 1.0 / k, rtol=0, atol=1e-7)
+        assert np.all(out["sigma"].cpu().numpy() == 0.5)
+    # k = E: weights equal the full softmax of the GPU logits
+    xb = tokens_x(cfg, 0, 4)
+    out = m.moe_route_topk(torch.from_numpy(xb.view(np.int16)).cuda(), dWr,
+                           torch.from_numpy(rb).cuda(), cfg.experts)
+    torch.cuda.synchronize()
+    lg = out["logits"].cpu().numpy()
+    for t in range(4):
+        p = O.softmax(lg[t].astype(np.float64))
+        idx = out["idx"].cpu().numpy()[t]
+        assert sorted(idx.tolist()) == list(range(cfg.experts))
+        assert np.allclose(out["w"].cpu().numpy()[t], p[idx], rtol=2e-6)
+    # T = 0 is a no-op
+    m.moe_route_topk(x0[:0], dWr, None, 2)
+
+
+# ------------------------------------------------------------ single expert
+
+@pytest.mark.parametrize("name,H,I,T", [("tiny", 256, 64, 3), ("decode35b", 2048, 512, 1),
+                                        ("decode35b", 2048, 512, 8),
+                                        ("decode80b_int8", 2048, 512, 2),
+                                        ("decode80b_int8", 512, 256, 5)])
+def test_expert_forward(torch, name, H, I, T):
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd.weights import upload_blob
+    cfg = CONFIGS[name].replace(hidden=H, inter=I)
+    _print("expert", name, H, I, T)
+    arr = expert_arrays(cfg, 0, 5)
+    blob = upload_blob(H, I, cfg.bits, arr)
+    xb = tokens_x(cfg, 0, T)
+    rng = np.random.default_rng(0)
+    y0 = rng.standard_normal((T, H)).astype(np.float32)
+    coef = rng.uniform(0.1, 1.0, T).astype(np.float32)
+    y = torch.from_numpy(y0.copy()).cuda()
+    m.moe_expert_forward(torch.from_numpy(xb.view(np.int16)).cuda(), H, I, cfg.bits, blob,
+                         torch.from_numpy(coef).cuda(), y)
+    torch.cuda.synchronize()
+    Wg, Wu, Wd = O.dequant_expert(arr, cfg.bits, 64)
+    for t in range(T):
+        e = O.swiglu(O.bf16_to_f64(xb[t]), Wg, Wu, Wd)[0] * float(coef[t])
+        err = np.max(np.abs(y.cpu().numpy()[t] - (y0[t] + e))) / np.max(np.abs(e))
+        assert err <= REL_TOL, err
+
+
+# -------------------------------------------------------------------- layer
+
+def _layer_case(torch, cfg, calls, layer=0):
+    """Run the layer on calls = [token-id lists] and compare every token."""
+    import int4_group_quantized_router_amd as m
+    dm = DeviceModel(cfg, layers=layer + 1)
+    L = dm.make_layers()[layer]
+    worst = 0.0
+    try:
+        for toks in calls:
+            T = len(toks)
+            xb = np.stack([token_x(cfg, t) for t in toks])
+            y16 = torch.empty((T, cfg.hidden), dtype=torch.int16, device="cuda")
+            y32 = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+            idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+            m.moe_layer_forward(L, torch.from_numpy(xb.view(np.int16)).cuda(), y16, y32, idx, w)
+            torch.cuda.synchronize()
+            Wr, rb, _ = router_arrays(cfg, layer)
+            for i in range(T):
+                ref = oracle_layer(cfg, layer, xb[i])
+                x = O.bf16_to_f64(xb[i])
+                check_routing(idx.cpu().numpy()[i], None, x, Wr, rb, cfg.top_k)
+                if np.array_equal(idx.cpu().numpy()[i], ref["idx"]):
+                    err = rel_err(y32.cpu().numpy()[i], ref["y"])
+                    worst = max(worst, err)
+                    assert err <= REL_TOL, (toks, i, err)
+            check_bf16_of_f32(y16.cpu().numpy(), y32.cpu().numpy())
+    finally:
+        dm.destroy()
+    _print("worst rel err", worst)
+    return worst
+
+
+def test_layer_tiny(torch):
+    cfg = CONFIGS["tiny"]
+    _print("layer tiny")
+    _layer_case(torch, cfg, [list(range(8)), [8], [9, 10, 11], [12]])
+
+
+@pytest.mark.parametrize("name", ["stream80b", "decode80b_int8", "decode35b"])
+def test_layer_full_shape(torch, name):
+    cfg = CONFIGS[name].replace(layers=1)
+    _print("layer", name)
+    _layer_case(torch, cfg, [[0], [1], list(range(2, 10)), [10, 11, 12], [13]])
+
+
+def test_layer_shared_inter_differs(torch):
+    cfg = CONFIGS["tiny"].replace(inter=128, shared_inter=64, experts=32, top_k=4)
+    _print("layer I != Is")
+    _layer_case(torch, cfg, [[0], list(range(1, 8))])
+
+
+# -------------------------------------------------------------------- stack
+
+def test_stack_teacher_forced(torch):
+    """Per-layer parity in a stack: each layer's GPU output against the oracle
+    run on the GPU's own bf16 input to that layer; the RMS rescale between
+    layers against the oracle's, to one bf16 ulp."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["decode35b"].replace(layers=4)
+    _print("stack", cfg.name)
+    dm = DeviceModel(cfg)
+    layers = dm.make_layers()
+    st = m.moe_stack_create(layers)
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    try:
+        for tok in range(3):
+            T = 1
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            xl = torch.empty((L, T, H), dtype=torch.int16, device="cuda")
+            yl = torch.empty((L, T, H), dtype=torch.float32, device="cuda")
+            idx = torch.empty((L, T, k), dtype=torch.int32, device="cuda")
+            w = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
+            ylast = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx, w=w)
+            torch.cuda.synchronize()
+            xl_, yl_ = xl.cpu().numpy().view(np.uint16), yl.cpu().numpy()
+            assert np.array_equal(xl_[0, 0], token_x(cfg, tok))
+            for l in range(L):
+                ref = oracle_layer(cfg, l, xl_[l, 0])
+                Wr, rb, _ = router_arrays(cfg, l)
+                check_routing(idx.cpu().numpy()[l, 0], None, O.bf16_to_f64(xl_[l, 0]), Wr, rb, k)
+                if np.array_equal(idx.cpu().numpy()[l, 0], ref["idx"]):
+                    assert rel_err(yl_[l, 0], ref["y"]) <= REL_TOL
+                if l + 1 < L:
+                    nxt = O.rms_rescale(yl_[l, 0])
+                    diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
+                    assert diff.max() <= 1
+            check_bf16_of_f32(ylast.cpu().numpy(), yl_[L - 1])
+    finally:
+        m.moe_stack_destroy(st)
+        dm.destroy()
+
+
+# --------------------------------------------------------------------- pool
+
+def test_pool_matches_resident_bitwise_and_replay(torch):
+    """An expert served from the slot pool (hit or miss) gives exactly the
+    resident result; the pool's decisions equal the oracle's replay."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from oracle.pool_replay import PoolReplay
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=3)
+    _print("pool", cfg.name)
+    dm = DeviceModel(cfg)
+    store, stride = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    cap = 24
+    pool = m.slotpool_create(store, cap, 0)
+    res_layers = dm.make_layers()
+    pool_layers = dm.make_layers(pool=pool)
+    s_res, s_pool = m.moe_stack_create(res_layers), m.moe_stack_create(pool_layers)
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    replay = PoolReplay(cap, stride)
+    try:
+        for rnd in range(2):
+            for tok in range(6):
+                x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+                outs = []
+                for st in (s_res, s_pool):
+                    yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                    idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                    y = m.moe_stack_forward(st, x0, y_layers=yl, idx=idx)
+                    torch.cuda.synchronize()
+                    outs.append((y.cpu().numpy(), yl.cpu().numpy(), idx.cpu().numpy()))
+                assert np.array_equal(outs[0][0], outs[1][0])
+                assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+                for l in range(L):
+                    ex = outs[1][2][l, 0].tolist()
+                    replay.acquire(l, ex)
+                    replay.release(l, ex)
+            stats = m.slotpool_get_stats(pool)
+            assert stats == replay.stats(), (stats, replay.stats())
+            for l in range(L):
+                for e in range(cfg.experts):
+                    want = replay.slot_of[(l, e)] if replay.resident(l, e) else -1
+                    assert m.slotpool_slot_of(pool, l, e) == want
+            # slot bytes equal store bytes (a hit: no copy in flight)
+            l, e = next(iter(replay.slot_of))
+            ptrs, miss = m.slotpool_acquire(pool, l, [e])
+            replay.acquire(l, [e])
+            assert not miss[0]
+            torch.cuda.synchronize()
+            got = _device_bytes(ptrs[0], stride)
+            src = m.expert_store_host_ptr(store, l, e)
+            want = np.ctypeslib.as_array((ctypes.c_uint8 * stride).from_address(src))
+            assert np.array_equal(got, want)
+            m.slotpool_release(pool, l, [e])
+            replay.release(l, [e])
+            # second round starts from an empty pool: every access misses at first
+            m.slotpool_flush(pool)
+            replay.flush()
+        with pytest.raises(m.MoEError) as ei:
+            m.slotpool_acquire(pool, 0, list(range(cap + 1)))
+        assert "POOL_EXHAUSTED" in str(ei.value)
+        torch.cuda.synchronize()
+    finally:
+        m.moe_stack_destroy(s_res)
+        m.moe_stack_destroy(s_pool)
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
