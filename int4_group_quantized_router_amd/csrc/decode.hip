@@ -28,6 +28,8 @@
 //   LDS and are combined in the fixed order j = 0..k-1, then the shared
 //   term, so the arithmetic never depends on where a blob lives (pool slot
 //   or resident) -- hit and miss give bit-identical outputs.
+#include <algorithm>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -48,7 +50,7 @@ struct Fmt {
 
 __device__ __forceinline__ const uint8_t* slot_blob(const DecodeArgs& a, int s) {
   if (a.routed_base) return a.routed_base + (int64_t)a.slot_expert[s] * a.stride;
-  return a.pool.p[s];
+  return a.slot_ptrs[s];
 }
 
 // Position of intermediate index i inside h: for int4 the 8 values of each
@@ -143,38 +145,59 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
   const int RPP = kWave / LPR;   // rows per wave per pass
   const int rows_per_wg = kWaves * PASSES * RPP;
 
-  // which expert slot / row block
+  // which expert slot / row block: the shared expert's blocks come first
+  // (they do not wait for routing), then the routed slots'
+  const int rb_shared = a.shared_blob ? (a.Is + rows_per_wg - 1) / rows_per_wg : 0;
   const int rb_routed = (a.I + rows_per_wg - 1) / rows_per_wg;
   int slot, rblock, nrows;
-  const uint8_t* blob;
+  const uint8_t* blob = nullptr;
   QLayout L;
   bool shared;
-  if ((int)blockIdx.x < a.n_slot_max * rb_routed) {
-    slot = blockIdx.x / rb_routed;
-    rblock = blockIdx.x % rb_routed;
-    if (slot >= *a.n_slots) return;
-    blob = slot_blob(a, slot);
-    L = a.lr;
-    nrows = a.I;
-    shared = false;
-  } else {
+  if ((int)blockIdx.x < rb_shared) {
     slot = -1;
-    rblock = blockIdx.x - a.n_slot_max * rb_routed;
+    rblock = blockIdx.x;
     blob = a.shared_blob;
     L = a.ls;
     nrows = a.Is;
     shared = true;
+  } else {
+    const int b = blockIdx.x - rb_shared;
+    slot = b / rb_routed;
+    rblock = b % rb_routed;
+    if (NT > 1 && slot >= *a.n_slots) return;
+    L = a.lr;
+    nrows = a.I;
+    shared = false;
   }
   int jt[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    jt[t] = (t < a.T) ? (shared ? a.k : (int)a.jmap[slot * kJmapStride + t]) : -1;
+  for (int t = 0; t < NT; ++t) {
+    if (NT == 1)  // one token: its k experts are distinct, slot s is choice j = s
+      jt[t] = shared ? a.k : slot;
+    else
+      jt[t] = (t < a.T) ? (shared ? a.k : (int)a.jmap[slot * kJmapStride + t]) : -1;
+  }
 
   const int sub = lane % LPR, rsub = lane / LPR;
   const int64_t row_bytes = (int64_t)H * BITS / 8;
   const int G = H / 64;
 
-  // weights for all passes first: keeps PASSES x 2 x CPL 16-byte loads in flight
+  // the lane's x slices (independent of routing: issued first), paired
+  uint32_t xp[NT][CPL][F::kPairs];
+  float xs[NT][CPL];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (jt[t] < 0) continue;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ci = sub + c * LPR;
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + ci * F::kEpc);
+      pair_natural<BITS>(src, xp[t][c], xs[t][c]);
+    }
+  }
+
+  if (!shared) blob = slot_blob(a, slot);
+  // weights for all passes: PASSES x 2 x CPL 16-byte loads in flight per lane
   uint4 q[2][PASSES][CPL];
   uint32_t sb[2][PASSES][CPL];
   int rows[PASSES];
@@ -193,20 +216,6 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
         q[m][p][c] = ok ? ld16(qb + ci * 16) : make_uint4(0, 0, 0, 0);
         sb[m][p][c] = ok ? sbb[ci * F::kEpc / 64] : 0u;
       }
-    }
-  }
-
-  // the lane's x slices, paired
-  uint32_t xp[NT][CPL][F::kPairs];
-  float xs[NT][CPL];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (jt[t] < 0) continue;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int ci = sub + c * LPR;
-      const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)t * H + ci * F::kEpc);
-      pair_natural<BITS>(src, xp[t][c], xs[t][c]);
     }
   }
 
@@ -356,6 +365,107 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
   }
 }
 
+// ------------------------------------------------- down+combine, one token
+//
+// Wave w owns slots w, w+4, ... (slot s < k is the token's choice j = s;
+// slot k is the shared expert).  It loads its slots' h slices once into
+// registers (no LDS staging), then the down-projection chunks of the
+// workgroup's R output rows for each of its slots; partial row sums meet in
+// LDS and one thread per row combines them in j order, then the shared term.
+template <int BITS, int SPW, int NPMAX>
+__global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a) {
+  using F = Fmt<BITS>;
+  constexpr int R = 8;
+  __shared__ float part[(kWaves * SPW) * R];
+  __shared__ float s_w[MOE_MAX_TOPK + 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int k = a.k, nsl = k + (a.shared_blob ? 1 : 0);
+  const int row0 = blockIdx.x * R;
+
+  if ((int)threadIdx.x < k) s_w[threadIdx.x] = a.w[threadIdx.x];
+  if ((int)threadIdx.x == k) s_w[k] = a.gate[0];
+
+  uint32_t hp[SPW][F::kPairs];
+  float hs[SPW];
+  uint4 q[SPW][NPMAX];
+  uint32_t sbw[SPW][NPMAX];
+  int C[SPW];
+#pragma unroll
+  for (int si = 0; si < SPW; ++si) {
+    const int s = wave + kWaves * si;
+    C[si] = 1;
+    if (s >= nsl) continue;
+    const bool sh = s == k;
+    const int inner = sh ? a.Is : a.I;
+    C[si] = inner / F::kEpc;
+    const int ci = lane % C[si];
+    const uint4* hsrc = reinterpret_cast<const uint4*>(a.h + (size_t)s * a.hI + ci * F::kEpc);
+#pragma unroll
+    for (int v = 0; v < F::kPairs / 4; ++v) {
+      const uint4 d = hsrc[v];
+      hp[si][4 * v] = d.x;
+      hp[si][4 * v + 1] = d.y;
+      hp[si][4 * v + 2] = d.z;
+      hp[si][4 * v + 3] = d.w;
+    }
+  }
+#pragma unroll
+  for (int si = 0; si < SPW; ++si) {
+    const int s = wave + kWaves * si;
+    if (s >= nsl) continue;
+    const bool sh = s == k;
+    const uint8_t* blob = sh ? a.shared_blob : slot_blob(a, s);
+    const QLayout L = sh ? a.ls : a.lr;
+    const int inner = sh ? a.Is : a.I;
+    const int ci = lane % C[si], RPP = kWave / C[si];
+    const int64_t row_bytes = (int64_t)inner * BITS / 8;
+#pragma unroll
+    for (int p = 0; p < NPMAX; ++p) {
+      const int rloc = p * RPP + lane / C[si];
+      const int row = row0 + rloc;
+      q[si][p] = make_uint4(0, 0, 0, 0);
+      sbw[si][p] = 0;
+      if (rloc < R && row < a.H) {
+        q[si][p] = ld16(blob + L.q_off[2] + (int64_t)row * row_bytes + ci * 16);
+        sbw[si][p] = reinterpret_cast<const uint32_t*>(blob + L.sb_off[2])
+            [(int64_t)row * (inner / 64) + ci * F::kEpc / 64];
+      }
+    }
+  }
+#pragma unroll
+  for (int si = 0; si < SPW; ++si) {
+    float s_ = 0.f;
+#pragma unroll
+    for (int v = 0; v < F::kPairs; ++v) s_ += bf16_lo(hp[si][v]) + bf16_hi(hp[si][v]);
+    hs[si] = s_;
+  }
+#pragma unroll
+  for (int si = 0; si < SPW; ++si) {
+    const int s = wave + kWaves * si;
+    if (s >= nsl) continue;
+    const int ci = lane % C[si], RPP = kWave / C[si];
+#pragma unroll
+    for (int p = 0; p < NPMAX; ++p) {
+      const int rloc = p * RPP + lane / C[si];
+      if (p * RPP >= R) break;
+      float acc = chunk_term<BITS>(0.f, sbw[si][p], chunk_dot<BITS>(q[si][p], hp[si]), hs[si]);
+      acc = group_sum(acc, C[si]);
+      if (ci == 0 && rloc < R) part[s * R + rloc] = acc;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < R) {
+    const int r = threadIdx.x, row = row0 + r;
+    if (row < a.H) {
+      float y = a.accumulate ? a.y_f32[row] : 0.f;
+      for (int j = 0; j < k; ++j) y = fmaf(s_w[j], part[j * R + r], y);
+      if (a.shared_blob) y = fmaf(s_w[k], part[k * R + r], y);
+      if (a.y_f32) a.y_f32[row] = y;
+      if (a.y_bf16) a.y_bf16[row] = (uint16_t)f32_to_bf16(y);
+    }
+  }
+}
+
 // ------------------------------------------------------------ dequant hook
 
 template <int BITS>
@@ -415,6 +525,32 @@ hipError_t gate_up_bits_nt(const DecodeArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <int BITS, int SPW, int NPMAX>
+hipError_t down1_launch(const DecodeArgs& a, hipStream_t s) {
+  const int blocks = (a.H + 7) / 8;
+  hipLaunchKernelGGL((down1_kernel<BITS, SPW, NPMAX>), dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, int SPW>
+hipError_t down1_spw(const DecodeArgs& a, hipStream_t s) {
+  // row passes needed for 8 rows: 8 / (64 / chunks per row)
+  const int cmax = std::max(a.I, a.shared_blob ? a.Is : 0) / Fmt<BITS>::kEpc;
+  const int np = (8 * cmax + kWave - 1) / kWave;
+  if (np <= 2) return down1_launch<BITS, SPW, 2>(a, s);
+  if (np <= 4) return down1_launch<BITS, SPW, 4>(a, s);
+  return down1_launch<BITS, SPW, 8>(a, s);
+}
+
+template <int BITS>
+hipError_t down1_bits(const DecodeArgs& a, hipStream_t s) {
+  const int nsl = a.k + (a.shared_blob ? 1 : 0);
+  if (nsl <= 4) return down1_spw<BITS, 1>(a, s);
+  if (nsl <= 8) return down1_spw<BITS, 2>(a, s);
+  if (nsl <= 12) return down1_spw<BITS, 3>(a, s);
+  return down1_spw<BITS, 5>(a, s);
+}
+
 template <int BITS, int NT>
 hipError_t down_bits_nt(const DecodeArgs& a, hipStream_t s) {
   const int kp1 = a.k + 1;
@@ -449,8 +585,8 @@ hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_down(const DecodeArgs& a, hipStream_t s) {
-  if (a.bits == 4) return a.T <= 1 ? down_bits_nt<4, 1>(a, s) : down_bits_nt<4, 8>(a, s);
-  return a.T <= 1 ? down_bits_nt<8, 1>(a, s) : down_bits_nt<8, 8>(a, s);
+  if (a.T <= 1) return a.bits == 4 ? down1_bits<4>(a, s) : down1_bits<8>(a, s);
+  return a.bits == 4 ? down_bits_nt<4, 8>(a, s) : down_bits_nt<8, 8>(a, s);
 }
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols, int bits,

@@ -41,10 +41,6 @@ inline hipError_t allow_lds(Kernel kernel, size_t bytes) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_topk_only(const RouteArgs& a, hipStream_t s);  // logits already written
 
-struct SlotPtrs {
-  const uint8_t* p[kMaxSlots];
-};
-
 // Decode (T <= 8) expert kernels.
 struct DecodeArgs {
   const uint16_t* x;          // bf16 [T,H] layer input
@@ -57,7 +53,8 @@ struct DecodeArgs {
   const int32_t* n_slots;     // device [1]
   const int32_t* slot_expert; // device [n_slot_max]
   const int8_t* jmap;         // device [n_slot_max][kJmapStride]
-  SlotPtrs pool;              // blob address per slot when routed_base is NULL
+  const uint8_t* const* slot_ptrs;  // device [n_slot_max]: blob address per slot
+                                    // when routed_base is NULL (pool mode)
   uint16_t* h;                // bf16 [T][k+1][hI], down-kernel order
   int hI;                     // max(I, Is)
   const float* w;             // [T,k] routing weights

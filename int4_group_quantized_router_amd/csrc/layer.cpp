@@ -36,8 +36,10 @@ struct moe_layer {
   uint16_t* h;
   float* y;
   int hI;
-  // pinned host mirror of `slots` for the pool path
+  // pool path: pinned host mirror of `slots`, and the slot-pointer table
   int32_t* host_slots;
+  const uint8_t** host_ptrs;   // pinned [kMaxSlots]
+  const uint8_t** dev_ptrs;    // device [kMaxSlots]
 };
 
 struct moe_stack {
@@ -164,7 +166,11 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
     int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, nullptr);
     if (st != MOE_OK) return st;
     d.routed_base = nullptr;
-    for (int i = 0; i < n; ++i) d.pool.p[i] = static_cast<const uint8_t*>(ptrs[i]);
+    for (int i = 0; i < n; ++i) L->host_ptrs[i] = static_cast<const uint8_t*>(ptrs[i]);
+    // host_ptrs is reused next call only after that call's stream sync
+    MOE_HIP_TRY(hipMemcpyAsync(L->dev_ptrs, L->host_ptrs, sizeof(void*) * n,
+                               hipMemcpyHostToDevice, stream));
+    d.slot_ptrs = L->dev_ptrs;
   } else {
     d.routed_base = L->resident_base + (int64_t)c.layer_index * c.experts * L->lay_r.stride;
   }
@@ -320,6 +326,7 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
       (size_t)T * H * 2,                 // x_cur
       (size_t)T * (k + 1) * L->hI * 2,   // h
       (size_t)T * H * 4,                 // y
+      (size_t)kMaxSlots * sizeof(void*), // dev_ptrs
   };
   size_t total = 0;
   for (size_t s : sizes) total += align256(s);
@@ -329,8 +336,8 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
     return fail(MOE_E_NOMEM, "workspace hipMalloc(%zu): %s", total, hipGetErrorString(he));
   }
   uint8_t* p = static_cast<uint8_t*>(L->ws);
-  void* parts[10];
-  for (int i = 0; i < 10; ++i) {
+  void* parts[11];
+  for (int i = 0; i < 11; ++i) {
     parts[i] = p;
     p += align256(sizes[i]);
   }
@@ -344,9 +351,13 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
   L->x_cur = static_cast<uint16_t*>(parts[7]);
   L->h = static_cast<uint16_t*>(parts[8]);
   L->y = static_cast<float*>(parts[9]);
+  L->dev_ptrs = static_cast<const uint8_t**>(parts[10]);
   he = hipMemset(L->ws, 0, total);
   if (he == hipSuccess && pool)
     he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (1 + T * k) * sizeof(int32_t),
+                       hipHostMallocDefault);
+  if (he == hipSuccess && pool)
+    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_ptrs), kMaxSlots * sizeof(void*),
                        hipHostMallocDefault);
   if (he == hipSuccess) he = hipDeviceSynchronize();
   if (he != hipSuccess) {
@@ -374,6 +385,7 @@ int32_t moe_layer_destroy(moe_layer* layer) {
   hipError_t e = hipDeviceSynchronize();
   if (layer->ws) (void)hipFree(layer->ws);
   if (layer->host_slots) (void)hipHostFree(layer->host_slots);
+  if (layer->host_ptrs) (void)hipHostFree(layer->host_ptrs);
   delete layer;
   if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
   return MOE_OK;

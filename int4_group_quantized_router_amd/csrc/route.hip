@@ -29,6 +29,7 @@ using namespace dev;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxIt = 8;  // 16-byte Wr loads per lane: H / (256 * waves per row) <= 8
 
 __device__ void stage_input(const RouteArgs& a, float* xs, float* red, int T) {
   const int tid = threadIdx.x;
@@ -59,47 +60,27 @@ __device__ void stage_input(const RouteArgs& a, float* xs, float* red, int T) {
   }
 }
 
-// Top-k of tokens [t0, t1) with one wave per token; selections go to LDS.
+// Top-k of tokens [t0, t1), one wave per token (ballot radix-select, see
+// wave_topk); selections go to LDS.  Logits are read from the device
+// coherence point: they may have been written by workgroups on other XCDs.
 template <int VPL>
 __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val) {
+  __shared__ int tmp_e[kWaves][MOE_MAX_TOPK];
+  __shared__ float tmp_v[kWaves][MOE_MAX_TOPK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   for (int t = t0 + wave; t < t1; t += kWaves) {
     const float* lg = a.logits + (size_t)t * E;
     float v[VPL];
+    uint32_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = lane + kWave * i;
-      v[i] = e < E ? lg[e] : -INFINITY;
+      v[i] = e < E ? ld_dev(lg + e) : 0.f;
+      key[i] = e < E ? order_key(v[i]) : 0u;
     }
-    uint32_t taken = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        const bool free_ = e < E && !((taken >> i) & 1u);
-        if (free_ && (v[i] > bv || (v[i] == bv && e < bi))) {
-          bv = v[i];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, kWave);
-        const int oi = __shfl_xor(bi, off, kWave);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) {
-        s_sel[(t - t0) * k + j] = bi;
-        s_val[(t - t0) * k + j] = bv;
-      }
-    }
+    wave_topk<VPL>(v, key, k, tmp_e[wave], tmp_v[wave], s_sel + (t - t0) * k,
+                   s_val + (t - t0) * k);
   }
 }
 
@@ -127,7 +108,7 @@ __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_s
         a.idx[(size_t)t * k + j] = s_sel[r * k + j];
       }
     }
-    if (a.sigma && a.wsg) a.sigma[t] = 1.0f / (1.0f + expf(-a.sigma[t]));
+    if (a.sigma && a.wsg) a.sigma[t] = 1.0f / (1.0f + expf(-ld_dev(a.sigma + t)));
   }
 }
 
@@ -171,6 +152,23 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 
   const int t0 = blockIdx.y * NT;
   const int T = min(NT, a.T - t0);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = a.H, E = a.E;
+  const int rows = E + (a.wsg && a.sigma ? 1 : 0);
+  const int wpr = (H % 512 == 0) ? 2 : 1;
+  const int item = blockIdx.x * kWaves + wave;
+  const int row = item / wpr, part = item % wpr;
+  const int span = H / wpr, c0 = part * span, nit = span / (4 * kWave);
+
+  // Wr does not depend on the input: start its loads before staging x.
+  float4 wv[kMaxIt];
+  if (row < rows) {
+    const float* wr = row < E ? a.Wr + (size_t)row * H : a.wsg;
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i)
+      if (i < nit) wv[i] = *reinterpret_cast<const float4*>(wr + c0 + lane * 4 + i * 4 * kWave);
+  }
+
   RouteArgs b = a;
   if (a.x) b.x = a.x + (size_t)t0 * a.H;
   if (a.y_prev) b.y_prev = a.y_prev + (size_t)t0 * a.H;
@@ -178,30 +176,25 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   stage_input(b, xs, red, T);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int H = a.H, E = a.E;
-  const int rows = E + (a.wsg && a.sigma ? 1 : 0);
-  const int wpr = (H % 512 == 0) ? 2 : 1;
-  const int item = blockIdx.x * kWaves + wave;
-  const int row = item / wpr, part = item % wpr;
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.f;
   if (row < rows) {
-    const float* wr = row < E ? a.Wr + (size_t)row * H : a.wsg;
-    const int span = H / wpr, c0 = part * span;
-    for (int c = c0 + lane * 4; c < c0 + span; c += 4 * kWave) {
-      const float4 wv = *reinterpret_cast<const float4*>(wr + c);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < T) {
-          const float4 xv = *reinterpret_cast<const float4*>(xs + t * H + c);
-          float s = acc[t];
-          s = fmaf(wv.x, xv.x, s);
-          s = fmaf(wv.y, xv.y, s);
-          s = fmaf(wv.z, xv.z, s);
-          s = fmaf(wv.w, xv.w, s);
-          acc[t] = s;
+    for (int i = 0; i < kMaxIt; ++i) {
+      if (i < nit) {
+        const int c = c0 + lane * 4 + i * 4 * kWave;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (t < T) {
+            const float4 xv = *reinterpret_cast<const float4*>(xs + t * H + c);
+            float s = acc[t];
+            s = fmaf(wv[i].x, xv.x, s);
+            s = fmaf(wv[i].y, xv.y, s);
+            s = fmaf(wv[i].z, xv.z, s);
+            s = fmaf(wv[i].w, xv.w, s);
+            acc[t] = s;
+          }
         }
       }
     }
@@ -226,22 +219,22 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     for (int t = 0; t < NT; ++t) {
       if (t < T && lane == t) {
         if (row < E)
-          a.logits[(size_t)(t0 + t) * E + row] = out[t] + (a.rb ? a.rb[row] : 0.f);
+          st_dev(a.logits + (size_t)(t0 + t) * E + row, out[t] + (a.rb ? a.rb[row] : 0.f));
         else
-          a.sigma[t0 + t] = out[t];
+          st_dev(a.sigma + t0 + t, out[t]);
       }
     }
   }
 
   if (!a.counter) return;
-  // Last block: every other block's logits are visible after the ticket.
-  __threadfence();
+  // Last block: the logits stores of every block are complete at the
+  // device coherence point before that block takes its ticket.
+  wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(a.counter, 1u) == gridDim.x - 1) ? 1 : 0;
+  if (threadIdx.x == 0) s_last = (ticket(a.counter) == gridDim.x - 1) ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  if (threadIdx.x == 0) *a.counter = 0u;
+  if (threadIdx.x == 0) st_dev(a.counter, 0u);
 
   __shared__ int s_sel[NT * MOE_MAX_TOPK];
   __shared__ float s_val[NT * MOE_MAX_TOPK];
