@@ -27,6 +27,7 @@ struct RouteArgs {
   int32_t* n_slots;       // [1]
   int32_t* slot_expert;   // [T*k]
   int8_t* jmap;           // [T*k][kJmapStride]: j of token t in slot s, or -1
+  int32_t* counts;        // [E] per-expert selection counts (atomic adds), or NULL
 };
 
 // Kernels whose LDS (dynamic `bytes` plus up to 8 KiB static) may exceed
@@ -67,6 +68,46 @@ struct DecodeArgs {
 hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_down(const DecodeArgs& a, hipStream_t s);
 bool decode_shape_supported(int H, int I, int Is, int bits);
+
+// Many-token (prefill) path: sort (token, choice) pairs by expert, grouped
+// MFMA GEMMs with dequant-to-bf16 weight tiles, fixed-order combine.
+constexpr int kPrefillBM = 128;  // rows per GEMM tile
+
+struct PrefillArgs {
+  int T, H, I, Is, E, k, bits, hI;
+  const uint16_t* x;            // bf16 [T, H]
+  const int32_t* idx;           // [T, k]
+  const float* w;               // [T, k]
+  const float* sigma;           // [T]
+  int32_t* counts;              // [E]: rows per expert (filled by the top-k, reset by the scan)
+  int32_t* row_off;             // [E + 2]: first sorted row of each group (group E = shared)
+  int32_t* n_tiles;             // [1]
+  int32_t* tile_group;          // [max_tiles]
+  int32_t* tile_m0;             // [max_tiles]
+  int max_tiles;
+  int32_t* perm_tok;            // [T*k + T]: sorted row -> token
+  int32_t* inv;                 // [T*k]: (t, j) -> sorted row
+  const uint8_t* routed_base;   // blob (l, 0), or NULL: then slot_ptrs[e]
+  const uint8_t* const* slot_ptrs;
+  int64_t stride;
+  QLayout lr, ls;
+  const uint8_t* shared_blob;
+  uint16_t* h;                  // bf16 [rows][hI]
+  float* yd;                    // f32 [rows][H]: every expert's down output
+  float* y_f32;                 // [T, H] or NULL
+  uint16_t* y_bf16;             // [T, H] or NULL
+};
+
+// Router for many tokens: logits = x Wr^T + rb with Wr held as three bf16
+// planes (hi + mid + lo == Wr exactly) on bf16 MFMA with f32 accumulation.
+// wr3: bf16 [3][E + 1][H]; row E holds wsg (zeros if wsg is NULL).
+hipError_t launch_split_router(const float* Wr, const float* wsg, int E, int H, uint16_t* wr3,
+                               hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3,
+                              const float* bias, int has_wsg, int E, float* logits,
+                              float* sigma_raw, hipStream_t s);
+hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_gemms(const PrefillArgs& a, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols,
                           int bits, int which, float* out_f32, uint16_t* out_bf16,

@@ -40,6 +40,28 @@ struct moe_layer {
   int32_t* host_slots;
   const uint8_t** host_ptrs;   // pinned [kMaxSlots]
   const uint8_t** dev_ptrs;    // device [kMaxSlots]
+  // many-token path: workspace allocated on first use, grown with T
+  void* pf;
+  int pf_T;
+  uint16_t* wr3;               // router as three bf16 planes [3][E+1][H]
+  bool wr3_ready;
+  float* pf_logits;
+  int32_t* pf_idx;
+  float* pf_w;
+  float* pf_sigma;
+  int32_t* pf_counts;
+  int32_t* pf_row_off;
+  int32_t* pf_ntiles;
+  int32_t* pf_tg;
+  int32_t* pf_tm;
+  int32_t* pf_perm;
+  int32_t* pf_inv;
+  uint16_t* pf_h;
+  float* pf_yd;
+  int pf_max_tiles;
+  const uint8_t** pf_dev_tab;  // device [E]: blob per expert (pool mode)
+  const uint8_t** pf_host_tab; // pinned [E]
+  int32_t* pf_host_rowoff;     // pinned [E+2]
 };
 
 struct moe_stack {
@@ -188,6 +210,165 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
   return MOE_OK;
 }
 
+int max_tiles_for(int T, int k, int E) {
+  return (T * k + kPrefillBM - 1) / kPrefillBM + E + (T + kPrefillBM - 1) / kPrefillBM + 1;
+}
+
+int32_t ensure_prefill_ws(moe_layer* L, int T) {
+  if (L->pf && L->pf_T >= T) return MOE_OK;
+  const moe_layer_cfg& c = L->cfg;
+  const int E = c.experts, k = c.top_k, H = c.hidden;
+  const int64_t P = (int64_t)T * k, R = P + T;
+  const int mt = max_tiles_for(T, k, E);
+  const size_t sizes[] = {
+      (size_t)3 * (E + 1) * H * 2,  // wr3
+      (size_t)T * E * 4,            // logits
+      (size_t)T * k * 4,            // idx
+      (size_t)T * k * 4,            // w
+      (size_t)T * 4,                // sigma
+      (size_t)E * 4,                // counts
+      (size_t)(E + 2) * 4,          // row_off
+      4,                            // n_tiles
+      (size_t)mt * 4,               // tile_group
+      (size_t)mt * 4,               // tile_m0
+      (size_t)R * 4,                // perm
+      (size_t)P * 4,                // inv
+      (size_t)R * L->hI * 2,        // h
+      (size_t)R * H * 4,            // yd
+      (size_t)E * sizeof(void*),    // dev_tab
+  };
+  size_t total = 0;
+  for (size_t sz : sizes) total += align256(sz);
+  if (L->pf) {
+    MOE_HIP_TRY(hipDeviceSynchronize());
+    (void)hipFree(L->pf);
+    L->pf = nullptr;
+  }
+  hipError_t e = hipMalloc(&L->pf, total);
+  if (e != hipSuccess) return fail(MOE_E_NOMEM, "prefill workspace hipMalloc(%zu): %s", total,
+                                   hipGetErrorString(e));
+  MOE_HIP_TRY(hipMemset(L->pf, 0, total));
+  uint8_t* p = static_cast<uint8_t*>(L->pf);
+  void* parts[15];
+  for (int i = 0; i < 15; ++i) {
+    parts[i] = p;
+    p += align256(sizes[i]);
+  }
+  L->wr3 = static_cast<uint16_t*>(parts[0]);
+  L->pf_logits = static_cast<float*>(parts[1]);
+  L->pf_idx = static_cast<int32_t*>(parts[2]);
+  L->pf_w = static_cast<float*>(parts[3]);
+  L->pf_sigma = static_cast<float*>(parts[4]);
+  L->pf_counts = static_cast<int32_t*>(parts[5]);
+  L->pf_row_off = static_cast<int32_t*>(parts[6]);
+  L->pf_ntiles = static_cast<int32_t*>(parts[7]);
+  L->pf_tg = static_cast<int32_t*>(parts[8]);
+  L->pf_tm = static_cast<int32_t*>(parts[9]);
+  L->pf_perm = static_cast<int32_t*>(parts[10]);
+  L->pf_inv = static_cast<int32_t*>(parts[11]);
+  L->pf_h = static_cast<uint16_t*>(parts[12]);
+  L->pf_yd = static_cast<float*>(parts[13]);
+  L->pf_dev_tab = static_cast<const uint8_t**>(parts[14]);
+  L->pf_max_tiles = mt;
+  L->pf_T = T;
+  L->wr3_ready = false;
+  if (L->pool && !L->pf_host_tab) {
+    MOE_HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&L->pf_host_tab), E * sizeof(void*),
+                              hipHostMallocDefault));
+    MOE_HIP_TRY(hipHostMalloc(reinterpret_cast<void**>(&L->pf_host_rowoff), (E + 2) * 4,
+                              hipHostMallocDefault));
+  }
+  return MOE_OK;
+}
+
+// Many tokens: MFMA router, sort by expert, grouped GEMMs, combine.
+int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16, float* y_f32,
+                        int32_t* idx_out, float* w_out, hipStream_t stream) {
+  int32_t st = ensure_prefill_ws(L, T);
+  if (st != MOE_OK) return st;
+  const moe_layer_cfg& c = L->cfg;
+  const int E = c.experts, k = c.top_k, H = c.hidden;
+  if (!L->wr3_ready) {
+    MOE_HIP_TRY(launch_split_router(L->Wr, L->wsg, E, H, L->wr3, stream));
+    L->wr3_ready = true;
+  }
+  MOE_HIP_TRY(launch_router_gemm(x, T, H, L->wr3, L->rb, 1, E, L->pf_logits, L->pf_sigma, stream));
+  RouteArgs r{};
+  r.T = T;
+  r.H = H;
+  r.E = E;
+  r.k = k;
+  r.wsg = L->wsg;
+  r.logits = L->pf_logits;
+  r.idx = idx_out ? idx_out : L->pf_idx;
+  r.w = w_out ? w_out : L->pf_w;
+  r.sigma = L->pf_sigma;
+  r.counts = L->pf_counts;
+  MOE_HIP_TRY(launch_topk_only(r, stream));
+
+  PrefillArgs p{};
+  p.T = T;
+  p.H = H;
+  p.I = c.inter;
+  p.Is = c.shared_inter;
+  p.E = E;
+  p.k = k;
+  p.bits = c.bits;
+  p.hI = L->hI;
+  p.x = x;
+  p.idx = r.idx;
+  p.w = r.w;
+  p.sigma = L->pf_sigma;
+  p.counts = L->pf_counts;
+  p.row_off = L->pf_row_off;
+  p.n_tiles = L->pf_ntiles;
+  p.tile_group = L->pf_tg;
+  p.tile_m0 = L->pf_tm;
+  p.max_tiles = L->pf_max_tiles;
+  p.perm_tok = L->pf_perm;
+  p.inv = L->pf_inv;
+  p.stride = L->lay_r.stride;
+  p.lr = to_qlayout(L->lay_r);
+  p.ls = to_qlayout(L->lay_s);
+  p.shared_blob = L->shared_blob;
+  p.h = L->pf_h;
+  p.yd = L->pf_yd;
+  p.y_f32 = y_f32;
+  p.y_bf16 = y_bf16;
+  MOE_HIP_TRY(launch_prefill_sort(p, stream));
+
+  std::vector<int32_t> used;
+  if (L->pool) {
+    MOE_HIP_TRY(hipMemcpyAsync(L->pf_host_rowoff, L->pf_row_off, (E + 2) * 4,
+                               hipMemcpyDeviceToHost, stream));
+    MOE_HIP_TRY(hipStreamSynchronize(stream));
+    for (int e = 0; e < E; ++e)
+      if (L->pf_host_rowoff[e + 1] > L->pf_host_rowoff[e]) used.push_back(e);
+    std::vector<const void*> ptrs(used.size());
+    st = slotpool_acquire(L->pool, c.layer_index, used.data(), (int)used.size(), stream,
+                          ptrs.data(), nullptr);
+    if (st != MOE_OK) return st;
+    for (int e = 0; e < E; ++e) L->pf_host_tab[e] = nullptr;
+    for (size_t i = 0; i < used.size(); ++i)
+      L->pf_host_tab[used[i]] = static_cast<const uint8_t*>(ptrs[i]);
+    MOE_HIP_TRY(hipMemcpyAsync(L->pf_dev_tab, L->pf_host_tab, E * sizeof(void*),
+                               hipMemcpyHostToDevice, stream));
+    p.routed_base = nullptr;
+    p.slot_ptrs = L->pf_dev_tab;
+  } else {
+    p.routed_base = L->resident_base + (int64_t)c.layer_index * E * L->lay_r.stride;
+  }
+  timer_mark(MOE_KERNEL_GATE_UP, true, stream);
+  hipError_t e = launch_prefill_gemms(p, stream);
+  timer_mark(MOE_KERNEL_GATE_UP, false, stream);
+  if (L->pool) {
+    st = slotpool_release(L->pool, c.layer_index, used.data(), (int)used.size(), stream);
+    if (st != MOE_OK) return st;
+  }
+  MOE_HIP_TRY(e);
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -219,7 +400,19 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
   r.idx = idx;
   r.w = w;
   r.sigma = sigma;
-  MOE_HIP_TRY(launch_route(r, stream));
+  if (T <= MOE_MAX_DECODE_T) {
+    MOE_HIP_TRY(launch_route(r, stream));
+  } else {
+    // many tokens: router on bf16 MFMA with Wr split into three exact planes
+    uint16_t* wr3 = nullptr;
+    MOE_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&wr3), (size_t)3 * (E + 1) * H * 2, stream));
+    hipError_t e = launch_split_router(Wr, r.wsg, E, H, wr3, stream);
+    if (e == hipSuccess)
+      e = launch_router_gemm(x, T, H, wr3, rb, r.wsg ? 1 : 0, E, logits, sigma, stream);
+    hipError_t e2 = hipFreeAsync(wr3, stream);
+    MOE_HIP_TRY(e);
+    MOE_HIP_TRY(e2);
+  }
   MOE_HIP_TRY(launch_topk_only(r, stream));
   return MOE_OK;
 }
@@ -374,7 +567,8 @@ int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T, uint16
   clear_error();
   MOE_REQUIRE(layer && x && y_bf16, "null argument");
   MOE_REQUIRE(T >= 1, "T must be >= 1");
-  MOE_REQUIRE(T <= MOE_MAX_DECODE_T, "T = %d: the many-token path is not available", T);
+  if (T > MOE_MAX_DECODE_T)
+    return forward_prefill(layer, x, T, y_bf16, y_f32, idx_out, w_out, stream);
   return forward_decode(layer, x, nullptr, nullptr, T, y_bf16, y_f32 ? y_f32 : layer->y, idx_out,
                         w_out, stream);
 }
@@ -386,6 +580,9 @@ int32_t moe_layer_destroy(moe_layer* layer) {
   if (layer->ws) (void)hipFree(layer->ws);
   if (layer->host_slots) (void)hipHostFree(layer->host_slots);
   if (layer->host_ptrs) (void)hipHostFree(layer->host_ptrs);
+  if (layer->pf) (void)hipFree(layer->pf);
+  if (layer->pf_host_tab) (void)hipHostFree(layer->pf_host_tab);
+  if (layer->pf_host_rowoff) (void)hipHostFree(layer->pf_host_rowoff);
   delete layer;
   if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
   return MOE_OK;

@@ -109,6 +109,9 @@ __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_s
       }
     }
     if (a.sigma && a.wsg) a.sigma[t] = 1.0f / (1.0f + expf(-ld_dev(a.sigma + t)));
+    if (a.counts) {
+      for (int j = 0; j < k; ++j) atomicAdd(a.counts + s_sel[r * k + j], 1);
+    }
   }
 }
 

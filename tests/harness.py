@@ -91,19 +91,31 @@ def rel_err(y_gpu, y_ref) -> float:
     return float(np.max(np.abs(y_gpu - y_ref)) / (den if den > 0 else 1.0))
 
 
-def logit_bounds(x, Wr, rb):
+def gemv_depth(H):
+    """Summation depth of the per-token router: 4 products per lane per
+    256-column step (H/256 steps at most), a 6-level butterfly, the two
+    half-rows and the bias."""
+    return 4 * (H // 256) + 10
+
+
+def mfma_depth(H):
+    """Summation depth of the many-token router: per 64-wide K group, 3 bf16
+    planes x 4 MFMA steps of 16 products each (192 additions, counted as if
+    sequential), then one addition per group into the total, then the bias."""
+    return 3 * 64 + H // 64 + 2
+
+
+def logit_bounds(x, Wr, rb, depth=None):
     """Per-expert bound on |f32 logit - exact logit|: gamma_D * (sum_h |x_h
     Wr[e,h]| + |rb_e|), the classic bound for a sum evaluated by a tree of
-    depth D.  The router sums 4 products per lane per 256-column step
-    (H/256 steps at most), then a 6-level butterfly, the two half-rows and the
-    bias, so D = 4*H/256 + 10 bounds its depth."""
+    depth D (see gemv_depth / mfma_depth)."""
     x = np.asarray(x, np.float64)
-    n = 4 * (x.shape[-1] // 256) + 10
+    n = depth if depth is not None else gemv_depth(x.shape[-1])
     gamma = n * U32 / (1 - n * U32)
     return gamma * (np.abs(np.asarray(Wr, np.float64)) @ np.abs(x) + np.abs(np.asarray(rb, np.float64)))
 
 
-def check_routing(idx_gpu, logits_gpu, x, Wr, rb, k, w_gpu=None):
+def check_routing(idx_gpu, logits_gpu, x, Wr, rb, k, w_gpu=None, depth=None):
     """Routing parity for one token.
 
     (i) the GPU's selection equals the oracle's selection rule applied to the
@@ -113,7 +125,7 @@ def check_routing(idx_gpu, logits_gpu, x, Wr, rb, k, w_gpu=None):
     Returns True if (ii) applied (the token was decidable)."""
     idx_gpu = np.asarray(idx_gpu, np.int64)
     exact = O.router_logits(x, Wr, rb)
-    B = logit_bounds(x, Wr, rb)
+    B = logit_bounds(x, Wr, rb, depth)
     if logits_gpu is not None:
         lg = np.asarray(logits_gpu, np.float64)
         assert np.array_equal(idx_gpu, O.select_topk(lg, k)), "GPU top-k differs from its logits"

@@ -11,8 +11,8 @@ import pytest
 from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, token_x, tokens_x
 from oracle import moe_oracle as O
 
-from harness import (REL_TOL, DeviceModel, check_bf16_of_f32, check_routing, oracle_layer,
-                     rel_err)
+from harness import (REL_TOL, DeviceModel, check_bf16_of_f32, check_routing, mfma_depth,
+                     oracle_layer, oracle_tokens, rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +80,10 @@ def test_route_topk(torch, name, T):
         torch.cuda.synchronize()
         idx, w = out["idx"].cpu().numpy(), out["w"].cpu().numpy()
         lg, sg = out["logits"].cpu().numpy(), out["sigma"].cpu().numpy()
+        depth = mfma_depth(cfg.hidden) if T > 8 else None
         for t in range(T):
             x = O.bf16_to_f64(xb[t])
-            decided += check_routing(idx[t], lg[t], x, Wr, rb, cfg.top_k, w[t])
+            decided += check_routing(idx[t], lg[t], x, Wr, rb, cfg.top_k, w[t], depth=depth)
             s_ref = O.sigmoid(np.dot(wsg.astype(np.float64), x))
             assert abs(sg[t] - s_ref) <= 1e-6
     assert decided >= 0.9 * 2 * T
@@ -306,3 +307,119 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
         dm.destroy()
         m.slotpool_destroy(pool)
         m.expert_store_destroy(store)
+
+
+# ------------------------------------------------------------------ prefill
+
+def _prefill_run(torch, m, L, cfg, xb):
+    T = xb.shape[0]
+    y16 = torch.empty((T, cfg.hidden), dtype=torch.int16, device="cuda")
+    y32 = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    m.moe_layer_forward(L, torch.from_numpy(xb.view(np.int16)).cuda(), y16, y32, idx, w)
+    torch.cuda.synchronize()
+    return y16.cpu().numpy(), y32.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _prefill_case(torch, cfg, T, t0=0):
+    """Many-token call against the oracle's bf16-weight mode on every token."""
+    import int4_group_quantized_router_amd as m
+    dm = DeviceModel(cfg, layers=1)
+    L = dm.make_layers()[0]
+    try:
+        xb = tokens_x(cfg, t0, T)
+        y16, y32, idx, w = _prefill_run(torch, m, L, cfg, xb)
+        ref = oracle_tokens(cfg, 0, xb, bf16_weights=True)
+        Wr, rb, _ = router_arrays(cfg, 0)
+        same, worst = 0, 0.0
+        for t in range(T):
+            check_routing(idx[t], None, O.bf16_to_f64(xb[t]), Wr, rb, cfg.top_k,
+                          depth=mfma_depth(cfg.hidden))
+            if np.array_equal(idx[t], ref["idx"][t]):
+                same += 1
+                err = rel_err(y32[t], ref["y"][t])
+                worst = max(worst, err)
+                assert err <= REL_TOL, (t, err)
+        assert same >= 0.95 * T
+        check_bf16_of_f32(y16, y32)
+        assert np.allclose(w.sum(axis=1), 1.0, atol=cfg.top_k * 2 ** -23 + 1e-7)
+        _print("prefill", cfg.name, T, "worst rel err", worst, "routing equal", same, "/", T)
+        return dm, L, xb, y32
+    except Exception:
+        dm.destroy()
+        raise
+
+
+@pytest.mark.parametrize("T", [9, 64, 200])
+def test_prefill_tiny(torch, T):
+    dm, *_ = _prefill_case(torch, CONFIGS["tiny"], T)
+    dm.destroy()
+
+
+@pytest.mark.parametrize("name,T", [("prefill80b", 300), ("decode80b_int8", 200)])
+def test_prefill_reduced_experts(torch, name, T):
+    cfg = CONFIGS[name].replace(layers=1, experts=64, top_k=4, zipf=None)
+    dm, *_ = _prefill_case(torch, cfg, T)
+    dm.destroy()
+
+
+def test_prefill_token_permutation_is_bitwise(torch):
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["prefill80b"].replace(layers=1, experts=64, top_k=4)
+    dm = DeviceModel(cfg, layers=1)
+    L = dm.make_layers()[0]
+    try:
+        xb = tokens_x(cfg, 0, 300)
+        perm = np.random.default_rng(3).permutation(300)
+        _, y_a, idx_a, _ = _prefill_run(torch, m, L, cfg, xb)
+        _, y_b, idx_b, _ = _prefill_run(torch, m, L, cfg, xb[perm])
+        assert np.array_equal(idx_a[perm], idx_b)
+        assert np.array_equal(y_a[perm].view(np.uint32), y_b.view(np.uint32))
+    finally:
+        dm.destroy()
+
+
+def test_prefill_full_size_sampled(torch):
+    """4096 tokens, 512 experts, top-10: every invariant on all tokens, the
+    oracle on a sample of tokens (per token, bf16-weight mode)."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["prefill80b"]
+    dm = DeviceModel(cfg, layers=1)
+    L = dm.make_layers()[0]
+    try:
+        xb = tokens_x(cfg, 0, cfg.tokens)
+        y16, y32, idx, w = _prefill_run(torch, m, L, cfg, xb)
+        assert np.all(np.isfinite(y32))
+        check_bf16_of_f32(y16, y32)
+        assert np.allclose(w.sum(axis=1), 1.0, atol=cfg.top_k * 2 ** -23 + 1e-7)
+        assert all(len(set(r)) == cfg.top_k for r in idx.tolist())
+        Wr, rb, _ = router_arrays(cfg, 0)
+        for t in [0, 1, 127, 128, 2047, 4000, 4094, 4095]:
+            ref = oracle_layer(cfg, 0, xb[t], bf16_weights=True)
+            check_routing(idx[t], None, O.bf16_to_f64(xb[t]), Wr, rb, cfg.top_k,
+                          depth=mfma_depth(cfg.hidden))
+            if np.array_equal(idx[t], ref["idx"]):
+                assert rel_err(y32[t], ref["y"]) <= REL_TOL
+    finally:
+        dm.destroy()
+
+
+def test_decode_and_prefill_agree(torch):
+    """The same tokens through the per-token path (T <= 8) and the many-token
+    path: each against its own oracle mode elsewhere; here, against each
+    other (they differ by the bf16 rounding of the weights)."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["prefill80b"].replace(layers=1, experts=64, top_k=4)
+    dm = DeviceModel(cfg, layers=1)
+    L = dm.make_layers()[0]
+    try:
+        xb = tokens_x(cfg, 0, 64)
+        _, y_p, idx_p, _ = _prefill_run(torch, m, L, cfg, xb)
+        for t0 in range(0, 64, 8):
+            _, y_d, idx_d, _ = _prefill_run(torch, m, L, cfg, xb[t0:t0 + 8])
+            for i in range(8):
+                if np.array_equal(idx_d[i], idx_p[t0 + i]):
+                    assert rel_err(y_d[i], y_p[t0 + i]) <= 1e-2
+    finally:
+        dm.destroy()
