@@ -44,6 +44,38 @@ def algorithmic_bytes(cfg):
             "layer": route + gate_up + down}
 
 
+def prefill_flops(cfg, T):
+    """MFMA FLOPs of the grouped GEMMs for one T-token call (routed + shared)."""
+    rows = T * cfg.top_k
+    gu = 2 * (rows * 2 * cfg.inter + T * 2 * cfg.shared_inter) * cfg.hidden
+    down = 2 * (rows * cfg.inter + T * cfg.shared_inter) * cfg.hidden
+    return gu, down
+
+
+def cpu_baseline_prefill(cfg, budget_s=20.0):
+    """Oracle (per token, bf16-weight mode) on the first tokens that fit the budget."""
+    import numpy as np
+    from moe_inputs import expert_arrays, router_arrays, shared_arrays, token_x
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    Wr, rb, wsg = router_arrays(cfg, 0)
+    sh = shared_arrays(cfg, 0)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s and n < cfg.tokens:
+        O.moe_layer(token_x(cfg, n), Wr, rb, wsg, sh, lambda e: expert_arrays(cfg, 0, e),
+                    cfg.top_k, cfg.bits, bf16_weights=True)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"{n} of {cfg.tokens} tokens, one at a time, in {dt:.1f} s (NumPy float64, "
+                      f"bf16-weight mode; BLAS {blas} threads)"}
+
+
 def cpu_baseline(cfg, budget_s=20.0):
     """Time the oracle on token 0 through as many layers as fit the budget."""
     import numpy as np
@@ -77,8 +109,8 @@ def cpu_baseline(cfg, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode35b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -94,7 +126,11 @@ def main():
     from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
 
     cfg = CONFIGS[args.workload]
-    assert cfg.batch == 1 and cfg.resident, "bench workload must be resident batch-1 decode"
+    if cfg.batch > 8:
+        return bench_prefill(args, cfg)
+    args.steps = 256 if args.steps is None else args.steps
+    args.warmup = 16 if args.warmup is None else args.warmup
+    assert cfg.batch == 1 and cfg.resident, "decode bench workload must be resident batch-1"
     torch.cuda.set_device(0)
     dims = {"hidden": cfg.hidden, "experts": cfg.experts, "top_k": cfg.top_k,
             "inter": cfg.inter, "shared_inter": cfg.shared_inter, "bits": cfg.bits}
@@ -190,6 +226,79 @@ def main():
     m.moe_stack_destroy(stack)
     for L in layers:
         m.moe_layer_destroy(L)
+
+
+def bench_prefill(args, cfg):
+    """One step = one MoE layer call on all cfg.tokens tokens (the prefill path)."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as W
+    from moe_inputs import expert_arrays, router_arrays, shared_arrays, tokens_x
+
+    steps = 20 if args.steps is None else args.steps
+    warmup = 3 if args.warmup is None else args.warmup
+    torch.cuda.set_device(0)
+    dims = {"hidden": cfg.hidden, "experts": cfg.experts, "top_k": cfg.top_k,
+            "inter": cfg.inter, "shared_inter": cfg.shared_inter, "bits": cfg.bits}
+    log(f"[bench] building {cfg.name}")
+    routed, _ = W.upload_resident(dims, 1, lambda l, e: expert_arrays(cfg, l, e))
+    Wr, rb, wsg = (torch.from_numpy(a).cuda() for a in router_arrays(cfg, 0))
+    sh = W.upload_blob(cfg.hidden, cfg.shared_inter, cfg.bits, shared_arrays(cfg, 0))
+    layer = m.moe_layer_create(dict(dims, layer_index=0), Wr, rb, sh, wsg, resident_base=routed)
+    T = cfg.tokens
+    X = torch.from_numpy(tokens_x(cfg, 0, T).view(np.int16)).cuda()
+    Y = torch.empty((T, cfg.hidden), dtype=torch.int16, device="cuda")
+    for _ in range(warmup):
+        m.moe_layer_forward(layer, X, Y)
+    torch.cuda.synchronize()
+    timers = {k: m.moe_timer_create(k, steps) for k in (0, 1, 2)}
+    ms = {}
+    t_all = 0.0
+    # one timer can be attached at a time: three passes over the same steps
+    for kind, name in ((1, "gate_up"), (2, "down"), (0, "route")):
+        m.moe_timer_attach(timers[kind])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            m.moe_layer_forward(layer, X, Y)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        m.moe_timer_attach(None)
+        ms[name] = float(np.mean(m.moe_timer_read(timers[kind])))
+        if kind == 1:
+            t_all = dt
+    for t in timers.values():
+        m.moe_timer_destroy(t)
+    gu_flops, dn_flops = prefill_flops(cfg, T)
+    achieved = gu_flops / (ms["gate_up"] / 1e3) / 1e12
+    both = (gu_flops + dn_flops) / ((ms["gate_up"] + ms["down"]) / 1e3) / 1e12
+    tok_s = T * steps / t_all
+    log(f"[bench] prefill {tok_s:.0f} tok/s, {t_all / steps * 1e3:.3f} ms/call; gate_up "
+        f"{ms['gate_up'] * 1e3:.1f} us, down {ms['down'] * 1e3:.1f} us, router {ms['route'] * 1e3:.1f} us")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(cfg)
+    out = {
+        "metric": "MoE layer tokens/sec, prefill (4096 tokens), 1 GPU",
+        "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": t_all / steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{cfg.bits} weights dequantised to bf16, bf16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {"workload": f"{cfg.name}: one MoE layer, {T} tokens, hidden {cfg.hidden}, "
+                               f"{cfg.experts} experts top-{cfg.top_k}, intermediate "
+                               f"{cfg.inter} + shared {cfg.shared_inter}, int{cfg.bits}",
+                   "gemm_flops_per_call": gu_flops + dn_flops,
+                   "gate_up_plus_down_TFLOPs": both,
+                   "gate_up_plus_down_frac_of_bf16_peak": both / 2500.0,
+                   "down_mean_us": ms["down"] * 1e3, "router_mean_us": ms["route"] * 1e3},
+        "roofline": {"kernel": "gu_gemm_kernel (grouped gate/up GEMM, dequant-to-bf16, MFMA)",
+                     "bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": achieved / 2500.0, "traffic": None,
+                     "flops_per_launch": gu_flops, "mean_launch_us": ms["gate_up"] * 1e3},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    m.moe_layer_destroy(layer)
 
 
 if __name__ == "__main__":

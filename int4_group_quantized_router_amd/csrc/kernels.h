@@ -107,7 +107,9 @@ hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* w
                               const float* bias, int has_wsg, int E, float* logits,
                               float* sigma_raw, hipStream_t s);
 hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s);
-hipError_t launch_prefill_gemms(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_gu(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols,
                           int bits, int which, float* out_f32, uint16_t* out_bf16,

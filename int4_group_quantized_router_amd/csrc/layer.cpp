@@ -292,7 +292,9 @@ int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16
     MOE_HIP_TRY(launch_split_router(L->Wr, L->wsg, E, H, L->wr3, stream));
     L->wr3_ready = true;
   }
+  timer_mark(MOE_KERNEL_ROUTE, true, stream);
   MOE_HIP_TRY(launch_router_gemm(x, T, H, L->wr3, L->rb, 1, E, L->pf_logits, L->pf_sigma, stream));
+  timer_mark(MOE_KERNEL_ROUTE, false, stream);
   RouteArgs r{};
   r.T = T;
   r.H = H;
@@ -359,8 +361,12 @@ int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16
     p.routed_base = L->resident_base + (int64_t)c.layer_index * E * L->lay_r.stride;
   }
   timer_mark(MOE_KERNEL_GATE_UP, true, stream);
-  hipError_t e = launch_prefill_gemms(p, stream);
+  hipError_t e = launch_prefill_gu(p, stream);
   timer_mark(MOE_KERNEL_GATE_UP, false, stream);
+  timer_mark(MOE_KERNEL_DOWN, true, stream);
+  if (e == hipSuccess) e = launch_prefill_down(p, stream);
+  timer_mark(MOE_KERNEL_DOWN, false, stream);
+  if (e == hipSuccess) e = launch_prefill_combine(p, stream);
   if (L->pool) {
     st = slotpool_release(L->pool, c.layer_index, used.data(), (int)used.size(), stream);
     if (st != MOE_OK) return st;

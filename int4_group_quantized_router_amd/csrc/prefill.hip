@@ -56,14 +56,25 @@ __device__ __forceinline__ f32x16_t mfma(const uint4& a, const uint4& b, const f
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  bf16x2_v r;
+  r.x = (__bf16)lo;
+  r.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
 
-// Work id with consecutive ids on the same XCD (grid padded to a multiple of 8).
-__device__ __forceinline__ int xcd_work_id() {
+// (tile, column tile) of this block.  Blocks are dealt round-robin to the 8
+// XCDs; tile i runs on XCD i % 8 with all its column tiles, so the column
+// tiles share the tile's rows in one L2 and the real tiles (a prefix of the
+// padded grid's tile range) spread evenly over the XCDs.
+__device__ __forceinline__ void tile_of_block(int nt_per_tile, int* tile, int* nt) {
   const int b = blockIdx.x;
-  return (b & 7) * (gridDim.x >> 3) + (b >> 3);
+  const int xcd = b & 7, j = b >> 3;
+  *tile = (j / nt_per_tile) * 8 + xcd;
+  *nt = j % nt_per_tile;
 }
 
 // Dequantise one 16-byte chunk of packed weights to bf16 (round to nearest
@@ -76,7 +87,12 @@ __device__ __forceinline__ void dequant_chunk(const uint4 raw, uint32_t sb, uint
     uint32_t o[16];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t lo = w[m] & 0x0F0F0F0Fu, hi = (w[m] >> 4) & 0x0F0F0F0Fu;
+      // nibbles to bytes; the asm keeps the optimiser from folding the masks
+      // into per-value bit-field extracts, so each byte converts with one
+      // v_cvt_f32_ubyte{0..3}
+      uint32_t lo, hi;
+      asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w[m]));
+      asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w[m] >> 4));
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // values 8m+2i (low nibble of byte i) and 8m+2i+1
         o[4 * m + i] = pack_bf16(fmaf(s, (float)((lo >> (8 * i)) & 0xFFu), b),
@@ -97,6 +113,27 @@ __device__ __forceinline__ void dequant_chunk(const uint4 raw, uint32_t sb, uint
     uint4* d = reinterpret_cast<uint4*>(dst);
     d[0] = make_uint4(o[0], o[1], o[2], o[3]);
     d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// One packed word -> bf16 values in natural order: 8 (int4, as a uint4) or
+// 4 (int8, low half of the uint4).
+template <int BITS>
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
+  if (BITS == 4) {
+    uint32_t lo, hi;
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
+    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16(fmaf(s, (float)((lo >> (8 * i)) & 0xFFu), b),
+                       fmaf(s, (float)((hi >> (8 * i)) & 0xFFu), b));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    const uint32_t o0 = pack_bf16(fmaf(s, (float)(w & 0xFFu), b), fmaf(s, (float)((w >> 8) & 0xFFu), b));
+    const uint32_t o1 = pack_bf16(fmaf(s, (float)((w >> 16) & 0xFFu), b), fmaf(s, (float)(w >> 24), b));
+    return make_uint4(o0, o1, 0u, 0u);
   }
 }
 
@@ -154,13 +191,13 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) tot[i][j] = f32x16_t{};
-  const uint4 z = make_uint4(0, 0, 0, 0);
+  // out-of-range rows / experts read row 0 (clamped above) and are never stored
   for (int kg = 0; kg < H / KG; ++kg) {
     uint4 af[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) af[rb][s] = av[rb] ? ld16(arow[rb] + kg * KG + s * 8) : z;
+      for (int s = 0; s < 4; ++s) af[rb][s] = ld16(arow[rb] + kg * KG + s * 8);
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -173,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          bf[cb][s] = bv[cb] ? ld16(brow[cb] + p * plane + kg * KG + s * 8) : z;
+          bf[cb][s] = ld16(brow[cb] + p * plane + kg * KG + s * 8);
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -275,222 +312,226 @@ __global__ __launch_bounds__(kThreads) void prefill_compact_kernel(PrefillArgs a
 }
 
 // ------------------------------------------------------ grouped GEMMs
+//
+// One kernel for both products.  Workgroup tile: 128 rows of one group x 256
+// weight rows -- for gate/up, 128 intermediate columns of gate and the same
+// 128 of up (so h = silu(g) * u is finished in registers); for down, 256
+// output columns.  Per 64-wide K group the workgroup stages the 128 A rows
+// (gathered token rows of x, or rows of h) and the 256 dequantised weight
+// rows in LDS (double-buffered), with global loads issued two groups ahead
+// through a ring of two register sets.  Eight waves (two per SIMD, so one
+// wave's dequantisation overlaps the other's MFMAs); each owns a 64-row x
+// 64-weight-row block = 2 x 2 MFMA 32x32x16 tiles, 64 f32 accumulators.
 
-// gate/up: tile = 128 rows of group g x 64 intermediate columns (gate and up).
+constexpr int BN = 256;                    // weight rows per tile
+constexpr int kGemmThreads = 512;          // 8 waves
+constexpr int kLdsA = BM * kLdsRow;        // bytes of one A stage
+constexpr int kLdsB = BN * kLdsRow;        // bytes of one B stage
+
 template <int BITS>
-__global__ __launch_bounds__(kThreads, 2) void gu_gemm_kernel(PrefillArgs a, int nt_per_tile) {
-  __shared__ __align__(16) uint8_t Bs[2][BM * kLdsRow];
-  const int wid = xcd_work_id();
-  const int tile = wid / nt_per_tile, nt = wid % nt_per_tile;
+struct GemmRegs {
+  static constexpr int CB = BN * (KG * BITS / 8) / 16 / kGemmThreads;  // B chunks per thread
+  uint4 a[2];        // A: 2 x 16 bytes per thread per K group
+  uint4 b[CB];       // B: packed weights
+  uint32_t sb[CB];   // (scale, bias) word of each B chunk's row
+};
+
+template <int BITS, bool GU>
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(PrefillArgs a,
+                                                                       int nt_per_tile) {
+  extern __shared__ __align__(16) uint8_t smem[];  // 2 x (A stage + B stage)
+  using R = GemmRegs<BITS>;
+  constexpr int CB = R::CB;
+  constexpr int GBYTES = KG * BITS / 8;  // packed bytes of one weight row per K group
+  constexpr int CPR = GBYTES / 16;       // 16-byte chunks per weight row per K group
+  int tile, nt;
+  tile_of_block(nt_per_tile, &tile, &nt);
   if (tile >= *a.n_tiles) return;
   const int g = a.tile_group[tile], m0 = a.tile_m0[tile];
   const bool shared = g == a.E;
-  const int N = shared ? a.Is : a.I;
-  const int c0 = nt * 64;
-  if (c0 >= N) return;
+  const int inner = shared ? a.Is : a.I;
+  // gate/up: N = intermediate columns (128 per tile), K = H.  down: N = H, K = inner.
+  const int c0 = nt * (GU ? BN / 2 : BN);
+  if (GU && c0 >= inner) return;
+  const int K = GU ? a.H : inner;
   const int r0 = a.row_off[g] + m0;
   const int mrows = min(BM, a.row_off[g + 1] - a.row_off[g] - m0);
   const uint8_t* blob = group_blob(a, g);
   const QLayout L = shared ? a.ls : a.lr;
-  const int H = a.H;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mh = wave >> 1, nh = wave & 1, kh = lane >> 5, l32 = lane & 31;
+  // waves w and w+4 share a SIMD: give each SIMD one low-row and one
+  // high-row wave, so skipped row blocks (below) shorten every SIMD's work
+  const int mq = wave >> 2, nq = wave & 3, kh = lane >> 5, l32 = lane & 31;
+  // row blocks of 32 entirely past the tile's rows do no MFMA work
+  const bool rb_live0 = mq * 64 < mrows, rb_live1 = mq * 64 + 32 < mrows;
 
-  const uint16_t* arow[2];
-  bool av[2];
+  // A rows this thread stages: row (tid >> 3) + 64 i, 16-byte part tid & 7.
+  // Rows past the tile read a valid row and only feed rows never stored.
+  const uint16_t* asrc[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int rl = mh * 64 + rb * 32 + l32;
-    av[rb] = rl < mrows;
-    arow[rb] = a.x + (size_t)(av[rb] ? a.perm_tok[r0 + rl] : 0) * H + kh * 32;
+  for (int i = 0; i < 2; ++i) {
+    const int rl = (tid >> 3) + 64 * i;
+    const int rr = rl < mrows ? rl : 0;
+    if (GU)
+      asrc[i] = a.x + (size_t)a.perm_tok[r0 + rr] * a.H + (tid & 7) * 8;
+    else
+      asrc[i] = a.h + (size_t)(r0 + rr) * a.hI + (tid & 7) * 8;
   }
-  constexpr int CPT = BITS == 4 ? 1 : 2;     // 16-byte chunks per thread per K group
-  constexpr int GB = KG * BITS / 8;          // packed bytes of one row in one K group
-  const int br = tid >> 1;                   // tile row: 0..63 gate, 64..127 up
-  const int wrow = c0 + (br & 63);
-  const int64_t row_bytes = (int64_t)H * BITS / 8;
-  const bool is_up = br >= 64;
-  const uint8_t* qrow = blob + (is_up ? L.q_off[1] : L.q_off[0]) + wrow * row_bytes;
-  const uint32_t* sbrow = reinterpret_cast<const uint32_t*>(
-                              blob + (is_up ? L.sb_off[1] : L.sb_off[0])) + (int64_t)wrow * (H / 64);
+  // B chunks this thread dequantises: chunk c = tid + 512 j -> row c / CPR, part c % CPR
+  const uint8_t* bsrc[CB];
+  const uint32_t* sbsrc[CB];
+  int bdst[CB];
+#pragma unroll
+  for (int j = 0; j < CB; ++j) {
+    const int c = tid + kGemmThreads * j;
+    const int br = c / CPR, part = c % CPR;
+    int m, wrow;
+    if (GU) {
+      m = br >= BN / 2 ? 1 : 0;
+      wrow = c0 + (br & (BN / 2 - 1));
+      if (wrow >= inner) wrow = 0;  // overhang of a small intermediate size: never stored
+    } else {
+      m = 2;
+      wrow = c0 + br;
+    }
+    const uint8_t* qb = blob + (m == 0 ? L.q_off[0] : m == 1 ? L.q_off[1] : L.q_off[2]);
+    const uint8_t* sbb = blob + (m == 0 ? L.sb_off[0] : m == 1 ? L.sb_off[1] : L.sb_off[2]);
+    bsrc[j] = qb + (int64_t)wrow * (K * BITS / 8) + part * 16;
+    sbsrc[j] = reinterpret_cast<const uint32_t*>(sbb) + (int64_t)wrow * (K / 64);
+    bdst[j] = kLdsA + br * kLdsRow + part * (256 / BITS);
+  }
 
+  auto load = [&](R& r, int kg) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) r.a[i] = ld16(asrc[i] + kg * KG);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      r.b[j] = ld16(bsrc[j] + kg * GBYTES);
+      r.sb[j] = sbsrc[j][kg];
+    }
+  };
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  uint4 braw[CPT], araw[2][4];
-  uint32_t bsb;
+  // weight-row base (in the B stage) of the wave's 2 column blocks
+  int bro[2];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) braw[c] = ld16(qrow + ((tid & 1) * CPT + c) * 16);
-  bsb = sbrow[0];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) araw[rb][s] = av[rb] ? ld16(arow[rb] + s * 8) : z;
+  for (int cb = 0; cb < 2; ++cb)
+    bro[cb] = GU ? (cb * (BN / 2) + nq * 32) : (nq * 64 + cb * 32);
 
-  const int NK = H / KG;
-  for (int kg = 0; kg < NK; ++kg) {
-    uint8_t* buf = Bs[kg & 1];
+  auto read_frags = [&](const uint8_t* stage, int s, uint4* af, uint4* bf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      dequant_chunk<BITS>(braw[c], bsb, buf + br * kLdsRow + ((tid & 1) * CPT + c) * (256 / BITS));
-    uint4 braw_n[CPT], araw_n[2][4];
-    uint32_t bsb_n = 0;
-    if (kg + 1 < NK) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c)
-        braw_n[c] = ld16(qrow + (kg + 1) * GB + ((tid & 1) * CPT + c) * 16);
-      bsb_n = sbrow[kg + 1];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          araw_n[rb][s] = av[rb] ? ld16(arow[rb] + (kg + 1) * KG + s * 8) : z;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 bf[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        bf[cb] = *reinterpret_cast<const uint4*>(buf + (cb * 64 + nh * 32 + l32) * kLdsRow +
-                                                 kh * 64 + s * 16);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma(araw[rb][s], bf[cb], acc[rb][cb]);
-    }
-    if (kg + 1 < NK) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) braw[c] = braw_n[c];
-      bsb = bsb_n;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) araw[rb][s] = araw_n[rb][s];
-    }
-  }
-  // acc[rb][0] = gate, acc[rb][1] = up for the same rows and columns
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int rl = mh * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
-      if (rl < mrows) {
-        const float gv = acc[rb][0][v], uv = acc[rb][1][v];
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        a.h[(size_t)(r0 + rl) * a.hI + c0 + nh * 32 + l32] = (uint16_t)f32_to_bf16(hv);
-      }
-    }
-}
-
-// down: tile = 128 rows of group g x 128 output columns.
-template <int BITS>
-__global__ __launch_bounds__(kThreads, 2) void down_gemm_kernel(PrefillArgs a, int nt_per_tile) {
-  __shared__ __align__(16) uint8_t Bs[2][BM * kLdsRow];
-  const int wid = xcd_work_id();
-  const int tile = wid / nt_per_tile, nt = wid % nt_per_tile;
-  if (tile >= *a.n_tiles) return;
-  const int g = a.tile_group[tile], m0 = a.tile_m0[tile];
-  const bool shared = g == a.E;
-  const int K = shared ? a.Is : a.I;
-  const int n0 = nt * BM;
-  const int r0 = a.row_off[g] + m0;
-  const int mrows = min(BM, a.row_off[g + 1] - a.row_off[g] - m0);
-  const uint8_t* blob = group_blob(a, g);
-  const QLayout L = shared ? a.ls : a.lr;
-  const int H = a.H;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mh = wave >> 1, nh = wave & 1, kh = lane >> 5, l32 = lane & 31;
-
-  const uint16_t* arow[2];
-  bool av[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int rl = mh * 64 + rb * 32 + l32;
-    av[rb] = rl < mrows;
-    arow[rb] = a.h + (size_t)(r0 + (av[rb] ? rl : 0)) * a.hI + kh * 32;
-  }
-  constexpr int CPT = BITS == 4 ? 1 : 2;
-  constexpr int GB = KG * BITS / 8;
-  const int br = tid >> 1;  // output column n0 + br
-  const int64_t row_bytes = (int64_t)K * BITS / 8;
-  const uint8_t* qrow = blob + L.q_off[2] + (int64_t)(n0 + br) * row_bytes;
-  const uint32_t* sbrow =
-      reinterpret_cast<const uint32_t*>(blob + L.sb_off[2]) + (int64_t)(n0 + br) * (K / 64);
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  uint4 braw[CPT], araw[2][4];
-  uint32_t bsb;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) braw[c] = ld16(qrow + ((tid & 1) * CPT + c) * 16);
-  bsb = sbrow[0];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) araw[rb][s] = av[rb] ? ld16(arow[rb] + s * 8) : z;
-
-  const int NK = K / KG;
-  for (int kg = 0; kg < NK; ++kg) {
-    uint8_t* buf = Bs[kg & 1];
-#pragma unroll
-    for (int c = 0; c < CPT; ++c)
-      dequant_chunk<BITS>(braw[c], bsb, buf + br * kLdsRow + ((tid & 1) * CPT + c) * (256 / BITS));
-    uint4 braw_n[CPT], araw_n[2][4];
-    uint32_t bsb_n = 0;
-    if (kg + 1 < NK) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c)
-        braw_n[c] = ld16(qrow + (kg + 1) * GB + ((tid & 1) * CPT + c) * 16);
-      bsb_n = sbrow[kg + 1];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          araw_n[rb][s] = av[rb] ? ld16(arow[rb] + (kg + 1) * KG + s * 8) : z;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 bf[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        bf[cb] = *reinterpret_cast<const uint4*>(buf + (nh * 64 + cb * 32 + l32) * kLdsRow +
-                                                 kh * 64 + s * 16);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma(araw[rb][s], bf[cb], acc[rb][cb]);
-    }
-    if (kg + 1 < NK) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) braw[c] = braw_n[c];
-      bsb = bsb_n;
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) araw[rb][s] = araw_n[rb][s];
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
+      af[rb] = *reinterpret_cast<const uint4*>(stage + (mq * 64 + rb * 32 + l32) * kLdsRow +
+                                               kh * 64 + s * 16);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
+      bf[cb] = *reinterpret_cast<const uint4*>(stage + kLdsA + (bro[cb] + l32) * kLdsRow +
+                                               kh * 64 + s * 16);
+  };
+  // Quarter `part` of staging a register set into LDS: the A rows (parts 0,
+  // 1) and 4*CB/4 packed words of the weight chunks, dequantised.
+  auto store_part = [&](const R& r, uint8_t* stage, int part) {
+    if (part < 2)
+      *reinterpret_cast<uint4*>(stage + ((tid >> 3) + 64 * part) * kLdsRow + (tid & 7) * 16) =
+          r.a[part];
+#pragma unroll
+    for (int f = part * CB; f < (part + 1) * CB; ++f) {
+      const int c = f / 4, m = f % 4;
+      const uint32_t wrd = m == 0 ? r.b[c].x : m == 1 ? r.b[c].y : m == 2 ? r.b[c].z : r.b[c].w;
+      const uint4 v = dequant_word<BITS>(wrd, bf16_lo(r.sb[c]), bf16_hi(r.sb[c]));
+      if (BITS == 4) {
+        *reinterpret_cast<uint4*>(stage + bdst[c] + m * 16) = v;
+      } else {
+        *reinterpret_cast<uint2*>(stage + bdst[c] + m * 8) = make_uint2(v.x, v.y);
+      }
+    }
+  };
+  // One K group: MFMAs on stage `sc` (already in LDS) interleaved with
+  // staging register set `r` into `ss`: after each group of four MFMAs (which
+  // run asynchronously on the matrix core) a quarter of the dequantisation
+  // issues on the VALU.
+  auto step = [&](const uint8_t* sc, const R& r, uint8_t* ss, bool do_store) {
+    uint4 af[2][2], bf[2][2];
+    read_frags(sc, 0, af[0], bf[0]);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      if (s4 < 3) read_frags(sc, s4 + 1, af[(s4 + 1) & 1], bf[(s4 + 1) & 1]);
+      if (rb_live0) {
+        acc[0][0] = mfma(af[s4 & 1][0], bf[s4 & 1][0], acc[0][0]);
+        acc[0][1] = mfma(af[s4 & 1][0], bf[s4 & 1][1], acc[0][1]);
+      }
+      if (rb_live1) {
+        acc[1][0] = mfma(af[s4 & 1][1], bf[s4 & 1][0], acc[1][0]);
+        acc[1][1] = mfma(af[s4 & 1][1], bf[s4 & 1][1], acc[1][1]);
+      }
+      if (do_store) {
+        __builtin_amdgcn_sched_barrier(0);
+        store_part(r, ss, s4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  const int NK = K / KG;
+  uint8_t* st0 = smem;
+  uint8_t* st1 = smem + kLdsA + kLdsB;
+  R r0_, r1_;
+  load(r0_, 0);
+  if (NK > 1) load(r1_, 1);
+#pragma unroll
+  for (int part = 0; part < 4; ++part) store_part(r0_, st0, part);
+  if (NK > 2) load(r0_, 2);
+  __syncthreads();
+  // step kg computes stage kg from LDS while staging kg+1 and loading kg+3
+  int kg = 0;
+  for (; kg + 4 < NK; kg += 2) {
+    step(st0, r1_, st1, true);
+    load(r1_, kg + 3);
+    __syncthreads();
+    step(st1, r0_, st0, true);
+    load(r0_, kg + 4);
+    __syncthreads();
+  }
+  for (; kg < NK; kg += 2) {
+    step(st0, r1_, st1, kg + 1 < NK);
+    if (kg + 3 < NK) load(r1_, kg + 3);
+    __syncthreads();
+    if (kg + 1 >= NK) break;
+    step(st1, r0_, st0, kg + 2 < NK);
+    if (kg + 4 < NK) load(r0_, kg + 4);
+    __syncthreads();
+  }
+
+  if (GU) {
+    // acc[rb][0] = gate, acc[rb][1] = up for the same rows and columns
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rl = mh * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
-        if (rl < mrows)
-          a.yd[(size_t)(r0 + rl) * H + n0 + nh * 64 + cb * 32 + l32] = acc[rb][cb][v];
+        const int rl = mq * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
+        const int col = c0 + nq * 32 + l32;
+        if (rl < mrows && col < inner) {
+          const float gv = acc[rb][0][v], uv = acc[rb][1][v];
+          const float hv = gv / (1.0f + __expf(-gv)) * uv;
+          a.h[(size_t)(r0 + rl) * a.hI + col] = (uint16_t)f32_to_bf16(hv);
+        }
       }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = mq * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
+          if (rl < mrows)
+            a.yd[(size_t)(r0 + rl) * a.H + c0 + nq * 64 + cb * 32 + l32] = acc[rb][cb][v];
+        }
+  }
 }
 
 // y[t] = sum_j w[t,j] * y_j[t] + sigma_t * y_shared[t]; one block per token.
@@ -560,24 +601,27 @@ hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_gemms(const PrefillArgs& a, hipStream_t s) {
-  const int nt_gu = std::max(a.I, a.Is) / 64;
-  const int nt_dn = a.H / BM;
-  hipError_t e;
-  if (a.bits == 4)
-    hipLaunchKernelGGL(gu_gemm_kernel<4>, dim3(pad8(a.max_tiles * nt_gu)), dim3(kThreads), 0, s,
-                       a, nt_gu);
-  else
-    hipLaunchKernelGGL(gu_gemm_kernel<8>, dim3(pad8(a.max_tiles * nt_gu)), dim3(kThreads), 0, s,
-                       a, nt_gu);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.bits == 4)
-    hipLaunchKernelGGL(down_gemm_kernel<4>, dim3(pad8(a.max_tiles * nt_dn)), dim3(kThreads), 0,
-                       s, a, nt_dn);
-  else
-    hipLaunchKernelGGL(down_gemm_kernel<8>, dim3(pad8(a.max_tiles * nt_dn)), dim3(kThreads), 0,
-                       s, a, nt_dn);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+template <int BITS, bool GU>
+hipError_t launch_grouped(const PrefillArgs& a, hipStream_t s) {
+  const int nt = GU ? (std::max(a.I, a.Is) + BN / 2 - 1) / (BN / 2) : a.H / BN;
+  const size_t lds = 2 * (size_t)(kLdsA + kLdsB);
+  hipError_t e = allow_lds(grouped_gemm_kernel<BITS, GU>, lds);
+  if (e != hipSuccess) return e;
+  const int tiles8 = pad8(a.max_tiles);  // every XCD gets tiles8 / 8 tiles x nt blocks
+  hipLaunchKernelGGL((grouped_gemm_kernel<BITS, GU>), dim3(tiles8 * nt), dim3(kGemmThreads), lds,
+                     s, a, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_gu(const PrefillArgs& a, hipStream_t s) {
+  return a.bits == 4 ? launch_grouped<4, true>(a, s) : launch_grouped<8, true>(a, s);
+}
+
+hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s) {
+  return a.bits == 4 ? launch_grouped<4, false>(a, s) : launch_grouped<8, false>(a, s);
+}
+
+hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefill_combine_kernel, dim3(a.T), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
