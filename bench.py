@@ -7,9 +7,13 @@ int4 group 64, Zipf(1.1) routing bias), all experts resident in HBM, tokens
 processed one at a time.  One step = one token through all 40 layers
 (router + gate/up + down/combine per layer, RMS rescale between layers).
 
+One-token calls run as ONE persistent kernel per token (all layers in one
+launch; ``--per-layer`` runs the three kernels per layer instead).
+
 Prints one JSON line: tokens/s, plus
-* ``roofline``: the gate/up dequant-GEMV kernel (the largest share of the
-  bytes) -- algorithmic bytes per launch / its mean launch time, measured with
+* ``roofline``: the dominant kernel -- the persistent stack kernel (or, with
+  ``--per-layer``, the gate/up dequant-GEMV kernel, the largest share of the
+  bytes): algorithmic bytes per launch / its mean launch time, measured with
   HIP events around every launch of it in the timed steps, against 8 TB/s;
 * ``cpu_baseline``: the float64 CPU oracle on a bounded sample (one token
   through all layers), converted to tokens/s.
@@ -113,6 +117,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode35b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="decode: three kernels per layer instead of one persistent kernel")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -145,7 +151,11 @@ def main():
         layers.append(m.moe_layer_create(dict(dims, layer_index=l), Wr, rb, sh, wsg,
                                          resident_base=routed))
     stack = m.moe_stack_create(layers)
-    log(f"[bench] built in {time.perf_counter() - t_build:.1f} s")
+    if args.per_layer:
+        m.moe_stack_set_persistent(stack, False)
+    persistent = m.moe_stack_persistent_active(stack)
+    log(f"[bench] built in {time.perf_counter() - t_build:.1f} s; "
+        f"{'persistent stack kernel' if persistent else 'per-layer kernels'}")
 
     n_tok = args.warmup + args.steps
     X = torch.from_numpy(tokens_x(cfg, 0, n_tok).view(np.int16)).cuda()
@@ -159,7 +169,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    timer = m.moe_timer_create(m._lib.MOE_KERNEL_GATE_UP, args.steps * cfg.layers)
+    kind = m._lib.MOE_KERNEL_STACK if persistent else m._lib.MOE_KERNEL_GATE_UP
+    timer = m.moe_timer_create(kind, args.steps * cfg.layers)
     m.moe_timer_attach(timer)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -173,11 +184,18 @@ def main():
 
     tok_s = args.steps / elapsed
     ab = algorithmic_bytes(cfg)
-    gu_mean_s = float(np.mean(gu_ms)) / 1e3
-    achieved = ab["gate_up"] / gu_mean_s / 1e9
     per_token_bytes = ab["layer"] * cfg.layers
+    k_mean_s = float(np.mean(gu_ms)) / 1e3
+    if persistent:
+        k_name = (f"stack_decode_kernel (one token through all {cfg.layers} layers: router, "
+                  f"top-k, dequant-GEMV gate/up + down, combine)")
+        k_bytes = per_token_bytes
+    else:
+        k_name = "gate_up_kernel (dequant-GEMV gate+up, fused SiLU*up)"
+        k_bytes = ab["gate_up"]
+    achieved = k_bytes / k_mean_s / 1e9
     log(f"[bench] {tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.3f} ms/token, "
-        f"gate_up mean {gu_mean_s * 1e6:.2f} us over {len(gu_ms)} launches")
+        f"kernel mean {k_mean_s * 1e6:.2f} us over {len(gu_ms)} launches")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -202,6 +220,7 @@ def main():
                         f"{cfg.experts} experts top-{cfg.top_k}, intermediate {cfg.inter} + "
                         f"shared {cfg.shared_inter}, int{cfg.bits} group 64, Zipf(1.1) bias, "
                         f"batch 1, all experts resident",
+            "launch": "one persistent kernel per token" if persistent else "3 kernels per layer",
             "batch": 1, "layers": cfg.layers, "tokens_timed": args.steps,
             "bytes_per_token": per_token_bytes,
             "stack_GBps": per_token_bytes * tok_s / 1e9,
@@ -209,15 +228,15 @@ def main():
             "layer_tokens_per_s": tok_s * cfg.layers,
         },
         "roofline": {
-            "kernel": "gate_up_kernel (dequant-GEMV gate+up, fused SiLU*up)",
+            "kernel": k_name,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": None,
-            "bytes_per_launch": ab["gate_up"],
-            "mean_launch_us": gu_mean_s * 1e6,
+            "bytes_per_launch": k_bytes,
+            "mean_launch_us": k_mean_s * 1e6,
             "launches": int(len(gu_ms)),
         },
         "cpu_baseline": cpu,

@@ -266,6 +266,17 @@ int32_t moe_layer_destroy(moe_layer* layer);
  * l > 0 takes x_l = bf16(y_{l-1} / sqrt(mean(y_{l-1}^2) + 1e-6)) (f32), a
  * weightless stand-in for the residual and norm layers between the pages'
  * MoE layers, fused into layer l's router.  All layers share H and top_k.
+ *
+ * One-token calls (T == 1) on a stack whose layers are all resident and
+ * share one shape run as ONE persistent kernel for the whole stack (one
+ * workgroup per compute unit, cooperative launch): the pages find their
+ * decode loop bound by dispatch, not IO ([ttj] "실무자가 따져볼 지점"), and
+ * this removes the launches and dependency stalls between layers.  Its
+ * outputs are bit-identical to the per-layer kernels'.  Workgroups hand
+ * data to each other through per-layer buffers owned by the stack, so calls
+ * on one stack must not overlap (use one stream).  Every wait inside the
+ * kernel is bounded (2 s); a call that ran out of time is reported as
+ * MOE_E_HIP by the next moe_stack_forward on the same stack.
  * ---------------------------------------------------------------------- */
 typedef struct moe_stack moe_stack;
 
@@ -278,6 +289,11 @@ int32_t moe_stack_create(moe_layer* const* layers, int32_t n_layers,
 int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T,
                           uint16_t* x_layers, float* y_layers, int32_t* idx,
                           float* w, uint16_t* y_last, hipStream_t stream);
+/* enable != 0 (the default): T == 1 calls take the persistent kernel when
+ * the stack qualifies; 0: always the per-layer kernels (for comparisons). */
+int32_t moe_stack_set_persistent(moe_stack* stack, int32_t enable);
+/* *active = 1 if the next T == 1 call runs the persistent kernel. */
+int32_t moe_stack_persistent_active(const moe_stack* stack, int32_t* active);
 int32_t moe_stack_destroy(moe_stack* stack);
 
 /* ------------------------------------------------------------------------
@@ -286,7 +302,12 @@ int32_t moe_stack_destroy(moe_stack* stack);
  * or stack forward is bracketed by two events recorded on the launch's
  * stream, up to `capacity` launches.  Not thread-safe; for benchmarks.
  * ---------------------------------------------------------------------- */
-enum { MOE_KERNEL_ROUTE = 0, MOE_KERNEL_GATE_UP = 1, MOE_KERNEL_DOWN = 2 };
+enum {
+  MOE_KERNEL_ROUTE = 0,
+  MOE_KERNEL_GATE_UP = 1,
+  MOE_KERNEL_DOWN = 2,
+  MOE_KERNEL_STACK = 3 /* the persistent one-token stack kernel */
+};
 
 typedef struct moe_timer moe_timer;
 

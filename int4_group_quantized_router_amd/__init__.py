@@ -297,6 +297,18 @@ def moe_stack_forward(stack, x0, y_last=None, x_layers=None, y_layers=None, idx=
     return y_last
 
 
+def moe_stack_set_persistent(stack, enable: bool) -> None:
+    _check(_lib_().moe_stack_set_persistent(_h(stack), 1 if enable else 0),
+           "moe_stack_set_persistent")
+
+
+def moe_stack_persistent_active(stack) -> bool:
+    out = C.c_int32()
+    _check(_lib_().moe_stack_persistent_active(_h(stack), C.byref(out)),
+           "moe_stack_persistent_active")
+    return bool(out.value)
+
+
 def moe_stack_destroy(stack) -> None:
     _check(_lib_().moe_stack_destroy(_h(stack)), "moe_stack_destroy")
 

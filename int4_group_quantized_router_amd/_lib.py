@@ -19,7 +19,7 @@ MOE_E_RANGE = -4
 MOE_E_POOL_EXHAUSTED = -5
 MOE_E_BUSY = -6
 MOE_MAX_TOPK = 16
-MOE_KERNEL_ROUTE, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN = 0, 1, 2
+MOE_KERNEL_ROUTE, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_STACK = 0, 1, 2, 3
 MOE_MAX_DECODE_T = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_NOMEM", -3: "MOE_E_HIP",
@@ -81,6 +81,8 @@ SIGNATURES = {
     "moe_layer_destroy": [_P],
     "moe_stack_create": [_P, _I32, C.POINTER(_P)],
     "moe_stack_forward": [_P, _P, _I32, _P, _P, _P, _P, _P, _P],
+    "moe_stack_set_persistent": [_P, _I32],
+    "moe_stack_persistent_active": [_P, C.POINTER(_I32)],
     "moe_stack_destroy": [_P],
     "moe_timer_create": [_I32, _I32, C.POINTER(_P)],
     "moe_timer_attach": [_P],

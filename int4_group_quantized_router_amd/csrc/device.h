@@ -37,18 +37,35 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64);
-// every lane of a group ends with the same value (butterfly; addition order
-// is the same for every lane up to commutativity, so the bits agree).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+// Cross-lane moves without LDS: DPP (data-parallel primitives) and readlane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-template <int WIDTH>
-__device__ __forceinline__ float group_sum_c(float v) {
-#pragma unroll
-  for (int off = WIDTH >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+// Sum over aligned groups of `width` lanes (a power of two <= 64); every
+// lane of a group ends with the same bits.  Inside 16 lanes a butterfly of
+// DPP adds: lane^1, lane^2 (quad permutes), then the 8- and 16-lane mirrors,
+// which pair lanes of the two halves once the halves are uniform.  The four
+// 16-lane sums r0..r3 then meet through readlane as r0+r1 (width 32) or
+// (r0+r1)+(r2+r3) (width 64).  Every wave-level reduction of the decode
+// kernels uses this one order.  All lanes must be active.
+__device__ __forceinline__ float group_sum(float v, int width) {
+  if (width >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if (width >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if (width >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if (width >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  if (width >= 32) {
+    const float r0 = readlane_f32(v, 0), r1 = readlane_f32(v, 16);
+    const float r2 = readlane_f32(v, 32), r3 = readlane_f32(v, 48);
+    if (width == 32)
+      v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+    else
+      v = (r0 + r1) + (r2 + r3);
+  }
   return v;
 }
 
@@ -86,6 +103,12 @@ __device__ __forceinline__ int32_t ld_dev(const int32_t* p) {
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ uint32_t ticket(uint32_t* counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -105,10 +128,13 @@ __device__ __forceinline__ uint64_t lanes_below() {
 
 // Top-k of up to 64*VPL logits held by one wave (value i of lane l is
 // expert l + 64 i, invalid entries key 0), ordered by (logit desc, index
-// asc).  k-th largest key by a 32-step bitwise search with ballot counts,
-// then the k winners (ties at the threshold: lowest indices) are compacted
-// to LDS and ranked.  Results: sel_e[j], sel_v[j] for j < k (LDS, wave's own
-// scratch of >= k entries each).  All lanes must call it.
+// asc).  A bitwise search from the top bit finds a threshold key t with at
+// least k keys >= t, stopping early as soon as exactly k are (then those k
+// are the answer); otherwise it ends at the k-th largest key and ties at t
+// go to the lowest indices.  The k winners are compacted to LDS and ranked
+// by broadcasting each one's key (readlane).  Results: sel_e[j], sel_v[j]
+// for j < k (LDS; tmp_e / tmp_v: the wave's own scratch of >= k entries).
+// All lanes must call it.
 template <int VPL>
 __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e, float* tmp_v,
                           int* sel_e, float* sel_v) {
@@ -119,7 +145,10 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) thr = cand;
+    if (cnt >= k) {
+      thr = cand;
+      if (cnt == k) break;
+    }
   }
   int n_gt = 0;
 #pragma unroll
@@ -144,16 +173,19 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  if (lane < k) {
-    const int e = tmp_e[lane];
-    const float x = tmp_v[lane];
-    const uint32_t kx = order_key(x);
-    int r = 0;
-    for (int m = 0; m < k; ++m) {
-      const uint32_t km = order_key(tmp_v[m]);
-      const int em = tmp_e[m];
+  const int e = lane < k ? tmp_e[lane] : 0;
+  const float x = lane < k ? tmp_v[lane] : 0.f;
+  const uint32_t kx = order_key(x);
+  int r = 0;
+#pragma unroll
+  for (int m = 0; m < MOE_MAX_TOPK; ++m) {
+    if (m < k) {
+      const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)kx, m);
+      const int em = __builtin_amdgcn_readlane(e, m);
       r += (km > kx) || (km == kx && em < e);
     }
+  }
+  if (lane < k) {
     sel_e[r] = e;
     sel_v[r] = x;
   }

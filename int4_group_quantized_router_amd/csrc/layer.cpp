@@ -66,6 +66,13 @@ struct moe_layer {
 
 struct moe_stack {
   std::vector<moe_layer*> layers;
+  // persistent one-token path (set up at create when the stack qualifies)
+  bool persistent_enabled;
+  bool persistent_ok;
+  int grid;
+  void* ps_mem;                 // device: layer table, hand-off buffers, epochs
+  int32_t* err_host;            // pinned, written by the kernel on a timeout
+  moe::StackArgs ps;            // constant part of the kernel arguments
 };
 
 struct moe_timer {
@@ -207,6 +214,103 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
     if (st != MOE_OK) return st;
   }
   MOE_HIP_TRY(e2);
+  return MOE_OK;
+}
+
+// Sets up the persistent one-token path if every layer is resident, all
+// layers share one shape and the device runs cooperative launches.  A stack
+// that does not qualify keeps persistent_ok = false (not an error).
+int32_t setup_persistent(moe_stack* st) {
+  st->persistent_ok = false;
+  const moe_layer* L0 = st->layers[0];
+  const moe_layer_cfg& c = L0->cfg;
+  const int n = (int)st->layers.size();
+  for (const moe_layer* L : st->layers) {
+    const moe_layer_cfg& d = L->cfg;
+    if (L->pool || !L->resident_base || L->device != L0->device) return MOE_OK;
+    if (d.hidden != c.hidden || d.experts != c.experts || d.top_k != c.top_k ||
+        d.inter != c.inter || d.shared_inter != c.shared_inter || d.bits != c.bits)
+      return MOE_OK;
+    if ((L->wsg != nullptr) != (L0->wsg != nullptr) ||
+        (L->shared_blob != nullptr) != (L0->shared_blob != nullptr))
+      return MOE_OK;
+  }
+  int coop = 0, cus = 0, clk_khz = 0;
+  MOE_HIP_TRY(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, L0->device));
+  MOE_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L0->device));
+  MOE_HIP_TRY(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, L0->device));
+  if (!coop || cus < 1 || clk_khz < 1) return MOE_OK;
+  const int H = c.hidden, E = c.experts, k = c.top_k;
+  if (!stack_decode_supported(H, E, k, c.inter, c.shared_inter, c.bits, cus)) return MOE_OK;
+  const int hwords = k * c.inter + (L0->shared_blob ? c.shared_inter : 0);
+  const int R = (H + cus - 1) / cus;
+  const size_t sizes[] = {
+      (size_t)n * sizeof(StackLayerDesc),
+      (size_t)n * kStackReplicas * H * 8,         // ybuf
+      (size_t)n * kStackReplicas * (E + 1) * 8,   // lbuf
+      (size_t)n * kStackReplicas * hwords * 4,    // hbuf
+      (size_t)cus * 4,               // epochs
+  };
+  size_t total = 0;
+  for (size_t sz : sizes) total += align256(sz);
+  hipError_t e = hipMalloc(&st->ps_mem, total);
+  if (e != hipSuccess) return fail(MOE_E_NOMEM, "stack hand-off buffers hipMalloc(%zu): %s", total,
+                                   hipGetErrorString(e));
+  uint8_t* p = static_cast<uint8_t*>(st->ps_mem);
+  void* parts[5];
+  for (int i = 0; i < 5; ++i) {
+    parts[i] = p;
+    p += align256(sizes[i]);
+  }
+  std::vector<StackLayerDesc> descs(n);
+  for (int l = 0; l < n; ++l) {
+    const moe_layer* L = st->layers[l];
+    descs[l].Wr = L->Wr;
+    descs[l].rb = L->rb;
+    descs[l].wsg = L->wsg;
+    descs[l].shared_blob = L->shared_blob;
+    descs[l].routed_base =
+        L->resident_base + (int64_t)L->cfg.layer_index * E * L->lay_r.stride;
+  }
+  // zeroed hand-off words carry tag 0, which no call uses
+  e = hipMemset(st->ps_mem, 0, total);
+  if (e == hipSuccess)
+    e = hipMemcpy(parts[0], descs.data(), sizes[0], hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipHostMalloc(reinterpret_cast<void**>(&st->err_host), sizeof(int32_t),
+                      hipHostMallocDefault);
+  if (e != hipSuccess) {
+    (void)hipFree(st->ps_mem);
+    st->ps_mem = nullptr;
+    return fail(MOE_E_HIP, "stack setup: %s", hipGetErrorString(e));
+  }
+  *st->err_host = 0;
+  StackArgs& a = st->ps;
+  a = StackArgs{};
+  a.layers = static_cast<const StackLayerDesc*>(parts[0]);
+  a.L = n;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.I = c.inter;
+  a.Is = c.shared_inter;
+  a.bits = c.bits;
+  a.hwords = hwords;
+  a.has_wsg = L0->wsg != nullptr;
+  a.has_shared = L0->shared_blob != nullptr;
+  a.stride = L0->lay_r.stride;
+  a.lr = to_qlayout(L0->lay_r);
+  a.ls = to_qlayout(L0->lay_s);
+  a.ybuf = static_cast<uint64_t*>(parts[1]);
+  a.lbuf = static_cast<uint64_t*>(parts[2]);
+  a.hbuf = static_cast<uint32_t*>(parts[3]);
+  a.epochs = static_cast<uint32_t*>(parts[4]);
+  a.err = st->err_host;
+  a.timeout_ticks = (int64_t)clk_khz * 1000 * 2;  // 2 s
+  a.rows_per_wg = R;
+  a.lds_bytes = stack_lds_bytes(H, E, k, hwords, R);
+  st->grid = cus;
+  st->persistent_ok = true;
   return MOE_OK;
 }
 
@@ -606,6 +710,12 @@ int32_t moe_stack_create(moe_layer* const* layers, int32_t n_layers, moe_stack**
   moe_stack* s = new (std::nothrow) moe_stack{};
   if (!s) return fail(MOE_E_NOMEM, "host allocation failed");
   s->layers.assign(layers, layers + n_layers);
+  s->persistent_enabled = true;
+  int32_t st = setup_persistent(s);
+  if (st != MOE_OK) {
+    delete s;
+    return st;
+  }
   *out = s;
   return MOE_OK;
 }
@@ -616,6 +726,24 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
   clear_error();
   MOE_REQUIRE(stack && x0 && y_last, "null argument");
   MOE_REQUIRE(T >= 1 && T <= MOE_MAX_DECODE_T, "T must be in [1, %d]", MOE_MAX_DECODE_T);
+  if (stack->err_host && *stack->err_host) {
+    *stack->err_host = 0;
+    return fail(MOE_E_HIP, "an earlier persistent decode call on this stack timed out");
+  }
+  if (T == 1 && stack->persistent_ok && stack->persistent_enabled) {
+    StackArgs a = stack->ps;
+    a.x0 = x0;
+    a.x_layers = x_layers;
+    a.y_layers = y_layers;
+    a.idx = idx;
+    a.w = w;
+    a.y_last = y_last;
+    timer_mark(MOE_KERNEL_STACK, true, stream);
+    hipError_t e = launch_stack_decode(a, stack->grid, stream);
+    timer_mark(MOE_KERNEL_STACK, false, stream);
+    MOE_HIP_TRY(e);
+    return MOE_OK;
+  }
   const int n = (int)stack->layers.size();
   const int H = stack->layers[0]->cfg.hidden, k = stack->layers[0]->cfg.top_k;
   const float* prev = nullptr;
@@ -633,14 +761,37 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
   return MOE_OK;
 }
 
+int32_t moe_stack_set_persistent(moe_stack* stack, int32_t enable) {
+  clear_error();
+  MOE_REQUIRE(stack, "null argument");
+  stack->persistent_enabled = enable != 0;
+  return MOE_OK;
+}
+
+int32_t moe_stack_persistent_active(const moe_stack* stack, int32_t* active) {
+  clear_error();
+  MOE_REQUIRE(stack && active, "null argument");
+  *active = (stack->persistent_ok && stack->persistent_enabled) ? 1 : 0;
+  return MOE_OK;
+}
+
 int32_t moe_stack_destroy(moe_stack* stack) {
+  clear_error();
+  if (!stack) return MOE_OK;
+  hipError_t e = hipSuccess;
+  if (stack->ps_mem) {
+    e = hipDeviceSynchronize();
+    (void)hipFree(stack->ps_mem);
+  }
+  if (stack->err_host) (void)hipHostFree(stack->err_host);
   delete stack;
+  if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 
 int32_t moe_timer_create(int32_t kernel, int32_t capacity, moe_timer** out) {
   clear_error();
-  MOE_REQUIRE(out && capacity >= 1 && kernel >= MOE_KERNEL_ROUTE && kernel <= MOE_KERNEL_DOWN,
+  MOE_REQUIRE(out && capacity >= 1 && kernel >= MOE_KERNEL_ROUTE && kernel <= MOE_KERNEL_STACK,
               "bad argument");
   moe_timer* t = new (std::nothrow) moe_timer{};
   if (!t) return fail(MOE_E_NOMEM, "host allocation failed");

@@ -211,6 +211,7 @@ def test_stack_teacher_forced(torch):
     layers = dm.make_layers()
     st = m.moe_stack_create(layers)
     H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    assert m.moe_stack_persistent_active(st)  # one-token calls: one launch per stack
     try:
         for tok in range(3):
             T = 1
@@ -234,6 +235,46 @@ def test_stack_teacher_forced(torch):
                     diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
                     assert diff.max() <= 1
             check_bf16_of_f32(ylast.cpu().numpy(), yl_[L - 1])
+    finally:
+        m.moe_stack_destroy(st)
+        dm.destroy()
+
+
+@pytest.mark.parametrize("name,L", [("tiny", 3), ("decode35b", 6), ("stream80b", 2),
+                                    ("decode80b_int8", 2)])
+def test_stack_persistent_matches_per_layer(torch, name, L):
+    """The one-launch stack kernel computes every value with the per-layer
+    kernels' arithmetic in the same order: all exports equal bit for bit, over
+    consecutive calls whose hand-off buffers still hold the previous call's
+    words."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS[name].replace(layers=L)
+    _print("stack persistent vs per-layer", name, L)
+    dm = DeviceModel(cfg)
+    st = m.moe_stack_create(dm.make_layers())
+    H, k = cfg.hidden, cfg.top_k
+    try:
+        assert m.moe_stack_persistent_active(st)
+        for tok in range(4):
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            outs = []
+            for persistent in (True, False):
+                m.moe_stack_set_persistent(st, persistent)
+                xl = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+                yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                w = torch.empty((L, 1, k), dtype=torch.float32, device="cuda")
+                y = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx, w=w)
+                torch.cuda.synchronize()
+                outs.append([t.cpu().numpy().view(np.uint32 if t.element_size() == 4 else np.uint16)
+                             for t in (y, xl, yl, idx, w)])
+            for got, want, what in zip(outs[0], outs[1], ("y", "x_layers", "y_layers", "idx", "w")):
+                assert np.array_equal(got, want), (name, tok, what)
+            # no exports: only the stack's own hand-off buffers
+            m.moe_stack_set_persistent(st, True)
+            y = m.moe_stack_forward(st, x0)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), outs[1][0])
     finally:
         m.moe_stack_destroy(st)
         dm.destroy()
