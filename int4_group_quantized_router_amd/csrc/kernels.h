@@ -115,26 +115,26 @@ hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t s);
 // compute unit runs every layer; workgroups hand data to each other through
 // tagged words (value and call tag in one atomic store), so no grid barrier
 // and no kernel boundary sits between the steps of a layer or between layers.
+// Shapes are compile-time (one instance per supported model shape).
 constexpr int kStackThreads = 512;
-constexpr int kStackGuPasses = 4;    // gate/up row groups per wave per layer (max)
-constexpr int kStackDownItems = 8;   // down row groups per wave per layer (max)
-constexpr int kStackHPairs = 32;     // staged h pairs per thread (max)
-constexpr int kStackReplicas = 8;    // copies of every hand-off word (one per XCD)
+constexpr int kStackGrid = 256;       // workgroups: one per compute unit of MI355X
+constexpr int kStackReplicas = 8;     // copies of every hand-off word (one per XCD)
+constexpr int kStackMaxLayers = 64;   // layer descriptors kept in LDS
 
 struct StackLayerDesc {
   const float* Wr;              // f32 [E, H]
   const float* rb;              // f32 [E] or NULL
   const float* wsg;             // f32 [H] or NULL
-  const uint8_t* shared_blob;   // or NULL
+  const uint8_t* shared_blob;   // shared expert
   const uint8_t* routed_base;   // device address of blob (l, 0)
 };
 
 struct StackArgs {
   const StackLayerDesc* layers; // device [L]
-  int L, H, E, k, I, Is, bits, has_wsg, has_shared;
-  int hwords;                   // h words per layer: k * I + (has_shared ? Is : 0)
-  int64_t stride;
-  QLayout lr, ls;
+  int L, E, has_wsg;
+  int64_t stride;               // routed blob stride
+  uint32_t lq[3], lsb[3];       // routed blob: q / (s,b) section offsets (gate, up, down)
+  uint32_t sq[3], ssb[3];       // shared blob
   const uint16_t* x0;           // bf16 [H]
   uint16_t* x_layers;           // bf16 [L][H] or NULL
   float* y_layers;              // f32 [L][H] or NULL
@@ -144,20 +144,19 @@ struct StackArgs {
   // hand-off words, per layer and replica (value | tag)
   uint64_t* ybuf;               // [L][replica][H]: f32 bits | tag << 32
   uint64_t* lbuf;               // [L][replica][E + 1]
-  uint32_t* hbuf;               // [L][replica][hwords]: slot j < k at j * I, shared at
+  uint32_t* hbuf;               // [L][replica][k * I + Is]: slot j < k at j * I, shared at
                                 // k * I; bf16 << 16 | 16-bit tag
   uint32_t* epochs;             // [grid]: calls completed, one counter per workgroup
   int32_t* err;                 // host-visible word set on a wait timeout
   int64_t timeout_ticks;        // wall-clock ticks a workgroup may wait in total
-  int rows_per_wg;              // output rows of the down step per workgroup
-  size_t lds_bytes;
 };
 
-// Checks the shape limits of the persistent kernel for a grid of `grid`
-// workgroups; returns false when the per-layer kernels must be used.
-bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int grid);
-size_t stack_lds_bytes(int H, int E, int k, int hwords, int rows_per_wg);
-hipError_t launch_stack_decode(const StackArgs& a, int grid, hipStream_t s);
+// True if the persistent kernel has an instance for this shape on a device
+// with `cus` compute units (else the per-layer kernels run).
+bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cus);
+size_t stack_lds_bytes(int H, int E, int k, int I, int Is, int bits);
+hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,
+                               hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols,
                           int bits, int which, float* out_f32, uint16_t* out_bf16,

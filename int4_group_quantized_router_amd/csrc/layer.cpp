@@ -231,25 +231,23 @@ int32_t setup_persistent(moe_stack* st) {
     if (d.hidden != c.hidden || d.experts != c.experts || d.top_k != c.top_k ||
         d.inter != c.inter || d.shared_inter != c.shared_inter || d.bits != c.bits)
       return MOE_OK;
-    if ((L->wsg != nullptr) != (L0->wsg != nullptr) ||
-        (L->shared_blob != nullptr) != (L0->shared_blob != nullptr))
-      return MOE_OK;
+    if ((L->wsg != nullptr) != (L0->wsg != nullptr) || !L->shared_blob) return MOE_OK;
   }
   int coop = 0, cus = 0, clk_khz = 0;
   MOE_HIP_TRY(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, L0->device));
   MOE_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L0->device));
   MOE_HIP_TRY(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, L0->device));
-  if (!coop || cus < 1 || clk_khz < 1) return MOE_OK;
+  if (!coop || cus < 1 || clk_khz < 1 || n > kStackMaxLayers) return MOE_OK;
   const int H = c.hidden, E = c.experts, k = c.top_k;
   if (!stack_decode_supported(H, E, k, c.inter, c.shared_inter, c.bits, cus)) return MOE_OK;
-  const int hwords = k * c.inter + (L0->shared_blob ? c.shared_inter : 0);
-  const int R = (H + cus - 1) / cus;
+  const int grid = kStackGrid;
+  const int hwords = k * c.inter + c.shared_inter;
   const size_t sizes[] = {
       (size_t)n * sizeof(StackLayerDesc),
       (size_t)n * kStackReplicas * H * 8,         // ybuf
       (size_t)n * kStackReplicas * (E + 1) * 8,   // lbuf
       (size_t)n * kStackReplicas * hwords * 4,    // hbuf
-      (size_t)cus * 4,               // epochs
+      (size_t)grid * 4,              // epochs
   };
   size_t total = 0;
   for (size_t sz : sizes) total += align256(sz);
@@ -289,27 +287,22 @@ int32_t setup_persistent(moe_stack* st) {
   a = StackArgs{};
   a.layers = static_cast<const StackLayerDesc*>(parts[0]);
   a.L = n;
-  a.H = H;
   a.E = E;
-  a.k = k;
-  a.I = c.inter;
-  a.Is = c.shared_inter;
-  a.bits = c.bits;
-  a.hwords = hwords;
   a.has_wsg = L0->wsg != nullptr;
-  a.has_shared = L0->shared_blob != nullptr;
   a.stride = L0->lay_r.stride;
-  a.lr = to_qlayout(L0->lay_r);
-  a.ls = to_qlayout(L0->lay_s);
+  for (int i = 0; i < 3; ++i) {
+    a.lq[i] = (uint32_t)L0->lay_r.q_off[i];
+    a.lsb[i] = (uint32_t)L0->lay_r.sb_off[i];
+    a.sq[i] = (uint32_t)L0->lay_s.q_off[i];
+    a.ssb[i] = (uint32_t)L0->lay_s.sb_off[i];
+  }
   a.ybuf = static_cast<uint64_t*>(parts[1]);
   a.lbuf = static_cast<uint64_t*>(parts[2]);
   a.hbuf = static_cast<uint32_t*>(parts[3]);
   a.epochs = static_cast<uint32_t*>(parts[4]);
   a.err = st->err_host;
   a.timeout_ticks = (int64_t)clk_khz * 1000 * 2;  // 2 s
-  a.rows_per_wg = R;
-  a.lds_bytes = stack_lds_bytes(H, E, k, hwords, R);
-  st->grid = cus;
+  st->grid = grid;
   st->persistent_ok = true;
   return MOE_OK;
 }
@@ -739,7 +732,9 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     a.w = w;
     a.y_last = y_last;
     timer_mark(MOE_KERNEL_STACK, true, stream);
-    hipError_t e = launch_stack_decode(a, stack->grid, stream);
+    const moe_layer_cfg& c = stack->layers[0]->cfg;
+    hipError_t e =
+        launch_stack_decode(a, c.hidden, c.top_k, c.inter, c.shared_inter, c.bits, stream);
     timer_mark(MOE_KERNEL_STACK, false, stream);
     MOE_HIP_TRY(e);
     return MOE_OK;

@@ -10,7 +10,9 @@
 // and dependency stalls of three kernels, so this kernel runs every layer of
 // the stack in one launch:
 //
-// * one workgroup per compute unit, all resident (cooperative launch);
+// * one workgroup per compute unit, all resident (cooperative launch); the
+//   shape (bits, H, I, Is, k, top-k width) is compile-time, so all index
+//   arithmetic folds to constants;
 // * a layer has three all-to-all hand-offs: its output y (every workgroup
 //   needs all of it for the next router and gate/up), the router logits
 //   (every workgroup runs the top-k itself) and the SwiGLU activations h
@@ -48,13 +50,9 @@ using namespace dev;
 
 constexpr int kNT = kStackThreads;
 constexpr int kNW = kNT / kWave;
-constexpr int kGuMax = kStackGuPasses;
-constexpr int kDnMax = kStackDownItems;
-constexpr int kHBatch = 8;
-constexpr int kHBatches = kStackHPairs / kHBatch;
-constexpr int kMaxH = 2048;
+constexpr int kG = kStackGrid;
 constexpr int kRep = kStackReplicas;
-constexpr int kWrIt = kMaxH / 256;  // float4 router loads per lane (full row per wave)
+constexpr int kHBatch = 8;
 
 __device__ __forceinline__ uint32_t tag32_of(uint32_t epoch) { return 2u * epoch + 1u; }
 __device__ __forceinline__ uint32_t tag16_of(uint32_t epoch) { return (epoch & 0x7FFFu) | 0x8000u; }
@@ -72,95 +70,26 @@ __device__ __forceinline__ bool poll_round(bool ok, int64_t deadline, bool* time
   return false;
 }
 
-// Wait for n 64-bit tagged words (n <= PER * kNT) and put their f32 values
-// into dst (LDS).  Returns false on timeout.
-template <int PER>
-__device__ bool poll_f32(const uint64_t* buf, int n, uint32_t tag, float* dst, int64_t deadline) {
-  uint32_t done = 0;
-  for (;;) {
-    uint64_t e[PER];
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = threadIdx.x + m * kNT;
-      e[m] = (i < n && !((done >> m) & 1u)) ? ld_dev(buf + i) : 0ull;
-    }
-    bool ok = true;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = threadIdx.x + m * kNT;
-      if (i < n && !((done >> m) & 1u)) {
-        if ((uint32_t)(e[m] >> 32) == tag) {
-          dst[i] = __uint_as_float((uint32_t)e[m]);
-          done |= 1u << m;
-        } else {
-          ok = false;
-        }
-      }
-    }
-    bool to = false;
-    if (poll_round(ok, deadline, &to)) return true;
-    if (to) return false;
-  }
-}
-
 // Wait for the previous layer's output y: thread t < 256 takes y[t + 256 m]
 // (the per-layer router's order for the sum of squares) into registers.
-__device__ bool poll_y(const uint64_t* buf, int H, uint32_t tag, float* yv, int64_t deadline) {
+template <int H>
+__device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t deadline) {
+  constexpr int M = H / 256;
   const int t = threadIdx.x;
   uint32_t done = 0;
   for (;;) {
-    uint64_t e[kMaxH / 256];
+    uint64_t e[M];
 #pragma unroll
-    for (int m = 0; m < kMaxH / 256; ++m) {
-      const int i = t + m * 256;
-      e[m] = (t < 256 && i < H && !((done >> m) & 1u)) ? ld_dev(buf + i) : 0ull;
-    }
+    for (int m = 0; m < M; ++m)
+      e[m] = (t < 256 && !((done >> m) & 1u)) ? ld_dev(buf + t + m * 256) : 0ull;
     bool ok = true;
+    if (t < 256) {
 #pragma unroll
-    for (int m = 0; m < kMaxH / 256; ++m) {
-      const int i = t + m * 256;
-      if (t < 256 && i < H && !((done >> m) & 1u)) {
-        if ((uint32_t)(e[m] >> 32) == tag) {
-          yv[m] = __uint_as_float((uint32_t)e[m]);
-          done |= 1u << m;
-        } else {
-          ok = false;
-        }
-      }
-    }
-    bool to = false;
-    if (poll_round(ok, deadline, &to)) return true;
-    if (to) return false;
-  }
-}
-
-// Wait for this layer's h words (dense: slot j < k at j * I, shared at k * I)
-// and stage them in LDS as bf16 pairs: hl[i] = (h[2i], h[2i+1]).
-__device__ bool poll_h(const uint32_t* hb, int hwords, uint32_t tag16, uint32_t* hl,
-                       int64_t deadline) {
-  const int npairs = hwords / 2;
-  const uint64_t* src = reinterpret_cast<const uint64_t*>(hb);
-  uint32_t done = 0;
-  for (;;) {
-    bool ok = true;
-    for (int bt = 0; bt < kHBatches; ++bt) {
-      const int base = threadIdx.x + bt * kHBatch * kNT;
-      if (base >= npairs) break;
-      uint64_t e[kHBatch];
-#pragma unroll
-      for (int m = 0; m < kHBatch; ++m) {
-        const int i = base + m * kNT;
-        e[m] = (i < npairs && !((done >> (bt * kHBatch + m)) & 1u)) ? ld_dev(src + i) : 0ull;
-      }
-#pragma unroll
-      for (int m = 0; m < kHBatch; ++m) {
-        const int i = base + m * kNT;
-        const int bit = bt * kHBatch + m;
-        if (i < npairs && !((done >> bit) & 1u)) {
-          const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
-          if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
-            hl[i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
-            done |= 1u << bit;
+      for (int m = 0; m < M; ++m) {
+        if (!((done >> m) & 1u)) {
+          if ((uint32_t)(e[m] >> 32) == tag) {
+            yv[m] = __uint_as_float((uint32_t)e[m]);
+            done |= 1u << m;
           } else {
             ok = false;
           }
@@ -173,9 +102,81 @@ __device__ bool poll_h(const uint32_t* hb, int hwords, uint32_t tag16, uint32_t*
   }
 }
 
-template <int BITS, int VPL, int CPL>
-__global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
+// Wait for pairs [FIRST, FIRST + COUNT) of this layer's h words (dense: slot
+// j < k at j * I, shared at k * I) and stage them in LDS as bf16 pairs:
+// hl[i] = (h[2i], h[2i+1]).
+template <int FIRST, int COUNT>
+__device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_t deadline) {
+  constexpr int PER = (COUNT + kNT - 1) / kNT;
+  static_assert(PER <= 32, "h pairs per thread");
+  uint32_t done = 0;
+  for (;;) {
+    bool ok = true;
+#pragma unroll
+    for (int b0 = 0; b0 < PER; b0 += kHBatch) {
+      uint64_t e[kHBatch];
+#pragma unroll
+      for (int m = 0; m < kHBatch; ++m) {
+        const int i = threadIdx.x + (b0 + m) * kNT;
+        e[m] = (b0 + m < PER && i < COUNT && !((done >> (b0 + m)) & 1u)) ? ld_dev(src + FIRST + i)
+                                                                         : 0ull;
+      }
+#pragma unroll
+      for (int m = 0; m < kHBatch; ++m) {
+        const int i = threadIdx.x + (b0 + m) * kNT;
+        if (b0 + m < PER && i < COUNT && !((done >> (b0 + m)) & 1u)) {
+          const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
+          if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
+            hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
+            done |= 1u << (b0 + m);
+          } else {
+            ok = false;
+          }
+        }
+      }
+    }
+    bool to = false;
+    if (poll_round(ok, deadline, &to)) return true;
+    if (to) return false;
+  }
+}
+
+// Compile-time geometry of one model shape.
+template <int BITS_, int H_, int I_, int IS_, int K_>
+struct Shape {
+  static constexpr int BITS = BITS_, H = H_, I = I_, IS = IS_, K = K_;
   using F = Fmt<BITS>;
+  static constexpr int EPC = F::kEpc;
+  // gate/up: a row group = RPP rows of a matrix, one wave pass; CPL chunks per lane
+  static constexpr int CG = H / EPC;
+  static constexpr int CPL = CG > kWave ? CG / kWave : 1;
+  static constexpr int LPR = CG / CPL, RPP = kWave / LPR;
+  static constexpr int PS = IS / RPP, PR = I / RPP;
+  // shared row groups go to waves 1..7 (wave 0 runs the selection meanwhile),
+  // routed row groups to all waves
+  static constexpr int NPS = (PS + (kNW - 1) * kG - 1) / ((kNW - 1) * kG);
+  static constexpr int NPR = (K * PR + kNW * kG - 1) / (kNW * kG);
+  // down: R output rows per workgroup; a row of a matrix with C chunks takes C lanes
+  static constexpr int R = H / kG;
+  static constexpr int CR = I / EPC, CS = IS / EPC;
+  static constexpr int RPPR = kWave / CR, RPPS = kWave / CS;
+  static constexpr int NIR = R > RPPR ? R / RPPR : 1, NIS = R > RPPS ? R / RPPS : 1;
+  static constexpr int NITEMS = K * NIR + NIS;
+  static constexpr int DN = (NITEMS + kNW - 1) / kNW;               // down items per wave
+  static constexpr int HW = K * I + IS;                             // h words per layer
+  static_assert(H % kG == 0 && (R & (R - 1)) == 0, "rows per workgroup");
+  static_assert(LPR * CPL == CG && LPR <= kWave && kWave % LPR == 0, "gate/up lanes");
+  static_assert(CR <= kWave && CS <= kWave && kWave % CR == 0 && kWave % CS == 0, "down lanes");
+  static_assert(R * kRep <= kNT, "combine threads");
+  static_assert(H <= 2048 && H % 256 == 0, "router row in one wave");
+};
+
+template <class S, int VPL>
+__global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
+  using F = typename S::F;
+  constexpr int BITS = S::BITS, H = S::H, I = S::I, IS = S::IS, K = S::K, R = S::R;
+  constexpr int CPL = S::CPL, LPR = S::LPR, RPP = S::RPP;
+  constexpr int kWrN = H / 256;  // float4 router loads per lane (a whole row per wave)
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float red[4];
   __shared__ int s_sel[MOE_MAX_TOPK];
@@ -183,21 +184,21 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   __shared__ float s_w[MOE_MAX_TOPK + 1];
   __shared__ int tmp_e[MOE_MAX_TOPK];
   __shared__ float tmp_v[MOE_MAX_TOPK];
+  __shared__ StackLayerDesc s_layers[kStackMaxLayers];
+  __shared__ float part[(K + 1) * R];
+  __shared__ float hsum[S::HW / S::EPC];
 
-  const int H = a.H, E = a.E, k = a.k, I = a.I, Is = a.Is;
-  const int R = a.rows_per_wg;
-  const int blk = blockIdx.x, G = gridDim.x;
-  const int wv0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ln0 = threadIdx.x & 63;
+  const int E = a.E;
+  const int blk = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int tid = threadIdx.x;
   const int e_rows = E + (a.has_wsg ? 1 : 0);
 
   // LDS carve-up (sizes as in stack_lds_bytes)
   float* xf = reinterpret_cast<float*>(smem);                       // [H] f32 input
   uint16_t* xb = reinterpret_cast<uint16_t*>(smem + (size_t)H * 4);  // [H] bf16 input
-  float* lg = reinterpret_cast<float*>(smem + (size_t)H * 6);        // [E + 1] logits
-  uint32_t* hl = reinterpret_cast<uint32_t*>(smem + (size_t)H * 6 + ((size_t)(E + 1) * 4 + 15) / 16 * 16);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(hl) + ((size_t)a.hwords * 2 + 15) / 16 * 16);
+  uint32_t* hl = reinterpret_cast<uint32_t*>(smem + (size_t)H * 6);  // [HW / 2] h pairs
 
   const int rep = blk % kRep;  // the XCD of this workgroup
   const uint32_t epoch = ld_dev(a.epochs + blk);
@@ -205,78 +206,30 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   const int64_t deadline = wall_clock64() + a.timeout_ticks;
   bool failed = false;
 
+  // layer descriptors stay in LDS: a scalar load per layer would miss the
+  // caches, which the weight stream keeps flushing
+  for (int i = tid; i < a.L * (int)(sizeof(StackLayerDesc) / 8); i += kNT)
+    reinterpret_cast<uint64_t*>(s_layers)[i] = reinterpret_cast<const uint64_t*>(a.layers)[i];
+  __syncthreads();
+
+  // this lane's place in a gate/up row group, and in the down row groups
+  const int sub = lane % LPR, rsub = lane / LPR;
+  const int gw = wave * kG + blk;  // global wave index: gate/up row group gw + n * 8G
+  const int row0 = blk * R;        // down rows [row0, row0 + R)
+
+  // router row of each wave (E = the shared gate), requested one layer ahead
+  const int rrow = blk + kG * wave;
+  float4 wv[kWrN];
+  float rbv = 0.f;
+  if (rrow < e_rows) {
+    const float* wr = rrow < E ? s_layers[0].Wr + (size_t)rrow * H : s_layers[0].wsg;
+#pragma unroll
+    for (int m = 0; m < kWrN; ++m) wv[m] = *reinterpret_cast<const float4*>(wr + m * 256 + lane * 4);
+    if (rrow < E && s_layers[0].rb) rbv = s_layers[0].rb[rrow];
+  }
+
   for (int l = 0; l < a.L && !failed; ++l) {
-    // The per-row-group index arithmetic below is cheap; hoisted out of the
-    // layer loop it would hold hundreds of registers for the whole loop.
-    // An empty asm makes the ids opaque per layer so it is redone each time.
-    int b = blk, wave = wv0, lane = ln0;
-    asm volatile("" : "+s"(b), "+s"(wave), "+v"(lane));
-    // gate/up geometry: a row group is RPP rows, one wave pass
-    const int Cg = H / F::kEpc, LPR = Cg / CPL, RPP = kWave / LPR;
-    const int sub = lane % LPR, rsub = lane / LPR;
-    const int64_t row_bytes_g = (int64_t)H * BITS / 8;
-    const int Gg = H / 64;
-    const int Ps = a.has_shared ? Is / RPP : 0, Pr = I / RPP;
-    const int P = Ps + k * Pr;
-    const int gw = wave * G + b;  // global wave index
-
-    // down geometry: this workgroup's rows [row0, row0 + R)
-    const int row0 = b * R;
-    const int Cr = I / F::kEpc, Cs = a.has_shared ? Is / F::kEpc : 1;
-    const int RPPr = kWave / Cr, RPPs = kWave / Cs;
-    const int NIr = (R + RPPr - 1) / RPPr, NIs = a.has_shared ? (R + RPPs - 1) / RPPs : 0;
-    const int n_items = k * NIr + NIs;
-    const StackLayerDesc D = a.layers[l];
-
-    // ---- requests that do not depend on routing: router row, shared expert
-    const int rrow = b + G * wave;  // router row of this wave (E = the shared gate)
-    float4 wv[kWrIt];
-    if (rrow < e_rows) {
-      const float* wr = rrow < E ? D.Wr + (size_t)rrow * H : D.wsg;
-#pragma unroll
-      for (int m = 0; m < kWrIt; ++m)
-        if (m * 256 < H) wv[m] = *reinterpret_cast<const float4*>(wr + m * 256 + lane * 4);
-    }
-
-    uint4 gq[kGuMax][2][CPL];
-    uint32_t gsb[kGuMax][2][CPL];
-#pragma unroll
-    for (int n = 0; n < kGuMax; ++n) {
-      const int p = gw + n * kNW * G;
-      if (p < Ps) {
-        const int row = p * RPP + rsub;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint8_t* qb = D.shared_blob + a.ls.q_off[m] + (int64_t)row * row_bytes_g;
-          const uint32_t* sbb = reinterpret_cast<const uint32_t*>(D.shared_blob + a.ls.sb_off[m]) +
-                                (int64_t)row * Gg;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const int ci = sub + c * LPR;
-            gq[n][m][c] = ld16(qb + ci * 16);
-            gsb[n][m][c] = sbb[ci * F::kEpc / 64];
-          }
-        }
-      }
-    }
-
-    uint4 dq[kDnMax];
-    uint32_t dsb[kDnMax];
-#pragma unroll
-    for (int n = 0; n < kDnMax; ++n) {
-      const int it = wave + n * kNW;
-      if (it >= k * NIr && it < n_items) {
-        const int pp = it - k * NIr;
-        const int ci = lane % Cs, rloc = pp * RPPs + lane / Cs, row = row0 + rloc;
-        dq[n] = make_uint4(0, 0, 0, 0);
-        dsb[n] = 0;
-        if (rloc < R && row < H) {
-          dq[n] = ld16(D.shared_blob + a.ls.q_off[2] + (int64_t)row * (Is * BITS / 8) + ci * 16);
-          dsb[n] = reinterpret_cast<const uint32_t*>(D.shared_blob + a.ls.sb_off[2])
-              [(int64_t)row * (Is / 64) + ci * F::kEpc / 64];
-        }
-      }
-    }
+    const StackLayerDesc D = s_layers[l];
 
     // ---- layer input: x0, or bf16(y / rms(y)) of the previous layer
     if (l == 0) {
@@ -284,12 +237,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         const uint16_t v = a.x0[i];
         xb[i] = v;
         xf[i] = bf16_to_f32(v);
-        if (b == 0 && a.x_layers) a.x_layers[i] = v;
+        if (blk == 0 && a.x_layers) a.x_layers[i] = v;
       }
       __syncthreads();
     } else {
-      float yv[kMaxH / 256];
-      if (!poll_y(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, H, tag, yv, deadline)) {
+      float yv[H / 256];
+      if (!poll_y<H>(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, tag, yv, deadline)) {
         failed = true;
         break;
       }
@@ -297,8 +250,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       if (tid < 256) {
         float s = 0.f;
 #pragma unroll
-        for (int m = 0; m < kMaxH / 256; ++m)
-          if (tid + m * 256 < H) s = fmaf(yv[m], yv[m], s);
+        for (int m = 0; m < H / 256; ++m) s = fmaf(yv[m], yv[m], s);
         s = group_sum(s, kWave);
         if (lane == 0) red[tid >> 6] = s;
       }
@@ -307,14 +259,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
       if (tid < 256) {
 #pragma unroll
-        for (int m = 0; m < kMaxH / 256; ++m) {
+        for (int m = 0; m < H / 256; ++m) {
           const int i = tid + m * 256;
-          if (i < H) {
-            const uint32_t bb = f32_to_bf16(yv[m] * r);
-            xb[i] = (uint16_t)bb;
-            xf[i] = bf16_to_f32(bb);
-            if (b == 0 && a.x_layers) a.x_layers[(size_t)l * H + i] = (uint16_t)bb;
-          }
+          const uint32_t bb = f32_to_bf16(yv[m] * r);
+          xb[i] = (uint16_t)bb;
+          xf[i] = bf16_to_f32(bb);
+          if (blk == 0 && a.x_layers) a.x_layers[(size_t)l * H + i] = (uint16_t)bb;
         }
       }
       __syncthreads();
@@ -322,201 +272,299 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
 
     // ---- router row: halves summed separately, as the per-layer router
     if (rrow < e_rows) {
-      const int nit = H / 256;
-      const int half = (H % 512 == 0) ? nit / 2 : nit;
+      constexpr int half = (H % 512 == 0) ? kWrN / 2 : kWrN;
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int m = 0; m < kWrIt; ++m) {
-        if (m < nit) {
-          const float4 xv = *reinterpret_cast<const float4*>(xf + m * 256 + lane * 4);
-          float s = m < half ? acc0 : acc1;
-          s = fmaf(wv[m].x, xv.x, s);
-          s = fmaf(wv[m].y, xv.y, s);
-          s = fmaf(wv[m].z, xv.z, s);
-          s = fmaf(wv[m].w, xv.w, s);
-          if (m < half) acc0 = s; else acc1 = s;
-        }
+      for (int m = 0; m < kWrN; ++m) {
+        const float4 xv = *reinterpret_cast<const float4*>(xf + m * 256 + lane * 4);
+        float s = m < half ? acc0 : acc1;
+        s = fmaf(wv[m].x, xv.x, s);
+        s = fmaf(wv[m].y, xv.y, s);
+        s = fmaf(wv[m].z, xv.z, s);
+        s = fmaf(wv[m].w, xv.w, s);
+        if (m < half) acc0 = s; else acc1 = s;
       }
       acc0 = group_sum(acc0, kWave);
       float out = acc0;
-      if (half < nit) out = acc0 + group_sum(acc1, kWave);
+      if (half < kWrN) out = acc0 + group_sum(acc1, kWave);
       if (lane < kRep) {
-        const float v = rrow < E ? out + (D.rb ? D.rb[rrow] : 0.f) : out;
+        const float v = rrow < E ? out + (D.rb ? rbv : 0.f) : out;
         st_dev(a.lbuf + ((size_t)l * kRep + lane) * (E + 1) + rrow, pack64(v, tag));
       }
     }
 
-    // ---- selection: every workgroup runs the top-k on all logits
-    if (!poll_f32<(1024 + 1 + kNT - 1) / kNT>(a.lbuf + ((size_t)l * kRep + rep) * (E + 1), e_rows,
-                                             tag, lg, deadline)) {
+    // ---- shared expert, independent of routing: its down rows are
+    // requested and its gate/up rows computed (h published) while the
+    // logits round trip is in flight
+    uint32_t* hb = a.hbuf + (size_t)l * kRep * S::HW;
+    uint32_t xp[CPL][F::kPairs];
+    float xs[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ci = sub + c * LPR;
+      pair_natural<BITS>(reinterpret_cast<const uint4*>(xb + ci * F::kEpc), xp[c], xs[c]);
+    }
+    // one row group of gate/up: h = bf16(silu(g) * u), kRep copies
+    auto gu_rows = [&](const uint4 (&q)[2][CPL], const uint32_t (&sbw)[2][CPL], int base, int row) {
+      float g = 0.f, u = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        g = chunk_term<BITS>(g, sbw[0][c], chunk_dot<BITS>(q[0][c], xp[c]), xs[c]);
+        u = chunk_term<BITS>(u, sbw[1][c], chunk_dot<BITS>(q[1][c], xp[c]), xs[c]);
+      }
+      g = group_sum(g, LPR);
+      u = group_sum(u, LPR);
+      if (sub < kRep) {  // every lane of the row group holds g and u
+        const float hv = g / (1.0f + __expf(-g)) * u;
+        st_dev(hb + (size_t)sub * S::HW + base + h_pos<BITS>(row), (f32_to_bf16(hv) << 16) | tag16);
+      }
+    };
+    auto gu_load = [&](const uint8_t* blob, const uint32_t* q_off, const uint32_t* sb_off, int row,
+                       uint4 (&q)[2][CPL], uint32_t (&sbw)[2][CPL]) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint8_t* qb = blob + q_off[m] + (size_t)row * (H * BITS / 8);
+        const uint32_t* sbb = reinterpret_cast<const uint32_t*>(blob + sb_off[m]) + (size_t)row * (H / 64);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const int ci = sub + c * LPR;
+          q[m][c] = ld16(qb + ci * 16);
+          sbw[m][c] = sbb[ci * F::kEpc / 64];
+        }
+      }
+    };
+
+    uint4 dq[S::DN];
+    uint32_t dsb[S::DN];
+#pragma unroll
+    for (int n = 0; n < S::DN; ++n) {
+      const int it = wave + n * kNW;
+      if (it >= K * S::NIR && it < S::NITEMS) {
+        const int pp = it - K * S::NIR;
+        const int ci = lane % S::CS, rloc = pp * S::RPPS + lane / S::CS;
+        dq[n] = make_uint4(0, 0, 0, 0);
+        dsb[n] = 0;
+        if (rloc < R) {
+          const int row = row0 + rloc;
+          dq[n] = ld16(D.shared_blob + a.sq[2] + (size_t)row * (IS * BITS / 8) + ci * 16);
+          dsb[n] = reinterpret_cast<const uint32_t*>(D.shared_blob + a.ssb[2])
+              [(size_t)row * (IS / 64) + ci * F::kEpc / 64];
+        }
+      }
+    }
+    // Wave 0 waits for the logits (in the registers the top-k reads) and
+    // selects; waves 1..7 compute the shared expert's gate/up meanwhile.
+    __shared__ int s_abort;
+    if (wave == 0) {
+      const uint64_t* lb = a.lbuf + ((size_t)l * kRep + rep) * (E + 1);
+      float v[VPL], vs = 0.f;
+      uint32_t key[VPL];
+      uint32_t done = 0;
+      bool timed_out = false;
+      for (;;) {
+        uint64_t e[VPL + 1];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          const int idx = lane + kWave * i;
+          e[i] = (idx < E && !((done >> i) & 1u)) ? ld_dev(lb + idx) : 0ull;
+        }
+        e[VPL] = (lane == 0 && a.has_wsg && !((done >> VPL) & 1u)) ? ld_dev(lb + E) : 0ull;
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i <= VPL; ++i) {
+          const bool need = i < VPL ? lane + kWave * i < E : (lane == 0 && a.has_wsg);
+          if (need && !((done >> i) & 1u)) {
+            if ((uint32_t)(e[i] >> 32) == tag) {
+              if (i < VPL) v[i] = __uint_as_float((uint32_t)e[i]); else vs = __uint_as_float((uint32_t)e[i]);
+              done |= 1u << i;
+            } else {
+              ok = false;
+            }
+          }
+        }
+        if (__ballot(!ok) == 0) break;
+        if (wall_clock64() > deadline) {
+          timed_out = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!timed_out) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+          if (lane + kWave * i >= E) v[i] = 0.f;
+          key[i] = lane + kWave * i < E ? order_key(v[i]) : 0u;
+        }
+        wave_topk<VPL>(v, key, K, tmp_e, tmp_v, s_sel, s_val);
+        // renormalised weights = softmax over the chosen logits, summed in j order
+        const float ex = lane < K ? expf(s_val[lane] - s_val[0]) : 0.f;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) sum += readlane_f32(ex, j);
+        if (lane < K) {
+          const float wj = ex / sum;
+          s_w[lane] = wj;
+          if (blk == 0 && a.w) a.w[(size_t)l * K + lane] = wj;
+          if (blk == 0 && a.idx) a.idx[(size_t)l * K + lane] = s_sel[lane];
+        }
+        if (lane == 0) s_w[K] = a.has_wsg ? 1.0f / (1.0f + expf(-vs)) : 0.f;
+      }
+      if (lane == 0) s_abort = timed_out ? 1 : 0;
+    } else {
+      uint4 gq[S::NPS][2][CPL];
+      uint32_t gsb[S::NPS][2][CPL];
+      const int q0 = (wave - 1) * kG + blk;
+#pragma unroll
+      for (int n = 0; n < S::NPS; ++n) {
+        const int p = q0 + n * (kNW - 1) * kG;
+        if (p < S::PS) gu_load(D.shared_blob, a.sq, a.ssb, p * RPP + rsub, gq[n], gsb[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < S::NPS; ++n) {
+        const int p = q0 + n * (kNW - 1) * kG;
+        if (p < S::PS) gu_rows(gq[n], gsb[n], K * I, p * RPP + rsub);
+      }
+    }
+    __syncthreads();
+    if (s_abort) {
       failed = true;
       break;
     }
-    if (wave == 0) {
-      float v[VPL];
-      uint32_t key[VPL];
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int e = lane + kWave * i;
-        v[i] = e < E ? lg[e] : 0.f;
-        key[i] = e < E ? order_key(v[i]) : 0u;
-      }
-      wave_topk<VPL>(v, key, k, tmp_e, tmp_v, s_sel, s_val);
-      // renormalised weights = softmax over the chosen logits, summed in j order
-      const float ex = lane < k ? expf(s_val[lane] - s_val[0]) : 0.f;
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j)
-        if (j < k) sum += readlane_f32(ex, j);
-      if (lane < k) {
-        const float wj = ex / sum;
-        s_w[lane] = wj;
-        if (b == 0 && a.w) a.w[(size_t)l * k + lane] = wj;
-        if (b == 0 && a.idx) a.idx[(size_t)l * k + lane] = s_sel[lane];
-      }
-      if (lane == 0) s_w[k] = a.has_wsg ? 1.0f / (1.0f + expf(-lg[E])) : 0.f;
-    }
-    __syncthreads();
 
-    // ---- routed gate/up requests
-#pragma unroll
-    for (int n = 0; n < kGuMax; ++n) {
-      const int p = gw + n * kNW * G;
-      if (p >= Ps && p < P) {
-        const int pr = p - Ps, j = pr / Pr;
-        const int row = (pr - j * Pr) * RPP + rsub;
-        const uint8_t* blob = D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint8_t* qb = blob + a.lr.q_off[m] + (int64_t)row * row_bytes_g;
-          const uint32_t* sbb = reinterpret_cast<const uint32_t*>(blob + a.lr.sb_off[m]) +
-                                (int64_t)row * Gg;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const int ci = sub + c * LPR;
-            gq[n][m][c] = ld16(qb + ci * 16);
-            gsb[n][m][c] = sbb[ci * F::kEpc / 64];
-          }
-        }
-      }
-    }
-
-    // ---- gate/up: h = bf16(silu(g) * u) for this wave's row groups
-    uint32_t* hb = a.hbuf + (size_t)l * kRep * a.hwords;
+    // ---- routed gate/up: row group gw + n * 8G of K * PR; at most DEPTH
+    // passes of weights are in flight per lane
     {
-      uint32_t xp[CPL][F::kPairs];
-      float xs[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const int ci = sub + c * LPR;
-        pair_natural<BITS>(reinterpret_cast<const uint4*>(xb + ci * F::kEpc), xp[c], xs[c]);
-      }
-#pragma unroll
-      for (int n = 0; n < kGuMax; ++n) {
-        const int p = gw + n * kNW * G;
-        if (p < P) {
-          int base, row;
-          if (p < Ps) {
-            base = k * I;
-            row = p * RPP + rsub;
-          } else {
-            const int pr = p - Ps, j = pr / Pr;
-            base = j * I;
-            row = (pr - j * Pr) * RPP + rsub;
-          }
-          float g = 0.f, u = 0.f;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            g = chunk_term<BITS>(g, gsb[n][0][c], chunk_dot<BITS>(gq[n][0][c], xp[c]), xs[c]);
-            u = chunk_term<BITS>(u, gsb[n][1][c], chunk_dot<BITS>(gq[n][1][c], xp[c]), xs[c]);
-          }
-          g = group_sum(g, LPR);
-          u = group_sum(u, LPR);
-          if (sub < kRep) {  // every lane of the row group holds g and u
-            const float hv = g / (1.0f + __expf(-g)) * u;
-            st_dev(hb + (size_t)sub * a.hwords + base + h_pos<BITS>(row),
-                   (f32_to_bf16(hv) << 16) | tag16);
-          }
+      constexpr int DEPTH = CPL == 1 ? S::NPR : 2;
+      uint4 gq[DEPTH][2][CPL];
+      uint32_t gsb[DEPTH][2][CPL];
+      auto routed_load = [&](int n) {
+        const int pr = gw + n * kNW * kG;
+        if (pr < K * S::PR) {
+          const int j = pr / S::PR;
+          const uint8_t* blob =
+              D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
+          gu_load(blob, a.lq, a.lsb, (pr % S::PR) * RPP + rsub, gq[n % DEPTH], gsb[n % DEPTH]);
         }
+      };
+#pragma unroll
+      for (int n = 0; n < DEPTH; ++n) routed_load(n);
+#pragma unroll
+      for (int n = 0; n < S::NPR; ++n) {
+        const int pr = gw + n * kNW * kG;
+        if (pr < K * S::PR) {
+          const int j = pr / S::PR;
+          gu_rows(gq[n % DEPTH], gsb[n % DEPTH], j * I, (pr % S::PR) * RPP + rsub);
+        }
+        if (n + DEPTH < S::NPR) routed_load(n + DEPTH);
       }
     }
 
     // ---- routed down requests for this workgroup's rows (needed after the h wait)
 #pragma unroll
-    for (int n = 0; n < kDnMax; ++n) {
+    for (int n = 0; n < S::DN; ++n) {
       const int it = wave + n * kNW;
-      if (it < k * NIr) {
-        const int j = it / NIr, pp = it - j * NIr;
-        const int ci = lane % Cr, rloc = pp * RPPr + lane / Cr, row = row0 + rloc;
+      if (it < K * S::NIR) {
+        const int j = it / S::NIR, pp = it % S::NIR;
+        const int ci = lane % S::CR, rloc = pp * S::RPPR + lane / S::CR;
         const uint8_t* blob = D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
         dq[n] = make_uint4(0, 0, 0, 0);
         dsb[n] = 0;
-        if (rloc < R && row < H) {
-          dq[n] = ld16(blob + a.lr.q_off[2] + (int64_t)row * (I * BITS / 8) + ci * 16);
-          dsb[n] = reinterpret_cast<const uint32_t*>(blob + a.lr.sb_off[2])
-              [(int64_t)row * (I / 64) + ci * F::kEpc / 64];
+        if (rloc < R) {
+          const int row = row0 + rloc;
+          dq[n] = ld16(blob + a.lq[2] + (size_t)row * (I * BITS / 8) + ci * 16);
+          dsb[n] = reinterpret_cast<const uint32_t*>(blob + a.lsb[2])
+              [(size_t)row * (I / 64) + ci * F::kEpc / 64];
         }
       }
     }
 
-    // ---- down + combine for rows [row0, row0 + R)
-    if (!poll_h(hb + (size_t)rep * a.hwords, a.hwords, tag16, hl, deadline)) {
+    // ---- next layer's router row
+    if (l + 1 < a.L && rrow < e_rows) {
+      const StackLayerDesc& Dn = s_layers[l + 1];
+      const float* wr = rrow < E ? Dn.Wr + (size_t)rrow * H : Dn.wsg;
+#pragma unroll
+      for (int m = 0; m < kWrN; ++m) wv[m] = *reinterpret_cast<const float4*>(wr + m * 256 + lane * 4);
+      if (rrow < E && Dn.rb) rbv = Dn.rb[rrow];
+    }
+
+    // ---- down + combine for rows [row0, row0 + R): shared rows first (its h
+    // was published during the logits round trip), then the routed rows
+    const uint64_t* hrep = reinterpret_cast<const uint64_t*>(hb + (size_t)rep * S::HW);
+    // per-chunk sums of h (the bias term's X), each once per workgroup
+    auto chunk_sums = [&](int c0, int c1) {
+      for (int i = c0 + tid; i < c1; i += kNT) {
+        const uint4* c4 = reinterpret_cast<const uint4*>(hl + (size_t)i * F::kPairs);
+        float hs = 0.f;
+#pragma unroll
+        for (int v = 0; v < F::kPairs / 4; ++v) {
+          const uint4 d = c4[v];
+          hs += bf16_lo(d.x) + bf16_hi(d.x);
+          hs += bf16_lo(d.y) + bf16_hi(d.y);
+          hs += bf16_lo(d.z) + bf16_hi(d.z);
+          hs += bf16_lo(d.w) + bf16_hi(d.w);
+        }
+        hsum[i] = hs;
+      }
+    };
+    auto down_items = [&](bool shared_part) {
+#pragma unroll
+      for (int n = 0; n < S::DN; ++n) {
+        const int it = wave + n * kNW;
+        const bool is_shared = it >= K * S::NIR;
+        if (it < S::NITEMS && is_shared == shared_part) {
+          const int s = is_shared ? K : it / S::NIR;
+          const int pp = is_shared ? it - K * S::NIR : it % S::NIR;
+          const int C = is_shared ? S::CS : S::CR, RP = is_shared ? S::RPPS : S::RPPR;
+          const int ci = lane % C, rloc = pp * RP + lane / C;
+          const int chunk = s * (I / F::kEpc) + ci;  // chunk index in the dense h
+          const uint4* hsrc = reinterpret_cast<const uint4*>(hl + (size_t)chunk * F::kPairs);
+          uint32_t hp[F::kPairs];
+#pragma unroll
+          for (int v = 0; v < F::kPairs / 4; ++v) {
+            const uint4 d = hsrc[v];
+            hp[4 * v] = d.x;
+            hp[4 * v + 1] = d.y;
+            hp[4 * v + 2] = d.z;
+            hp[4 * v + 3] = d.w;
+          }
+          float acc = chunk_term<BITS>(0.f, dsb[n], chunk_dot<BITS>(dq[n], hp), hsum[chunk]);
+          acc = group_sum(acc, C);
+          if (ci == 0 && rloc < R) part[s * R + rloc] = acc;
+        }
+      }
+    };
+    if (!poll_h<K * I / 2, IS / 2>(hrep, tag16, hl, deadline)) {
       failed = true;
       break;
     }
     __syncthreads();
-#pragma unroll
-    for (int n = 0; n < kDnMax; ++n) {
-      const int it = wave + n * kNW;
-      if (it < n_items) {
-        int s, C, pp, RPPx;
-        if (it < k * NIr) {
-          s = it / NIr;
-          pp = it - s * NIr;
-          C = Cr;
-          RPPx = RPPr;
-        } else {
-          s = k;
-          pp = it - k * NIr;
-          C = Cs;
-          RPPx = RPPs;
-        }
-        const int ci = lane % C, rloc = pp * RPPx + lane / C;
-        const uint4* hsrc = reinterpret_cast<const uint4*>(hl + (size_t)s * (I / 2) + ci * (F::kEpc / 2));
-        uint32_t hp[F::kPairs];
-#pragma unroll
-        for (int v = 0; v < F::kPairs / 4; ++v) {
-          const uint4 d = hsrc[v];
-          hp[4 * v] = d.x;
-          hp[4 * v + 1] = d.y;
-          hp[4 * v + 2] = d.z;
-          hp[4 * v + 3] = d.w;
-        }
-        float hs = 0.f;
-#pragma unroll
-        for (int v = 0; v < F::kPairs; ++v) hs += bf16_lo(hp[v]) + bf16_hi(hp[v]);
-        float acc = chunk_term<BITS>(0.f, dsb[n], chunk_dot<BITS>(dq[n], hp), hs);
-        acc = group_sum(acc, C);
-        if (ci == 0 && rloc < R) part[s * R + rloc] = acc;
-      }
+    chunk_sums(K * I / F::kEpc, S::HW / F::kEpc);
+    __syncthreads();
+    down_items(true);
+    if (!poll_h<0, K * I / 2>(hrep, tag16, hl, deadline)) {
+      failed = true;
+      break;
     }
+    __syncthreads();
+    chunk_sums(0, K * I / F::kEpc);
+    __syncthreads();
+    down_items(false);
     __syncthreads();
     if (tid < R * kRep) {  // kRep threads per row, one per copy
       const int r = tid % R, cp = tid / R, row = row0 + r;
-      if (row < H) {
-        float y = 0.f;
+      float y = 0.f;
 #pragma unroll
-        for (int j = 0; j < MOE_MAX_TOPK; ++j)
-          if (j < k) y = fmaf(s_w[j], part[j * R + r], y);
-        if (a.has_shared) y = fmaf(s_w[k], part[k * R + r], y);
-        st_dev(a.ybuf + ((size_t)l * kRep + cp) * H + row, pack64(y, tag));
-        if (cp == 0) {
-          if (a.y_layers) a.y_layers[(size_t)l * H + row] = y;
-          if (l == a.L - 1) a.y_last[row] = (uint16_t)f32_to_bf16(y);
-        }
+      for (int j = 0; j < K; ++j) y = fmaf(s_w[j], part[j * R + r], y);
+      y = fmaf(s_w[K], part[K * R + r], y);
+      st_dev(a.ybuf + ((size_t)l * kRep + cp) * H + row, pack64(y, tag));
+      if (cp == 0) {
+        if (a.y_layers) a.y_layers[(size_t)l * H + row] = y;
+        if (l == a.L - 1) a.y_last[row] = (uint16_t)f32_to_bf16(y);
       }
     }
-    __syncthreads();
+    // No barrier here: the next LDS writes that could meet this layer's
+    // reads (s_w, part, hl) come after the next layer's y wait, itself a
+    // workgroup barrier.
   }
 
   if (tid == 0) {
@@ -525,54 +573,50 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   }
 }
 
-template <int BITS, int CPL>
-hipError_t launch_bits(const StackArgs& a, int grid, hipStream_t s) {
-  const int vpl = (a.E + 63) / 64;
+template <class S, int VPL>
+hipError_t launch_shape(const StackArgs& a, hipStream_t s) {
+  const size_t lds = stack_lds_bytes(S::H, a.E, S::K, S::I, S::IS, S::BITS);
+  hipError_t e = allow_lds(stack_decode_kernel<S, VPL>, lds);
+  if (e != hipSuccess) return e;
   void* args[] = {const_cast<StackArgs*>(&a)};
-#define MOE_STACK_CASE(V)                                                                    \
-  if (vpl <= V) {                                                                            \
-    const void* fn = reinterpret_cast<const void*>(&stack_decode_kernel<BITS, V, CPL>);      \
-    hipError_t e = allow_lds(stack_decode_kernel<BITS, V, CPL>, a.lds_bytes);                \
-    if (e != hipSuccess) return e;                                                           \
-    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kNT), args, (unsigned)a.lds_bytes, s); \
-  }
-  MOE_STACK_CASE(1)
-  MOE_STACK_CASE(2)
-  MOE_STACK_CASE(4)
-  MOE_STACK_CASE(8)
-  MOE_STACK_CASE(16)
-#undef MOE_STACK_CASE
-  return hipErrorInvalidValue;
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stack_decode_kernel<S, VPL>),
+                                    dim3(kG), dim3(kNT), args, (unsigned)lds, s);
 }
+
+// The instances: (bits, H, I, Is, k) x top-k width (64 * VPL >= E).
+#define MOE_STACK_SHAPES(X)             \
+  X(4, 2048, 512, 512, 8, 4)  /* 256 experts, top-8 */  \
+  X(4, 2048, 512, 512, 10, 8) /* 512 experts, top-10 */ \
+  X(8, 2048, 512, 512, 10, 8) /* int8, 512 experts, top-10 */ \
+  X(4, 256, 64, 64, 2, 1)     /* small test shape */
 
 }  // namespace
 
-size_t stack_lds_bytes(int H, int E, int k, int hwords, int rows_per_wg) {
-  return (size_t)H * 6 + ((size_t)(E + 1) * 4 + 15) / 16 * 16 + ((size_t)hwords * 2 + 15) / 16 * 16 +
-         (size_t)(k + 1) * rows_per_wg * 4;
+size_t stack_lds_bytes(int H, int E, int k, int I, int Is, int bits) {
+  (void)bits;
+  (void)E;
+  return (size_t)H * 6 + (size_t)(k * I + Is) * 2;
 }
 
-bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int grid) {
-  if (!decode_shape_supported(H, I, Is, bits) || grid < 1) return false;
-  if (E + 1 > kNW * grid || E > 1024) return false;  // one router row per wave
-  const int epc = 128 / bits;
-  const int C = H / epc, cpl = C <= 64 ? 1 : C / 64;
-  const int rpp = kWave / (C / cpl);
-  if (Is + k * I > (int64_t)kGuMax * kNW * grid * rpp) return false;
-  const int R = (H + grid - 1) / grid;
-  const int ni = k * ((R + kWave / (I / epc) - 1) / (kWave / (I / epc))) +
-                 (R + kWave / (Is / epc) - 1) / (kWave / (Is / epc));
-  if (ni > kDnMax * kNW) return false;
-  if ((k * I + Is) / 2 > kStackHPairs * kNT) return false;
-  if (R * kRep > kNT) return false;
-  return stack_lds_bytes(H, E, k, k * I + Is, R) + 1024 <= 160 * 1024;
+bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cus) {
+  if (cus < kG || E + 1 > kNW * kG || E < k) return false;
+  const int vpl = (E + 63) / 64;
+#define MOE_STACK_MATCH(B, HH, II, SS, KK, V) \
+  if (bits == B && H == HH && I == II && Is == SS && k == KK && vpl <= V && vpl > V / 2) return true;
+  MOE_STACK_SHAPES(MOE_STACK_MATCH)
+#undef MOE_STACK_MATCH
+  return false;
 }
 
-hipError_t launch_stack_decode(const StackArgs& a, int grid, hipStream_t s) {
-  const int C = a.H / (128 / a.bits);
-  if (a.bits == 4) return launch_bits<4, 1>(a, grid, s);
-  if (C <= 64) return launch_bits<8, 1>(a, grid, s);
-  return launch_bits<8, 2>(a, grid, s);
+hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,
+                               hipStream_t s) {
+  const int vpl = (a.E + 63) / 64;
+#define MOE_STACK_LAUNCH(B, HH, II, SS, KK, V)                                       \
+  if (bits == B && H == HH && I == II && Is == SS && k == KK && vpl <= V && vpl > V / 2) \
+    return launch_shape<Shape<B, HH, II, SS, KK>, V>(a, s);
+  MOE_STACK_SHAPES(MOE_STACK_LAUNCH)
+#undef MOE_STACK_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe
