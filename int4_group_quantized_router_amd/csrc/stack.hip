@@ -52,7 +52,6 @@ constexpr int kNT = kStackThreads;
 constexpr int kNW = kNT / kWave;
 constexpr int kG = kStackGrid;
 constexpr int kRep = kStackReplicas;
-constexpr int kHBatch = 8;
 
 __device__ __forceinline__ uint32_t tag32_of(uint32_t epoch) { return 2u * epoch + 1u; }
 __device__ __forceinline__ uint32_t tag16_of(uint32_t epoch) { return (epoch & 0x7FFFu) | 0x8000u; }
@@ -102,42 +101,51 @@ __device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t dea
   }
 }
 
-// Wait for pairs [FIRST, FIRST + COUNT) of this layer's h words (dense: slot
-// j < k at j * I, shared at k * I) and stage them in LDS as bf16 pairs:
-// hl[i] = (h[2i], h[2i+1]).
+// Pairs [FIRST, FIRST + COUNT) of this layer's h words (dense: slot j < k
+// at j * I, shared at k * I), PER per thread.
+template <int COUNT>
+constexpr int h_per() {
+  return (COUNT + kNT - 1) / kNT;
+}
+
+// Request this thread's pairs; `done` marks pairs already staged.
 template <int FIRST, int COUNT>
-__device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_t deadline) {
-  constexpr int PER = (COUNT + kNT - 1) / kNT;
+__device__ __forceinline__ void h_request(const uint64_t* src, uint32_t done,
+                                          uint64_t (&e)[h_per<COUNT>()]) {
+#pragma unroll
+  for (int m = 0; m < h_per<COUNT>(); ++m) {
+    const int i = threadIdx.x + m * kNT;
+    e[m] = (i < COUNT && !((done >> m) & 1u)) ? ld_dev(src + FIRST + i) : 0ull;
+  }
+}
+
+// Wait for the pairs, starting from the already requested round `e`, and
+// stage them in LDS as bf16 pairs: hl[i] = (h[2i], h[2i+1]).
+template <int FIRST, int COUNT>
+__device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_t deadline,
+                       uint64_t (&e)[h_per<COUNT>()]) {
+  constexpr int PER = h_per<COUNT>();
   static_assert(PER <= 32, "h pairs per thread");
   uint32_t done = 0;
   for (;;) {
     bool ok = true;
 #pragma unroll
-    for (int b0 = 0; b0 < PER; b0 += kHBatch) {
-      uint64_t e[kHBatch];
-#pragma unroll
-      for (int m = 0; m < kHBatch; ++m) {
-        const int i = threadIdx.x + (b0 + m) * kNT;
-        e[m] = (b0 + m < PER && i < COUNT && !((done >> (b0 + m)) & 1u)) ? ld_dev(src + FIRST + i)
-                                                                         : 0ull;
-      }
-#pragma unroll
-      for (int m = 0; m < kHBatch; ++m) {
-        const int i = threadIdx.x + (b0 + m) * kNT;
-        if (b0 + m < PER && i < COUNT && !((done >> (b0 + m)) & 1u)) {
-          const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
-          if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
-            hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
-            done |= 1u << (b0 + m);
-          } else {
-            ok = false;
-          }
+    for (int m = 0; m < PER; ++m) {
+      const int i = threadIdx.x + m * kNT;
+      if (i < COUNT && !((done >> m) & 1u)) {
+        const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
+        if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
+          hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
+          done |= 1u << m;
+        } else {
+          ok = false;
         }
       }
     }
     bool to = false;
     if (poll_round(ok, deadline, &to)) return true;
     if (to) return false;
+    h_request<FIRST, COUNT>(src, done, e);
   }
 }
 
@@ -430,6 +438,10 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       failed = true;
       break;
     }
+    // the shared h (published while the logits were in flight) is requested
+    // after the first routed gate/up pass and looked at after the last
+    const uint64_t* hrep = reinterpret_cast<const uint64_t*>(hb + (size_t)rep * S::HW);
+    uint64_t hsh[h_per<IS / 2>()];
 
     // ---- routed gate/up: row group gw + n * 8G of K * PR; at most DEPTH
     // passes of weights are in flight per lane
@@ -456,6 +468,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           gu_rows(gq[n % DEPTH], gsb[n % DEPTH], j * I, (pr % S::PR) * RPP + rsub);
         }
         if (n + DEPTH < S::NPR) routed_load(n + DEPTH);
+        if (n == 0) h_request<K * I / 2, IS / 2>(hrep, 0u, hsh);
       }
     }
 
@@ -489,7 +502,6 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
 
     // ---- down + combine for rows [row0, row0 + R): shared rows first (its h
     // was published during the logits round trip), then the routed rows
-    const uint64_t* hrep = reinterpret_cast<const uint64_t*>(hb + (size_t)rep * S::HW);
     // per-chunk sums of h (the bias term's X), each once per workgroup
     auto chunk_sums = [&](int c0, int c1) {
       for (int i = c0 + tid; i < c1; i += kNT) {
@@ -533,7 +545,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
       }
     };
-    if (!poll_h<K * I / 2, IS / 2>(hrep, tag16, hl, deadline)) {
+    if (!poll_h<K * I / 2, IS / 2>(hrep, tag16, hl, deadline, hsh)) {
       failed = true;
       break;
     }
@@ -541,7 +553,9 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     chunk_sums(K * I / F::kEpc, S::HW / F::kEpc);
     __syncthreads();
     down_items(true);
-    if (!poll_h<0, K * I / 2>(hrep, tag16, hl, deadline)) {
+    uint64_t hrt[h_per<K * I / 2>()];
+    h_request<0, K * I / 2>(hrep, 0u, hrt);
+    if (!poll_h<0, K * I / 2>(hrep, tag16, hl, deadline, hrt)) {
       failed = true;
       break;
     }
