@@ -66,18 +66,28 @@ __device__ __forceinline__ void pair_natural(const uint4* src, uint32_t* xp, flo
   }
 }
 
+// (w & m) | c as one VALU op.  gfx950's three-operand encoding takes no
+// 32-bit literal, so left to itself the compiler splits this into an AND and
+// an OR with literals; here m sits in an SGPR and c in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
 // sum over the chunk of (128 + q) * x (int4) or q * x (int8), f32.
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const uint4 w4, const uint32_t* xp) {
   const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
   float d0 = 0.f, d1 = 0.f;
   if (BITS == 4) {
+    constexpr uint32_t M = 0x000F000Fu, C = 0x43004300u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      d0 = dot2((w[m] & 0x000F000Fu) | 0x43004300u, xp[4 * m + 0], d0);
-      d1 = dot2(((w[m] >> 4) & 0x000F000Fu) | 0x43004300u, xp[4 * m + 1], d1);
-      d0 = dot2(((w[m] >> 8) & 0x000F000Fu) | 0x43004300u, xp[4 * m + 2], d0);
-      d1 = dot2(((w[m] >> 12) & 0x000F000Fu) | 0x43004300u, xp[4 * m + 3], d1);
+      d0 = dot2(and_or(w[m], M, C), xp[4 * m + 0], d0);
+      d1 = dot2(and_or(w[m] >> 4, M, C), xp[4 * m + 1], d1);
+      d0 = dot2(and_or(w[m] >> 8, M, C), xp[4 * m + 2], d0);
+      d1 = dot2(and_or(w[m] >> 12, M, C), xp[4 * m + 3], d1);
     }
   } else {
 #pragma unroll
