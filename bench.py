@@ -32,6 +32,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM counters of the persistent stack kernel on the 40-layer 35B-shaped
+# stack (profiles/decode35b_stack_decode_kernel.md), per launch, with the
+# factors that map a plain copy's counter readings onto its byte count.
+STACK_TRAFFIC = {
+    "decode35b": {"fetch_kib": 361948, "write_kib": 53786,
+                  "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -110,6 +118,23 @@ def cpu_baseline(cfg, budget_s=20.0):
                       f"tokens/s = 1 / (s per layer x {cfg.layers})"}
 
 
+def calibrate_copy(nbytes):
+    """A plain device copy of known size: what the HBM counters (FETCH_SIZE,
+    WRITE_SIZE) read for it scales their readings of the MoE kernels."""
+    import torch
+    torch.cuda.set_device(0)
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 10
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 10,
+                      "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true",
                     help="decode: three kernels per layer instead of one persistent kernel")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run 10 device-to-device copies of BYTES (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -127,6 +154,8 @@ def main():
 
     import numpy as np
     import torch
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
     import int4_group_quantized_router_amd as m
     from int4_group_quantized_router_amd import weights as W
     from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
@@ -194,6 +223,10 @@ def main():
         k_name = "gate_up_kernel (dequant-GEMV gate+up, fused SiLU*up)"
         k_bytes = ab["gate_up"]
     achieved = k_bytes / k_mean_s / 1e9
+    traffic = None
+    if persistent and cfg.name in STACK_TRAFFIC:
+        t = STACK_TRAFFIC[cfg.name]
+        traffic = (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
     log(f"[bench] {tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.3f} ms/token, "
         f"kernel mean {k_mean_s * 1e6:.2f} us over {len(gu_ms)} launches")
 
@@ -234,7 +267,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic,
             "bytes_per_launch": k_bytes,
             "mean_launch_us": k_mean_s * 1e6,
             "launches": int(len(gu_ms)),
