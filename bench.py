@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true",
                     help="decode: three kernels per layer instead of one persistent kernel")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="stream80b / decode80b_int8: build only this many layers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 10 device-to-device copies of BYTES (reference for HBM counters)")
     args = ap.parse_args()
@@ -161,8 +163,14 @@ def main():
     from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
 
     cfg = CONFIGS[args.workload]
+    if args.layers:
+        cfg = cfg.replace(layers=args.layers)
     if cfg.batch > 8:
         return bench_prefill(args, cfg)
+    if not cfg.resident:
+        return bench_stream(args, cfg)
+    if cfg.name != "decode35b":
+        return bench_decode_other(args, cfg)
     args.steps = 256 if args.steps is None else args.steps
     args.warmup = 16 if args.warmup is None else args.warmup
     assert cfg.batch == 1 and cfg.resident, "decode bench workload must be resident batch-1"
@@ -278,6 +286,130 @@ def main():
     m.moe_stack_destroy(stack)
     for L in layers:
         m.moe_layer_destroy(L)
+
+
+def _build_stack(cfg, pool=None):
+    """Layers (resident, or served by `pool`) and their stack for cfg."""
+    import torch
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as W
+    from moe_inputs import expert_arrays, router_arrays, shared_arrays
+    dims = {"hidden": cfg.hidden, "experts": cfg.experts, "top_k": cfg.top_k,
+            "inter": cfg.inter, "shared_inter": cfg.shared_inter, "bits": cfg.bits}
+    routed = None
+    if pool is None:
+        routed, _ = W.upload_resident(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    layers, keep = [], [routed]
+    for l in range(cfg.layers):
+        Wr, rb, wsg = (torch.from_numpy(a).cuda() for a in router_arrays(cfg, l))
+        sh = W.upload_blob(cfg.hidden, cfg.shared_inter, cfg.bits, shared_arrays(cfg, l))
+        keep += [Wr, rb, wsg, sh]
+        layers.append(m.moe_layer_create(dict(dims, layer_index=l), Wr, rb, sh, wsg,
+                                         resident_base=routed, pool=pool))
+    return layers, m.moe_stack_create(layers), keep
+
+
+def _run_tokens(m, stack, X, Y, T, warmup, steps):
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def bench_decode_other(args, cfg):
+    """Resident decode of another stack shape (e.g. int8 experts), batch 1
+    (persistent kernel) and batch 8 (per-layer kernels)."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from moe_inputs import tokens_x
+    steps = 64 if args.steps is None else args.steps
+    warmup = 8 if args.warmup is None else args.warmup
+    torch.cuda.set_device(0)
+    log(f"[bench] building {cfg.name}: {cfg.layers} layers x {cfg.experts} experts, int{cfg.bits}")
+    layers, stack, keep = _build_stack(cfg)
+    ab = algorithmic_bytes(cfg)
+    res = {}
+    for T in (1, 8):
+        n = (warmup + steps) * T
+        X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
+        Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
+        dt = _run_tokens(m, stack, X, Y, T, warmup, steps)
+        res[T] = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
+                  "path": ("persistent stack kernel" if T == 1 and m.moe_stack_persistent_active(stack)
+                           else "per-layer kernels")}
+        log(f"[bench] T={T}: {res[T]['tokens_per_s']:.1f} tok/s ({res[T]['path']})")
+    per_token = ab["layer"] * cfg.layers
+    out = {"metric": f"MoE stack tokens/sec at batch 1 and 8, int{cfg.bits} experts, 1 GPU",
+           "value": res[1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": f"int{cfg.bits} weights, f32 accumulate, bf16 I/O",
+           "data": "synthetic (seeded; random-init weights of the stated shape)",
+           "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden {cfg.hidden}, "
+                                  f"{cfg.experts} experts top-{cfg.top_k}, intermediate {cfg.inter}, "
+                                  f"int{cfg.bits}, all resident",
+                      "batch1": res[1], "batch8": res[8],
+                      "bytes_per_token_batch1": per_token,
+                      "batch1_GBps": per_token * res[1]["tokens_per_s"] / 1e9}}
+    print(json.dumps(out), flush=True)
+    m.moe_stack_destroy(stack)
+    for L in layers:
+        m.moe_layer_destroy(L)
+
+
+def bench_stream(args, cfg):
+    """Batch-1 decode with routed experts served from the HBM slot pool
+    (floor(pool_frac * L * E) slots) filled from the pinned host store."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as W
+    from moe_inputs import expert_arrays, tokens_x
+    steps = 128 if args.steps is None else args.steps
+    warmup = 0 if args.warmup is None else args.warmup
+    torch.cuda.set_device(0)
+    dims = {"hidden": cfg.hidden, "experts": cfg.experts, "inter": cfg.inter, "bits": cfg.bits}
+    log(f"[bench] filling the pinned store: {cfg.layers} layers x {cfg.experts} experts")
+    t_b = time.perf_counter()
+    store, stride = W.fill_store(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    cap = int(cfg.pool_frac * cfg.layers * cfg.experts)
+    pool = m.slotpool_create(store, cap, 0)
+    layers, stack, keep = _build_stack(cfg, pool=pool)
+    log(f"[bench] built in {time.perf_counter() - t_b:.1f} s; pool {cap} slots x {stride} B")
+    n = warmup + steps
+    X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
+    Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
+    s0 = m.slotpool_get_stats(pool)
+    dt = _run_tokens(m, stack, X, Y, 1, warmup, steps)
+    s1 = m.slotpool_get_stats(pool)
+    d = {k: s1[k] - s0[k] for k in s1}
+    acc = d["hits"] + d["misses"]
+    tok_s = steps / dt
+    log(f"[bench] {tok_s:.1f} tok/s; hits {d['hits']} misses {d['misses']} "
+        f"({d['hits'] / max(acc, 1):.3f} hit rate); {d['bytes_h2d'] / dt / 1e9:.2f} GB/s host->HBM")
+    out = {"metric": "MoE stack tokens/sec, batch-1 decode with expert streaming (30% HBM pool), 1 GPU",
+           "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": f"int{cfg.bits} weights, f32 accumulate, bf16 I/O",
+           "data": "synthetic (seeded; random-init weights of the stated shape)",
+           "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden {cfg.hidden}, "
+                                  f"{cfg.experts} experts top-{cfg.top_k}, int{cfg.bits}, slot pool "
+                                  f"{cap} = floor({cfg.pool_frac} x L x E), pool starts empty",
+                      "pool_hits": d["hits"], "pool_misses": d["misses"],
+                      "pool_evictions": d["evictions"], "hit_rate": d["hits"] / max(acc, 1),
+                      "bytes_h2d": d["bytes_h2d"], "h2d_GBps": d["bytes_h2d"] / dt / 1e9}}
+    print(json.dumps(out), flush=True)
+    m.moe_stack_destroy(stack)
+    for L in layers:
+        m.moe_layer_destroy(L)
+    m.slotpool_destroy(pool)
+    m.expert_store_destroy(store)
 
 
 def bench_prefill(args, cfg):
