@@ -123,12 +123,12 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const uint8_t* qb = blob + L.q_off[m] + (int64_t)r * row_bytes;
-      const uint32_t* sbb = reinterpret_cast<const uint32_t*>(blob + L.sb_off[m]) + (int64_t)r * G;
+      const uint8_t* sbb = blob + L.sb_off[m] + (int64_t)r * G * 4;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int ci = sub + c * LPR;
         q[m][p][c] = ok ? ld16(qb + ci * 16) : make_uint4(0, 0, 0, 0);
-        sb[m][p][c] = ok ? sbb[ci * F::kEpc / 64] : 0u;
+        sb[m][p][c] = ok ? ldu32(sbb + (ci * F::kEpc / 64) * 4) : 0u;
       }
     }
   }
@@ -235,8 +235,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
       if (rloc[bi] < R && row < a.H) {
         const int64_t row_bytes = (int64_t)inner * BITS / 8;
         q[bi] = ld16(blob + L.q_off[2] + (int64_t)row * row_bytes + ci[bi] * 16);
-        sbw[bi] = reinterpret_cast<const uint32_t*>(blob + L.sb_off[2])
-            [(int64_t)row * (inner / 64) + ci[bi] * F::kEpc / 64];
+        sbw[bi] = ldu32(blob + L.sb_off[2] + ((int64_t)row * (inner / 64) + ci[bi] * F::kEpc / 64) * 4);
       }
     }
 #pragma unroll
@@ -341,8 +340,7 @@ __global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a) {
       sbw[si][p] = 0;
       if (rloc < R && row < a.H) {
         q[si][p] = ld16(blob + L.q_off[2] + (int64_t)row * row_bytes + ci * 16);
-        sbw[si][p] = reinterpret_cast<const uint32_t*>(blob + L.sb_off[2])
-            [(int64_t)row * (inner / 64) + ci * F::kEpc / 64];
+        sbw[si][p] = ldu32(blob + L.sb_off[2] + ((int64_t)row * (inner / 64) + ci * F::kEpc / 64) * 4);
       }
     }
   }

@@ -69,9 +69,27 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+// Loads through global-address-space pointers.  A pointer the compiler
+// cannot prove global (read from a table, selected at run time) would be
+// loaded with FLAT instructions, which also count against the LDS wait
+// counter: every later LDS wait would then also wait for the HBM load.
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+
 // 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
+  const u32x4_v v = *(__attribute__((address_space(1))) const u32x4_v*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ldf4(const void* p) {
+  const f32x4_v v = *(__attribute__((address_space(1))) const f32x4_v*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ldu32(const void* p) {
+  return *(__attribute__((address_space(1))) const uint32_t*)p;
+}
+__device__ __forceinline__ float ldf(const void* p) {
+  return *(__attribute__((address_space(1))) const float*)p;
 }
 
 }  // namespace dev

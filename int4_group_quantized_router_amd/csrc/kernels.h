@@ -71,7 +71,7 @@ bool decode_shape_supported(int H, int I, int Is, int bits);
 
 // Many-token (prefill) path: sort (token, choice) pairs by expert, grouped
 // MFMA GEMMs with dequant-to-bf16 weight tiles, fixed-order combine.
-constexpr int kPrefillBM = 128;  // rows per GEMM tile
+constexpr int kPrefillBM = 96;   // rows per grouped-GEMM tile (routed experts average ~80 rows)
 
 struct PrefillArgs {
   int T, H, I, Is, E, k, bits, hI;

@@ -34,6 +34,7 @@
 // (the dispatcher deals blocks round-robin over the 8 XCDs): the 16 or 8
 // column tiles of one row tile then share its rows in that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -47,7 +48,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int BM = kPrefillBM;
+constexpr int BM = kPrefillBM;        // grouped-GEMM tile rows
+constexpr int RBM = 128;              // router GEMM tile (tokens and experts)
 constexpr int KG = 64;                // K per step = one quantisation group
 constexpr int kLdsRow = KG * 2 + 16;  // bytes per weight row in LDS (padded)
 
@@ -75,45 +77,6 @@ __device__ __forceinline__ void tile_of_block(int nt_per_tile, int* tile, int* n
   const int xcd = b & 7, j = b >> 3;
   *tile = (j / nt_per_tile) * 8 + xcd;
   *nt = j % nt_per_tile;
-}
-
-// Dequantise one 16-byte chunk of packed weights to bf16 (round to nearest
-// even of the exact f32 value s*q + b) and store it in natural order.
-template <int BITS>
-__device__ __forceinline__ void dequant_chunk(const uint4 raw, uint32_t sb, uint8_t* dst) {
-  const float s = bf16_lo(sb), b = bf16_hi(sb);
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-  if (BITS == 4) {
-    uint32_t o[16];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // nibbles to bytes; the asm keeps the optimiser from folding the masks
-      // into per-value bit-field extracts, so each byte converts with one
-      // v_cvt_f32_ubyte{0..3}
-      uint32_t lo, hi;
-      asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w[m]));
-      asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w[m] >> 4));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)  // values 8m+2i (low nibble of byte i) and 8m+2i+1
-        o[4 * m + i] = pack_bf16(fmaf(s, (float)((lo >> (8 * i)) & 0xFFu), b),
-                                 fmaf(s, (float)((hi >> (8 * i)) & 0xFFu), b));
-    }
-    uint4* d = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) d[v] = make_uint4(o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]);
-  } else {
-    uint32_t o[8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        o[2 * m + i] = pack_bf16(fmaf(s, (float)((w[m] >> (16 * i)) & 0xFFu), b),
-                                 fmaf(s, (float)((w[m] >> (16 * i + 8)) & 0xFFu), b));
-    }
-    uint4* d = reinterpret_cast<uint4*>(dst);
-    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
-  }
 }
 
 // One packed word -> bf16 values in natural order: 8 (int4, as a uint4) or
@@ -167,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
     float* logits, float* sigma_raw) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int mh = wave >> 1, nh = wave & 1, kh = lane >> 5, l32 = lane & 31;
-  const int t0 = blockIdx.x * BM, e0 = blockIdx.y * BM;
+  const int t0 = blockIdx.x * RBM, e0 = blockIdx.y * RBM;
   const int rows = E + (has_wsg ? 1 : 0);
   const int64_t plane = (int64_t)(E + 1) * H;
   const uint16_t* arow[2];
@@ -316,34 +279,39 @@ __global__ __launch_bounds__(kThreads) void prefill_compact_kernel(PrefillArgs a
 // One kernel for both products.  Workgroup tile: 128 rows of one group x 256
 // weight rows -- for gate/up, 128 intermediate columns of gate and the same
 // 128 of up (so h = silu(g) * u is finished in registers); for down, 256
-// output columns.  Per 64-wide K group the workgroup stages the 128 A rows
-// (gathered token rows of x, or rows of h) and the 256 dequantised weight
-// rows in LDS (double-buffered), with global loads issued two groups ahead
-// through a ring of two register sets.  Eight waves (two per SIMD, so one
-// wave's dequantisation overlaps the other's MFMAs); each owns a 64-row x
-// 64-weight-row block = 2 x 2 MFMA 32x32x16 tiles, 64 f32 accumulators.
+// output columns.  Four waves, one per SIMD, two workgroups per CU.  Wave w
+// owns 64 weight rows (gate/up: 32 gate + the same 32 up; down: 64 outputs)
+// for all 128 rows: 4 x 2 MFMA 32x32x16 tiles, 128 f32 accumulators.
+//
+// Per 64-wide K group (one quantisation group):
+// * A (128 gathered token rows of x, or rows of h) is staged in LDS, double
+//   buffered, from registers loaded two groups ahead;
+// * each lane's B operand for the four MFMA steps is 32 consecutive weights
+//   of one weight row -- 16 packed bytes (int4) -- loaded straight from HBM
+//   two groups ahead and dequantised in registers right before its MFMA
+//   step, so the VALU work of step s+1 overlaps the matrix core on step s.
+//   No weight goes through LDS and no weight is dequantised twice.
 
-constexpr int BN = 256;                    // weight rows per tile
-constexpr int kGemmThreads = 512;          // 8 waves
-constexpr int kLdsA = BM * kLdsRow;        // bytes of one A stage
-constexpr int kLdsB = BN * kLdsRow;        // bytes of one B stage
+constexpr int kGemmThreads = 256;  // 4 waves
 
 template <int BITS>
-struct GemmRegs {
-  static constexpr int CB = BN * (KG * BITS / 8) / 16 / kGemmThreads;  // B chunks per thread
-  uint4 a[2];        // A: 2 x 16 bytes per thread per K group
-  uint4 b[CB];       // B: packed weights
-  uint32_t sb[CB];   // (scale, bias) word of each B chunk's row
+struct BRaw {  // one K group of packed weights for the lane's two weight rows
+  static constexpr int N = BITS == 4 ? 1 : 2;  // 16-byte loads per row
+  uint4 q[2][N];
+  uint32_t sb[2];
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct ARow {  // one thread's three 16-byte A pieces of one K group (native
+  u32x4_t v0, v1, v2;  // vectors: a copy of HIP's uint4 struct from global
+};                     // memory would stay a memcpy into scratch)
+
 template <int BITS, bool GU>
-__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(PrefillArgs a,
+__global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillArgs a,
                                                                        int nt_per_tile) {
-  extern __shared__ __align__(16) uint8_t smem[];  // 2 x (A stage + B stage)
-  using R = GemmRegs<BITS>;
-  constexpr int CB = R::CB;
-  constexpr int GBYTES = KG * BITS / 8;  // packed bytes of one weight row per K group
-  constexpr int CPR = GBYTES / 16;       // 16-byte chunks per weight row per K group
+  __shared__ __align__(16) uint8_t As[2][BM * kLdsRow];
+  using R = BRaw<BITS>;
   int tile, nt;
   tile_of_block(nt_per_tile, &tile, &nt);
   if (tile >= *a.n_tiles) return;
@@ -351,169 +319,197 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(PrefillAr
   const bool shared = g == a.E;
   const int inner = shared ? a.Is : a.I;
   // gate/up: N = intermediate columns (128 per tile), K = H.  down: N = H, K = inner.
-  const int c0 = nt * (GU ? BN / 2 : BN);
+  const int c0 = nt * (GU ? 128 : 256);
   if (GU && c0 >= inner) return;
   const int K = GU ? a.H : inner;
+  const int NK = K / KG;
   const int r0 = a.row_off[g] + m0;
   const int mrows = min(BM, a.row_off[g + 1] - a.row_off[g] - m0);
+  const int nrb = min(BM / 32, (mrows + 31) / 32);  // row blocks of 32 with any live row
   const uint8_t* blob = group_blob(a, g);
   const QLayout L = shared ? a.ls : a.lr;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // waves w and w+4 share a SIMD: give each SIMD one low-row and one
-  // high-row wave, so skipped row blocks (below) shorten every SIMD's work
-  const int mq = wave >> 2, nq = wave & 3, kh = lane >> 5, l32 = lane & 31;
-  // row blocks of 32 entirely past the tile's rows do no MFMA work
-  const bool rb_live0 = mq * 64 < mrows, rb_live1 = mq * 64 + 32 < mrows;
+  const int kh = lane >> 5, l32 = lane & 31;
+  // gate/up waves whose 32 columns lie past a small intermediate size only
+  // help staging
+  const bool wave_live = !GU || c0 + 32 * wave < inner;
 
-  // A rows this thread stages: row (tid >> 3) + 64 i, 16-byte part tid & 7.
-  // Rows past the tile read a valid row and only feed rows never stored.
-  const uint16_t* asrc[2];
+  // A: thread stages 16 bytes (8 values) of rows tid / 8 + 32 i, i < 3, part
+  // tid % 8, so one load instruction covers 8 whole 128-byte row segments.
+  // Rows past the tile read a valid row and only feed accumulator rows that
+  // are never stored.
+  const int apart = tid & 7;
+  const uint16_t* abase = GU ? a.x : a.h;
+  uint32_t aoff[BM / 32];  // element offsets (x: T * H, h: rows * hI, both < 2^31)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rl = (tid >> 3) + 64 * i;
+  for (int i = 0; i < BM / 32; ++i) {
+    const int rl = (tid >> 3) + 32 * i;
     const int rr = rl < mrows ? rl : 0;
-    if (GU)
-      asrc[i] = a.x + (size_t)a.perm_tok[r0 + rr] * a.H + (tid & 7) * 8;
-    else
-      asrc[i] = a.h + (size_t)(r0 + rr) * a.hI + (tid & 7) * 8;
+    aoff[i] = GU ? (uint32_t)a.perm_tok[r0 + rr] * (uint32_t)a.H + apart * 8
+                 : (uint32_t)(r0 + rr) * (uint32_t)a.hI + apart * 8;
   }
-  // B chunks this thread dequantises: chunk c = tid + 512 j -> row c / CPR, part c % CPR
-  const uint8_t* bsrc[CB];
-  const uint32_t* sbsrc[CB];
-  int bdst[CB];
+  const int adst = (tid >> 3) * kLdsRow + apart * 16;
+
+  // B: the lane's weight row in each of its two column blocks, K slice
+  // [32 kh, 32 kh + 32) of every group
+  const uint8_t* bsrc[2];
+  const uint8_t* sbsrc[2];
 #pragma unroll
-  for (int j = 0; j < CB; ++j) {
-    const int c = tid + kGemmThreads * j;
-    const int br = c / CPR, part = c % CPR;
+  for (int cb = 0; cb < 2; ++cb) {
     int m, wrow;
     if (GU) {
-      m = br >= BN / 2 ? 1 : 0;
-      wrow = c0 + (br & (BN / 2 - 1));
-      if (wrow >= inner) wrow = 0;  // overhang of a small intermediate size: never stored
+      m = cb;
+      wrow = min(c0 + 32 * wave + l32, inner - 1);  // past inner: never stored
     } else {
       m = 2;
-      wrow = c0 + br;
+      wrow = c0 + 64 * wave + 32 * cb + l32;
     }
-    const uint8_t* qb = blob + (m == 0 ? L.q_off[0] : m == 1 ? L.q_off[1] : L.q_off[2]);
-    const uint8_t* sbb = blob + (m == 0 ? L.sb_off[0] : m == 1 ? L.sb_off[1] : L.sb_off[2]);
-    bsrc[j] = qb + (int64_t)wrow * (K * BITS / 8) + part * 16;
-    sbsrc[j] = reinterpret_cast<const uint32_t*>(sbb) + (int64_t)wrow * (K / 64);
-    bdst[j] = kLdsA + br * kLdsRow + part * (256 / BITS);
+    const int64_t qo = m == 0 ? L.q_off[0] : m == 1 ? L.q_off[1] : L.q_off[2];
+    const int64_t so = m == 0 ? L.sb_off[0] : m == 1 ? L.sb_off[1] : L.sb_off[2];
+    bsrc[cb] = blob + qo + (int64_t)wrow * (K * BITS / 8) + kh * (32 * BITS / 8);
+    sbsrc[cb] = blob + so + (int64_t)wrow * (K / 64) * 4;
   }
 
-  auto load = [&](R& r, int kg) {
+  auto load_a = [&](ARow& r, int kg) __attribute__((always_inline)) {
+    const uint16_t* base = abase + kg * KG;
+    r.v0 = *reinterpret_cast<const u32x4_t*>(base + aoff[0]);
+    r.v1 = *reinterpret_cast<const u32x4_t*>(base + aoff[1]);
+    r.v2 = *reinterpret_cast<const u32x4_t*>(base + aoff[2]);
+  };
+  auto store_a = [&](const ARow& r, int buf) __attribute__((always_inline)) {
+    uint8_t* d = &As[buf][adst];
+    *reinterpret_cast<u32x4_t*>(d) = r.v0;
+    *reinterpret_cast<u32x4_t*>(d + 32 * kLdsRow) = r.v1;
+    *reinterpret_cast<u32x4_t*>(d + 64 * kLdsRow) = r.v2;
+  };
+  auto load_b = [&](R& r, int kg) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r.a[i] = ld16(asrc[i] + kg * KG);
+    for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      r.b[j] = ld16(bsrc[j] + kg * GBYTES);
-      r.sb[j] = sbsrc[j][kg];
+      for (int i = 0; i < R::N; ++i) r.q[cb][i] = ld16(bsrc[cb] + kg * (KG * BITS / 8) + 16 * i);
+      r.sb[cb] = ldu32(sbsrc[cb] + kg * 4);
     }
   };
-  f32x16_t acc[2][2];
+  // bf16 B operand of MFMA step s for column block cb: weights 8s..8s+7 of
+  // the lane's 32
+  auto b_operand = [&](const R& r, int cb, int s) __attribute__((always_inline)) -> uint4 {
+    const float sc = bf16_lo(r.sb[cb]), bi = bf16_hi(r.sb[cb]);
+    if (BITS == 4) {
+      const uint4 q = r.q[cb][0];
+      const uint32_t w = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
+      return dequant_word<4>(w, sc, bi);
+    } else {
+      const uint4 q = r.q[cb][s >> 1];
+      const uint32_t w0 = (s & 1) ? q.z : q.x, w1 = (s & 1) ? q.w : q.y;
+      const uint4 lo = dequant_word<8>(w0, sc, bi), hi = dequant_word<8>(w1, sc, bi);
+      return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+  };
+
+  f32x16_t acc[BM / 32][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BM / 32; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-  // weight-row base (in the B stage) of the wave's 2 column blocks
-  int bro[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-    bro[cb] = GU ? (cb * (BN / 2) + nq * 32) : (nq * 64 + cb * 32);
 
-  auto read_frags = [&](const uint8_t* stage, int s, uint4* af, uint4* bf) {
+  // one K group on A stage `buf` with packed weights `r`.  MFMA step s runs
+  // on operands prepared during step s-1 (A fragments read from LDS, B
+  // dequantised in registers); the scheduler is told to interleave each of
+  // the step's MFMAs with a share of the next step's dequantisation, so the
+  // VALU works while the matrix core does.  NRB (row blocks with any live
+  // row) is a compile-time count.
+  auto compute = [&](auto nrb_c, int buf, const R& r) __attribute__((always_inline)) {
+    constexpr int NRB = decltype(nrb_c)::value;
+    if (!wave_live) return;
+    const uint8_t* st = As[buf];
+    uint4 af[2][NRB], bo[2][2];
+    bo[0][0] = b_operand(r, 0, 0);
+    bo[0][1] = b_operand(r, 1, 0);
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-      af[rb] = *reinterpret_cast<const uint4*>(stage + (mq * 64 + rb * 32 + l32) * kLdsRow +
-                                               kh * 64 + s * 16);
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-      bf[cb] = *reinterpret_cast<const uint4*>(stage + kLdsA + (bro[cb] + l32) * kLdsRow +
-                                               kh * 64 + s * 16);
-  };
-  // Quarter `part` of staging a register set into LDS: the A rows (parts 0,
-  // 1) and 4*CB/4 packed words of the weight chunks, dequantised.
-  auto store_part = [&](const R& r, uint8_t* stage, int part) {
-    if (part < 2)
-      *reinterpret_cast<uint4*>(stage + ((tid >> 3) + 64 * part) * kLdsRow + (tid & 7) * 16) =
-          r.a[part];
-#pragma unroll
-    for (int f = part * CB; f < (part + 1) * CB; ++f) {
-      const int c = f / 4, m = f % 4;
-      const uint32_t wrd = m == 0 ? r.b[c].x : m == 1 ? r.b[c].y : m == 2 ? r.b[c].z : r.b[c].w;
-      const uint4 v = dequant_word<BITS>(wrd, bf16_lo(r.sb[c]), bf16_hi(r.sb[c]));
-      if (BITS == 4) {
-        *reinterpret_cast<uint4*>(stage + bdst[c] + m * 16) = v;
-      } else {
-        *reinterpret_cast<uint2*>(stage + bdst[c] + m * 8) = make_uint2(v.x, v.y);
-      }
-    }
-  };
-  // One K group: MFMAs on stage `sc` (already in LDS) interleaved with
-  // staging register set `r` into `ss`: after each group of four MFMAs (which
-  // run asynchronously on the matrix core) a quarter of the dequantisation
-  // issues on the VALU.
-  auto step = [&](const uint8_t* sc, const R& r, uint8_t* ss, bool do_store) {
-    uint4 af[2][2], bf[2][2];
-    read_frags(sc, 0, af[0], bf[0]);
+    for (int rb = 0; rb < NRB; ++rb)
+      af[0][rb] = *reinterpret_cast<const uint4*>(st + (rb * 32 + l32) * kLdsRow + kh * 64);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      if (s4 < 3) read_frags(sc, s4 + 1, af[(s4 + 1) & 1], bf[(s4 + 1) & 1]);
-      if (rb_live0) {
-        acc[0][0] = mfma(af[s4 & 1][0], bf[s4 & 1][0], acc[0][0]);
-        acc[0][1] = mfma(af[s4 & 1][0], bf[s4 & 1][1], acc[0][1]);
+      const int cur = s4 & 1, nxt = cur ^ 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (s4 < 3) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          af[nxt][rb] = *reinterpret_cast<const uint4*>(st + (rb * 32 + l32) * kLdsRow + kh * 64 +
+                                                        (s4 + 1) * 16);
       }
-      if (rb_live1) {
-        acc[1][0] = mfma(af[s4 & 1][1], bf[s4 & 1][0], acc[1][0]);
-        acc[1][1] = mfma(af[s4 & 1][1], bf[s4 & 1][1], acc[1][1]);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        acc[rb][0] = mfma(af[cur][rb], bo[cur][0], acc[rb][0]);
+        acc[rb][1] = mfma(af[cur][rb], bo[cur][1], acc[rb][1]);
       }
-      if (do_store) {
-        __builtin_amdgcn_sched_barrier(0);
-        store_part(r, ss, s4);
-        __builtin_amdgcn_sched_barrier(0);
+      if (s4 < 3) {
+        bo[nxt][0] = b_operand(r, 0, s4 + 1);
+        bo[nxt][1] = b_operand(r, 1, s4 + 1);
+        // LDS reads first, then one MFMA per share of the dequant VALU ops
+        __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NRB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, BITS == 4 ? 48 / (2 * NRB) : 40 / (2 * NRB), 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // the K pipeline for a compile-time row-block count
+  auto run = [&](auto nrb_c) __attribute__((always_inline)) {
+    // prologue: A of groups 0 (in LDS) and 1 (in registers); B of groups 0, 1
+    ARow ar;
+    R bq0, bq1;
+    load_a(ar, 0);
+    load_b(bq0, 0);
+    if (NK > 1) load_b(bq1, 1);
+    store_a(ar, 0);
+    if (NK > 1) load_a(ar, 1);
+    __syncthreads();
+    // iteration kg: MFMAs on group kg; stage A of kg+1; request A of kg+2 and
+    // B of kg+2 (into the register set group kg just used)
+    int kg = 0;
+    for (; kg + 2 < NK; kg += 2) {
+      compute(nrb_c, 0, bq0);
+      load_b(bq0, kg + 2);
+      store_a(ar, 1);
+      load_a(ar, kg + 2);
+      __syncthreads();
+      compute(nrb_c, 1, bq1);
+      if (kg + 3 < NK) load_b(bq1, kg + 3);
+      store_a(ar, 0);
+      if (kg + 3 < NK) load_a(ar, kg + 3);
+      __syncthreads();
+    }
+    if (kg < NK) {  // one or two groups left: kg (stage 0) and maybe kg + 1 (in registers)
+      compute(nrb_c, 0, bq0);
+      if (kg + 1 < NK) {
+        store_a(ar, 1);
+        __syncthreads();
+        compute(nrb_c, 1, bq1);
       }
     }
   };
-
-  const int NK = K / KG;
-  uint8_t* st0 = smem;
-  uint8_t* st1 = smem + kLdsA + kLdsB;
-  R r0_, r1_;
-  load(r0_, 0);
-  if (NK > 1) load(r1_, 1);
-#pragma unroll
-  for (int part = 0; part < 4; ++part) store_part(r0_, st0, part);
-  if (NK > 2) load(r0_, 2);
-  __syncthreads();
-  // step kg computes stage kg from LDS while staging kg+1 and loading kg+3
-  int kg = 0;
-  for (; kg + 4 < NK; kg += 2) {
-    step(st0, r1_, st1, true);
-    load(r1_, kg + 3);
-    __syncthreads();
-    step(st1, r0_, st0, true);
-    load(r0_, kg + 4);
-    __syncthreads();
-  }
-  for (; kg < NK; kg += 2) {
-    step(st0, r1_, st1, kg + 1 < NK);
-    if (kg + 3 < NK) load(r1_, kg + 3);
-    __syncthreads();
-    if (kg + 1 >= NK) break;
-    step(st1, r0_, st0, kg + 2 < NK);
-    if (kg + 4 < NK) load(r0_, kg + 4);
-    __syncthreads();
+  static_assert(BM == 96, "row-block dispatch below");
+  switch (nrb) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 3>{}); break;
   }
 
+  if (!wave_live) return;
   if (GU) {
     // acc[rb][0] = gate, acc[rb][1] = up for the same rows and columns
+    const int col = c0 + 32 * wave + l32;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < BM / 32; ++rb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rl = mq * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
-        const int col = c0 + nq * 32 + l32;
+        const int rl = rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
         if (rl < mrows && col < inner) {
           const float gv = acc[rb][0][v], uv = acc[rb][1][v];
           const float hv = gv / (1.0f + __expf(-gv)) * uv;
@@ -522,14 +518,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(PrefillAr
       }
   } else {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < BM / 32; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int rl = mq * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
+          const int rl = rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
           if (rl < mrows)
-            a.yd[(size_t)(r0 + rl) * a.H + c0 + nq * 64 + cb * 32 + l32] = acc[rb][cb][v];
+            a.yd[(size_t)(r0 + rl) * a.H + c0 + 64 * wave + 32 * cb + l32] = acc[rb][cb][v];
         }
   }
 }
@@ -587,7 +583,7 @@ hipError_t launch_split_router(const float* Wr, const float* wsg, int E, int H, 
 hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3,
                               const float* bias, int has_wsg, int E, float* logits,
                               float* sigma_raw, hipStream_t s) {
-  const dim3 grid((T + BM - 1) / BM, (E + (has_wsg ? 1 : 0) + BM - 1) / BM);
+  const dim3 grid((T + RBM - 1) / RBM, (E + (has_wsg ? 1 : 0) + RBM - 1) / RBM);
   hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(kThreads), 0, s, x, T, H, wr3, bias, E,
                      has_wsg, logits, sigma_raw);
   return hipGetLastError();
@@ -603,12 +599,9 @@ hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s) {
 
 template <int BITS, bool GU>
 hipError_t launch_grouped(const PrefillArgs& a, hipStream_t s) {
-  const int nt = GU ? (std::max(a.I, a.Is) + BN / 2 - 1) / (BN / 2) : a.H / BN;
-  const size_t lds = 2 * (size_t)(kLdsA + kLdsB);
-  hipError_t e = allow_lds(grouped_gemm_kernel<BITS, GU>, lds);
-  if (e != hipSuccess) return e;
+  const int nt = GU ? (std::max(a.I, a.Is) + 127) / 128 : a.H / 256;
   const int tiles8 = pad8(a.max_tiles);  // every XCD gets tiles8 / 8 tiles x nt blocks
-  hipLaunchKernelGGL((grouped_gemm_kernel<BITS, GU>), dim3(tiles8 * nt), dim3(kGemmThreads), lds,
+  hipLaunchKernelGGL((grouped_gemm_kernel<BITS, GU>), dim3(tiles8 * nt), dim3(kGemmThreads), 0,
                      s, a, nt);
   return hipGetLastError();
 }

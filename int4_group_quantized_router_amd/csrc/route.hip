@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     const float* wr = row < E ? a.Wr + (size_t)row * H : a.wsg;
 #pragma unroll
     for (int i = 0; i < kMaxIt; ++i)
-      if (i < nit) wv[i] = *reinterpret_cast<const float4*>(wr + c0 + lane * 4 + i * 4 * kWave);
+      if (i < nit) wv[i] = ldf4(wr + c0 + lane * 4 + i * 4 * kWave);
   }
 
   RouteArgs b = a;

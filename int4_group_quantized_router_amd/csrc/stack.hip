@@ -232,8 +232,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   if (rrow < e_rows) {
     const float* wr = rrow < E ? s_layers[0].Wr + (size_t)rrow * H : s_layers[0].wsg;
 #pragma unroll
-    for (int m = 0; m < kWrN; ++m) wv[m] = *reinterpret_cast<const float4*>(wr + m * 256 + lane * 4);
-    if (rrow < E && s_layers[0].rb) rbv = s_layers[0].rb[rrow];
+    for (int m = 0; m < kWrN; ++m) wv[m] = ldf4(wr + m * 256 + lane * 4);
+    if (rrow < E && s_layers[0].rb) rbv = ldf(s_layers[0].rb + rrow);
   }
 
   for (int l = 0; l < a.L && !failed; ++l) {
@@ -332,12 +332,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const uint8_t* qb = blob + q_off[m] + (size_t)row * (H * BITS / 8);
-        const uint32_t* sbb = reinterpret_cast<const uint32_t*>(blob + sb_off[m]) + (size_t)row * (H / 64);
+        const uint8_t* sbb = blob + sb_off[m] + (size_t)row * (H / 64) * 4;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
           const int ci = sub + c * LPR;
           q[m][c] = ld16(qb + ci * 16);
-          sbw[m][c] = sbb[ci * F::kEpc / 64];
+          sbw[m][c] = ldu32(sbb + (ci * F::kEpc / 64) * 4);
         }
       }
     };
@@ -355,8 +355,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         if (rloc < R) {
           const int row = row0 + rloc;
           dq[n] = ld16(D.shared_blob + a.sq[2] + (size_t)row * (IS * BITS / 8) + ci * 16);
-          dsb[n] = reinterpret_cast<const uint32_t*>(D.shared_blob + a.ssb[2])
-              [(size_t)row * (IS / 64) + ci * F::kEpc / 64];
+          dsb[n] = ldu32(D.shared_blob + a.ssb[2] + ((size_t)row * (IS / 64) + ci * F::kEpc / 64) * 4);
         }
       }
     }
@@ -485,8 +484,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         if (rloc < R) {
           const int row = row0 + rloc;
           dq[n] = ld16(blob + a.lq[2] + (size_t)row * (I * BITS / 8) + ci * 16);
-          dsb[n] = reinterpret_cast<const uint32_t*>(blob + a.lsb[2])
-              [(size_t)row * (I / 64) + ci * F::kEpc / 64];
+          dsb[n] = ldu32(blob + a.lsb[2] + ((size_t)row * (I / 64) + ci * F::kEpc / 64) * 4);
         }
       }
     }
@@ -496,8 +494,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       const StackLayerDesc& Dn = s_layers[l + 1];
       const float* wr = rrow < E ? Dn.Wr + (size_t)rrow * H : Dn.wsg;
 #pragma unroll
-      for (int m = 0; m < kWrN; ++m) wv[m] = *reinterpret_cast<const float4*>(wr + m * 256 + lane * 4);
-      if (rrow < E && Dn.rb) rbv = Dn.rb[rrow];
+      for (int m = 0; m < kWrN; ++m) wv[m] = ldf4(wr + m * 256 + lane * 4);
+      if (rrow < E && Dn.rb) rbv = ldf(Dn.rb + rrow);
     }
 
     // ---- down + combine for rows [row0, row0 + R): shared rows first (its h
