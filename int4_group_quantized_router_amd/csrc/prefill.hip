@@ -459,36 +459,42 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // the K pipeline for a compile-time row-block count
+  // the K pipeline for a compile-time row-block count.  Loads run two K
+  // groups ahead: group kg+2's A and B are requested before group kg+1's A
+  // (already in registers) is staged, so in-order completion never makes the
+  // staging wait for the newest requests.
   auto run = [&](auto nrb_c) __attribute__((always_inline)) {
-    // prologue: A of groups 0 (in LDS) and 1 (in registers); B of groups 0, 1
-    ARow ar;
+    ARow a0, a1;
     R bq0, bq1;
-    load_a(ar, 0);
+    load_a(a0, 0);
     load_b(bq0, 0);
-    if (NK > 1) load_b(bq1, 1);
-    store_a(ar, 0);
-    if (NK > 1) load_a(ar, 1);
+    if (NK > 1) {
+      load_a(a1, 1);
+      load_b(bq1, 1);
+    }
+    store_a(a0, 0);
     __syncthreads();
-    // iteration kg: MFMAs on group kg; stage A of kg+1; request A of kg+2 and
-    // B of kg+2 (into the register set group kg just used)
     int kg = 0;
     for (; kg + 2 < NK; kg += 2) {
+      // group kg on stage 0; a1 holds A of kg+1
       compute(nrb_c, 0, bq0);
+      load_a(a0, kg + 2);
       load_b(bq0, kg + 2);
-      store_a(ar, 1);
-      load_a(ar, kg + 2);
+      store_a(a1, 1);
       __syncthreads();
+      // group kg+1 on stage 1; a0 holds A of kg+2
       compute(nrb_c, 1, bq1);
-      if (kg + 3 < NK) load_b(bq1, kg + 3);
-      store_a(ar, 0);
-      if (kg + 3 < NK) load_a(ar, kg + 3);
+      if (kg + 3 < NK) {
+        load_a(a1, kg + 3);
+        load_b(bq1, kg + 3);
+      }
+      store_a(a0, 0);
       __syncthreads();
     }
-    if (kg < NK) {  // one or two groups left: kg (stage 0) and maybe kg + 1 (in registers)
+    if (kg < NK) {  // one or two groups left: kg (stage 0) and maybe kg + 1 (a1)
       compute(nrb_c, 0, bq0);
       if (kg + 1 < NK) {
-        store_a(ar, 1);
+        store_a(a1, 1);
         __syncthreads();
         compute(nrb_c, 1, bq1);
       }
