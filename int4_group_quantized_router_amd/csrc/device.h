@@ -76,6 +76,11 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
 typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
+// 16-byte global load as a native vector (stays in registers as-is).
+__device__ __forceinline__ u32x4_v ld16v(const void* p) {
+  return *(__attribute__((address_space(1))) const u32x4_v*)p;
+}
+
 // 16-byte global load.
 __device__ __forceinline__ uint4 ld16(const void* p) {
   const u32x4_v v = *(__attribute__((address_space(1))) const u32x4_v*)p;

@@ -28,6 +28,11 @@ struct RouteArgs {
   int32_t* slot_expert;   // [T*k]
   int8_t* jmap;           // [T*k][kJmapStride]: j of token t in slot s, or -1
   int32_t* counts;        // [E] per-expert selection counts (atomic adds), or NULL
+  // top-k over MFMA partial sums (launch_topk_only): logits = sum of
+  // part[0..ksplit) in order + rb, written to `logits` when that is not
+  // NULL; the shared gate is then sigmoid(x . wsg) computed per token here
+  const float* part;      // f32 [ksplit][T][E], or NULL
+  int ksplit;
 };
 
 // Kernels whose LDS (dynamic `bytes` plus up to 8 KiB static) may exceed
@@ -98,14 +103,15 @@ struct PrefillArgs {
   uint16_t* y_bf16;             // [T, H] or NULL
 };
 
-// Router for many tokens: logits = x Wr^T + rb with Wr held as three bf16
-// planes (hi + mid + lo == Wr exactly) on bf16 MFMA with f32 accumulation.
-// wr3: bf16 [3][E + 1][H]; row E holds wsg (zeros if wsg is NULL).
-hipError_t launch_split_router(const float* Wr, const float* wsg, int E, int H, uint16_t* wr3,
-                               hipStream_t s);
-hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3,
-                              const float* bias, int has_wsg, int E, float* logits,
-                              float* sigma_raw, hipStream_t s);
+// Router for many tokens on bf16 MFMA with f32 accumulation: Wr is held as
+// three bf16 planes (hi + mid + lo == Wr exactly), wr3: bf16 [3][E][H].  The
+// GEMM splits K into router_splits(T, E, H) slices and writes partial sums
+// part: f32 [splits][T][E]; the top-k adds them in slice order, then rb.
+constexpr int kRouterMaxSplits = 4;
+int router_splits(int T, int E, int H);  // 1, 2 or 4
+hipError_t launch_split_router(const float* Wr, int E, int H, uint16_t* wr3, hipStream_t s);
+hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3, int E,
+                              float* part, hipStream_t s);
 hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_gu(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);

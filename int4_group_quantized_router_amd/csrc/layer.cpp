@@ -318,8 +318,8 @@ int32_t ensure_prefill_ws(moe_layer* L, int T) {
   const int64_t P = (int64_t)T * k, R = P + T;
   const int mt = max_tiles_for(T, k, E);
   const size_t sizes[] = {
-      (size_t)3 * (E + 1) * H * 2,  // wr3
-      (size_t)T * E * 4,            // logits
+      (size_t)3 * E * H * 2,        // wr3
+      (size_t)kRouterMaxSplits * T * E * 4,  // router partial sums (any T' <= T)
       (size_t)T * k * 4,            // idx
       (size_t)T * k * 4,            // w
       (size_t)T * 4,                // sigma
@@ -386,19 +386,22 @@ int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16
   const moe_layer_cfg& c = L->cfg;
   const int E = c.experts, k = c.top_k, H = c.hidden;
   if (!L->wr3_ready) {
-    MOE_HIP_TRY(launch_split_router(L->Wr, L->wsg, E, H, L->wr3, stream));
+    MOE_HIP_TRY(launch_split_router(L->Wr, E, H, L->wr3, stream));
     L->wr3_ready = true;
   }
   timer_mark(MOE_KERNEL_ROUTE, true, stream);
-  MOE_HIP_TRY(launch_router_gemm(x, T, H, L->wr3, L->rb, 1, E, L->pf_logits, L->pf_sigma, stream));
+  MOE_HIP_TRY(launch_router_gemm(x, T, H, L->wr3, E, L->pf_logits, stream));
   timer_mark(MOE_KERNEL_ROUTE, false, stream);
   RouteArgs r{};
+  r.x = x;
   r.T = T;
   r.H = H;
   r.E = E;
   r.k = k;
+  r.rb = L->rb;
   r.wsg = L->wsg;
-  r.logits = L->pf_logits;
+  r.part = L->pf_logits;
+  r.ksplit = router_splits(T, E, H);
   r.idx = idx_out ? idx_out : L->pf_idx;
   r.w = w_out ? w_out : L->pf_w;
   r.sigma = L->pf_sigma;
@@ -506,15 +509,24 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
   if (T <= MOE_MAX_DECODE_T) {
     MOE_HIP_TRY(launch_route(r, stream));
   } else {
-    // many tokens: router on bf16 MFMA with Wr split into three exact planes
+    // many tokens: router on bf16 MFMA with Wr split into three exact planes;
+    // the top-k sums the K slices' partials and computes the shared gate
+    const int ks = router_splits(T, E, H);
     uint16_t* wr3 = nullptr;
-    MOE_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&wr3), (size_t)3 * (E + 1) * H * 2, stream));
-    hipError_t e = launch_split_router(Wr, r.wsg, E, H, wr3, stream);
-    if (e == hipSuccess)
-      e = launch_router_gemm(x, T, H, wr3, rb, r.wsg ? 1 : 0, E, logits, sigma, stream);
+    float* part = nullptr;
+    MOE_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&wr3), (size_t)3 * E * H * 2, stream));
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part), (size_t)ks * T * E * 4, stream);
+    if (e == hipSuccess) e = launch_split_router(Wr, E, H, wr3, stream);
+    if (e == hipSuccess) e = launch_router_gemm(x, T, H, wr3, E, part, stream);
+    r.part = part;
+    r.ksplit = ks;
+    if (e == hipSuccess) e = launch_topk_only(r, stream);
     hipError_t e2 = hipFreeAsync(wr3, stream);
+    hipError_t e3 = part ? hipFreeAsync(part, stream) : hipSuccess;
     MOE_HIP_TRY(e);
     MOE_HIP_TRY(e2);
+    MOE_HIP_TRY(e3);
+    return MOE_OK;
   }
   MOE_HIP_TRY(launch_topk_only(r, stream));
   return MOE_OK;

@@ -49,7 +49,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int BM = kPrefillBM;        // grouped-GEMM tile rows
-constexpr int RBM = 128;              // router GEMM tile (tokens and experts)
 constexpr int KG = 64;                // K per step = one quantisation group
 constexpr int kLdsRow = KG * 2 + 16;  // bytes per weight row in LDS (padded)
 
@@ -107,13 +106,12 @@ __device__ __forceinline__ const uint8_t* group_blob(const PrefillArgs& a, int g
 
 // ------------------------------------------------------------- router
 
-__global__ __launch_bounds__(kThreads) void split_router_kernel(const float* Wr, const float* wsg,
-                                                                int E, int H, uint16_t* wr3) {
-  const int64_t n = (int64_t)(E + 1) * H;
+__global__ __launch_bounds__(kThreads) void split_router_kernel(const float* Wr, int E, int H,
+                                                                uint16_t* wr3) {
+  const int64_t n = (int64_t)E * H;
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= n) return;
-  const int64_t e = i / H;
-  const float W = e < E ? Wr[i] : (wsg ? wsg[i - (int64_t)E * H] : 0.f);
+  const float W = Wr[i];
   const uint32_t hi = f32_to_bf16(W);
   const float r1 = W - bf16_to_f32(hi);
   const uint32_t mid = f32_to_bf16(r1);
@@ -123,69 +121,107 @@ __global__ __launch_bounds__(kThreads) void split_router_kernel(const float* Wr,
   wr3[2 * n + i] = (uint16_t)f32_to_bf16(r2);
 }
 
-// logits for a 128-token x 128-expert tile; row E of the planes is wsg
-// (its result, wsg . x, goes to sigma_raw).
-__global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
-    const uint16_t* x, int T, int H, const uint16_t* wr3, const float* bias, int E, int has_wsg,
-    float* logits, float* sigma_raw) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Partial logits of a 128-token x 128-expert tile over one slice of the K
+// groups: part[split][t][e] = sum over the slice of x[t] . (hi + mid + lo)[e].
+// Each 64-wide K step is staged in LDS (x rows and the three planes' rows,
+// 16-byte pieces, 8 threads per 128-byte row segment so every load
+// instruction reads whole segments), double buffered, the next step's loads
+// in flight during this step's MFMAs.  Four waves, each 64 tokens x 64
+// experts (2 x 2 MFMA 32x32x16 tiles).  Per step the products go to a fresh
+// accumulator that is then added to the running total, so every f32 sum has
+// a bounded depth.  Tokens / experts past the end read a valid row and are
+// never stored.
+constexpr int RT = 128;
+constexpr int kRouterStage = 4 * RT * kLdsRow;  // x rows + three planes: 73,728 bytes
+
+__global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t* x, int T, int H,
+                                                                  const uint16_t* wr3, int E,
+                                                                  int n_et, int ks, float* part) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int mt, inner;
+  tile_of_block(n_et * ks, &mt, &inner);
+  if (mt * RT >= T) return;
+  const int et = inner / ks, sp = inner % ks;
+  const int G = H / KG;
+  const int g0 = sp * G / ks, nk = (sp + 1) * G / ks - g0;
+  const int t0 = mt * RT, e0 = et * RT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mh = wave >> 1, nh = wave & 1, kh = lane >> 5, l32 = lane & 31;
-  const int t0 = blockIdx.x * RBM, e0 = blockIdx.y * RBM;
-  const int rows = E + (has_wsg ? 1 : 0);
-  const int64_t plane = (int64_t)(E + 1) * H;
-  const uint16_t* arow[2];
-  bool av[2];
+  const int64_t plane = (int64_t)E * H;
+
+  const int part8 = tid & 7, r8 = tid >> 3;
+  uint32_t aoff[4], boff[4];  // element offsets: T * H and E * H are < 2^31
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int t = t0 + mh * 64 + rb * 32 + l32;
-    av[rb] = t < T;
-    arow[rb] = x + (size_t)(av[rb] ? t : 0) * H + kh * 32;
+  for (int i = 0; i < 4; ++i) {
+    aoff[i] = (uint32_t)min(t0 + r8 + 32 * i, T - 1) * (uint32_t)H + part8 * 8;
+    boff[i] = (uint32_t)min(e0 + r8 + 32 * i, E - 1) * (uint32_t)H + part8 * 8;
   }
-  const uint16_t* brow[2];
-  bool bv[2];
+  const int sdst = r8 * kLdsRow + part8 * 16;
+  u32x4_v ra[4], rw[3][4];
+  auto load = [&](int g) __attribute__((always_inline)) {
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int e = e0 + nh * 64 + cb * 32 + l32;
-    bv[cb] = e < rows;
-    brow[cb] = wr3 + (size_t)(bv[cb] ? e : 0) * H + kh * 32;
-  }
+    for (int i = 0; i < 4; ++i) ra[i] = ld16v(x + g * KG + aoff[i]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rw[p][i] = ld16v(wr3 + p * plane + g * KG + boff[i]);
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+    uint8_t* st = smem + buf * kRouterStage + sdst;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_v*>(st + 32 * i * kLdsRow) = ra[i];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4_v*>(st + ((p + 1) * RT + 32 * i) * kLdsRow) = rw[p][i];
+  };
+
   f32x16_t tot[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) tot[i][j] = f32x16_t{};
-  // out-of-range rows / experts read row 0 (clamped above) and are never stored
-  for (int kg = 0; kg < H / KG; ++kg) {
-    uint4 af[2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) af[rb][s] = ld16(arow[rb] + kg * KG + s * 8);
+  load(g0);
+  store(0);
+  __syncthreads();
+  for (int i = 0; i < nk; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < nk) load(g0 + i + 1);
+    const uint8_t* st = smem + buf * kRouterStage + kh * 64;
     f32x16_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+      for (int c = 0; c < 2; ++c) acc[r][c] = f32x16_t{};
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      uint4 bf[2][4];
+    for (int s4 = 0; s4 < 4; ++s4) {
+      uint4 af[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int rb = 0; rb < 2; ++rb)
+        af[rb] = *reinterpret_cast<const uint4*>(st + (mh * 64 + rb * 32 + l32) * kLdsRow + s4 * 16);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          bf[cb][s] = ld16(brow[cb] + p * plane + kg * KG + s * 8);
+      for (int p = 0; p < 3; ++p) {
+        uint4 bf[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+        for (int cb = 0; cb < 2; ++cb)
+          bf[cb] = *reinterpret_cast<const uint4*>(
+              st + ((p + 1) * RT + nh * 64 + cb * 32 + l32) * kLdsRow + s4 * 16);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma(af[rb][s], bf[cb][s], acc[rb][cb]);
+          for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = mfma(af[rb], bf[cb], acc[rb][cb]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) tot[i][j] += acc[i][j];
+      for (int c = 0; c < 2; ++c) tot[r][c] += acc[r][c];
+    if (i + 1 < nk) store(buf ^ 1);
+    __syncthreads();
   }
+  float* out = part + (size_t)sp * T * E;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -194,11 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
       for (int v = 0; v < 16; ++v) {
         const int t = t0 + mh * 64 + rb * 32 + (v >> 2) * 8 + kh * 4 + (v & 3);
         const int e = e0 + nh * 64 + cb * 32 + l32;
-        if (t >= T || e >= rows) continue;
-        if (e < E)
-          logits[(size_t)t * E + e] = tot[rb][cb][v] + (bias ? bias[e] : 0.f);
-        else
-          sigma_raw[t] = tot[rb][cb][v];
+        if (t < T && e < E) out[(size_t)t * E + e] = tot[rb][cb][v];
       }
 }
 
@@ -207,45 +239,80 @@ __global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(
 // One block: group sizes (group E = shared expert = all tokens) -> row
 // offsets and the tile list; resets the counts for the next call.
 __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a) {
-  __shared__ int s_rows[1026];
-  __shared__ int s_tiles[1026];
+  constexpr int kPer = 5;  // groups per thread: up to kThreads * kPer groups
+  __shared__ int s_wr[kThreads / kWave], s_wt[kThreads / kWave];
   const int G = a.E + 1;
-  for (int g = threadIdx.x; g < G; g += kThreads) {
-    const int c = g < a.E ? a.counts[g] : a.T;
-    s_rows[g] = c;
-    s_tiles[g] = (c + BM - 1) / BM;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g0 = threadIdx.x * kPer;
+  int c[kPer], r = 0, tl = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int g = g0 + i;
+    c[i] = g < a.E ? a.counts[g] : (g == a.E ? a.T : 0);
+    r += c[i];
+    tl += (c[i] + BM - 1) / BM;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int r = 0, tl = 0;
-    for (int g = 0; g < G; ++g) {
-      const int c = s_rows[g], n = s_tiles[g];
-      s_rows[g] = r;
-      s_tiles[g] = tl;
-      r += c;
-      tl += n;
+  // inclusive wave scan of (r, tl), then across the waves
+  int ir = r, it = tl;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int yr = __shfl_up(ir, d), yt = __shfl_up(it, d);
+    if (lane >= d) {
+      ir += yr;
+      it += yt;
     }
-    s_rows[G] = r;
-    s_tiles[G] = tl;
-    a.row_off[G] = r;
-    *a.n_tiles = tl;
+  }
+  if (lane == kWave - 1) {
+    s_wr[wave] = ir;
+    s_wt[wave] = it;
   }
   __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kThreads) {
-    a.row_off[g] = s_rows[g];
-    const int n = s_tiles[g + 1] - s_tiles[g];
-    for (int i = 0; i < n; ++i) {
-      if (s_tiles[g] + i < a.max_tiles) {
-        a.tile_group[s_tiles[g] + i] = g;
-        a.tile_m0[s_tiles[g] + i] = i * BM;
+  int br = ir - r, bt = it - tl;
+  for (int w = 0; w < wave; ++w) {
+    br += s_wr[w];
+    bt += s_wt[w];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int g = g0 + i;
+    if (g < G) {
+      a.row_off[g] = br;
+      const int n = (c[i] + BM - 1) / BM;
+      for (int j = 0; j < n; ++j) {
+        if (bt + j < a.max_tiles) {
+          a.tile_group[bt + j] = g;
+          a.tile_m0[bt + j] = j * BM;
+        }
+      }
+      if (g < a.E) a.counts[g] = 0;  // cursors of the scatter
+      if (g == G - 1) {
+        a.row_off[G] = br + c[i];
+        *a.n_tiles = bt + n;
       }
     }
-    if (g < a.E) a.counts[g] = 0;
+    br += c[i];
+    bt += (c[i] + BM - 1) / BM;
   }
 }
 
-// One block per group: the group's rows in token order (stable).
-__global__ __launch_bounds__(kThreads) void prefill_compact_kernel(PrefillArgs a) {
+// Scatter every (token, choice) pair p = t * k + j to its expert's segment
+// at an atomic cursor (order inside a segment arbitrary; fixed by the sort).
+// perm_tok temporarily holds p.
+__global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(PrefillArgs a) {
+  const int p = blockIdx.x * kThreads + threadIdx.x;
+  if (p >= a.T * a.k) return;
+  const int e = a.idx[p];
+  a.perm_tok[a.row_off[e] + atomicAdd(a.counts + e, 1)] = p;
+}
+
+constexpr int kSortMax = 8192;  // longest segment sorted in LDS
+
+// One block per group: its rows in (token, choice) order, i.e. p ascending
+// (stable w.r.t. token order), then perm_tok = token, inv = row.  Segments
+// up to kSortMax long are sorted in LDS (bitonic); a longer segment is
+// rebuilt by a ballot compaction over all pairs.  Resets the counters.
+__global__ __launch_bounds__(kThreads) void prefill_segsort_kernel(PrefillArgs a) {
+  __shared__ int keys[kSortMax];
   __shared__ int s_wcnt[kThreads / kWave];
   const int e = blockIdx.x;
   const int base = a.row_off[e];
@@ -253,25 +320,54 @@ __global__ __launch_bounds__(kThreads) void prefill_compact_kernel(PrefillArgs a
     for (int t = threadIdx.x; t < a.T; t += kThreads) a.perm_tok[base + t] = t;
     return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int P = a.T * a.k;
-  int running = 0;
-  for (int p0 = 0; p0 < P; p0 += kThreads) {
-    const int p = p0 + threadIdx.x;
-    const bool match = p < P && a.idx[p] == e;
-    const unsigned long long bal = __ballot(match);
-    if (lane == 0) s_wcnt[wave] = __popcll(bal);
+  const int n = a.row_off[e + 1] - base;
+  if (n <= kSortMax) {
+    int N = 1;
+    while (N < n) N <<= 1;
+    for (int i = threadIdx.x; i < N; i += kThreads) keys[i] = i < n ? a.perm_tok[base + i] : 0x7fffffff;
     __syncthreads();
-    int before = running;
-    for (int w = 0; w < wave; ++w) before += s_wcnt[w];
-    if (match) {
-      const int pos = base + before + __popcll(bal & lanes_below());
-      a.perm_tok[pos] = p / a.k;
-      a.inv[p] = pos;
+    for (int kk = 2; kk <= N; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < N; i += kThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const int x = keys[i], y = keys[ixj];
+            if ((x > y) == ((i & kk) == 0)) {
+              keys[i] = y;
+              keys[ixj] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
-    for (int w = 0; w < kThreads / kWave; ++w) running += s_wcnt[w];
-    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      const int p = keys[i];
+      a.perm_tok[base + i] = p / a.k;
+      a.inv[p] = base + i;
+    }
+  } else {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int P = a.T * a.k;
+    int running = 0;
+    for (int p0 = 0; p0 < P; p0 += kThreads) {
+      const int p = p0 + threadIdx.x;
+      const bool match = p < P && a.idx[p] == e;
+      const unsigned long long bal = __ballot(match);
+      if (lane == 0) s_wcnt[wave] = __popcll(bal);
+      __syncthreads();
+      int before = running;
+      for (int w = 0; w < wave; ++w) before += s_wcnt[w];
+      if (match) {
+        const int pos = base + before + __popcll(bal & lanes_below());
+        a.perm_tok[pos] = p / a.k;
+        a.inv[p] = pos;
+      }
+      for (int w = 0; w < kThreads / kWave; ++w) running += s_wcnt[w];
+      __syncthreads();
+    }
   }
+  if (threadIdx.x == 0) a.counts[e] = 0;
 }
 
 // ------------------------------------------------------ grouped GEMMs
@@ -578,20 +674,31 @@ int pad8(int n) { return (n + 7) / 8 * 8; }
 
 }  // namespace
 
-hipError_t launch_split_router(const float* Wr, const float* wsg, int E, int H, uint16_t* wr3,
-                               hipStream_t s) {
-  const int64_t n = (int64_t)(E + 1) * H;
+int router_splits(int T, int E, int H) {
+  const int tiles = (T + RT - 1) / RT * ((E + RT - 1) / RT);
+  int ks = 1;
+  while (2 * ks <= kRouterMaxSplits && 2 * ks <= H / KG && tiles * ks < 256) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_split_router(const float* Wr, int E, int H, uint16_t* wr3, hipStream_t s) {
+  const int64_t n = (int64_t)E * H;
   hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((n + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, s, Wr, wsg, E, H, wr3);
+                     dim3(kThreads), 0, s, Wr, E, H, wr3);
   return hipGetLastError();
 }
 
-hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3,
-                              const float* bias, int has_wsg, int E, float* logits,
-                              float* sigma_raw, hipStream_t s) {
-  const dim3 grid((T + RBM - 1) / RBM, (E + (has_wsg ? 1 : 0) + RBM - 1) / RBM);
-  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(kThreads), 0, s, x, T, H, wr3, bias, E,
-                     has_wsg, logits, sigma_raw);
+hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3, int E,
+                              float* part, hipStream_t s) {
+  if ((int64_t)T * H >= (1ll << 31) || (int64_t)E * H >= (1ll << 31) || H % KG != 0)
+    return hipErrorInvalidValue;
+  const int ks = router_splits(T, E, H);
+  const int n_et = (E + RT - 1) / RT;
+  const size_t lds = 2 * (size_t)kRouterStage;
+  hipError_t e = allow_lds(router_gemm_kernel, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(router_gemm_kernel, dim3(pad8((T + RT - 1) / RT) * n_et * ks), dim3(kThreads),
+                     lds, s, x, T, H, wr3, E, n_et, ks, part);
   return hipGetLastError();
 }
 
@@ -599,7 +706,11 @@ hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_compact_kernel, dim3(a.E + 1), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_scatter_kernel, dim3((a.T * a.k + kThreads - 1) / kThreads),
+                     dim3(kThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_segsort_kernel, dim3(a.E + 1), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -63,8 +63,11 @@ __device__ void stage_input(const RouteArgs& a, float* xs, float* red, int T) {
 // Top-k of tokens [t0, t1), one wave per token (ballot radix-select, see
 // wave_topk); selections go to LDS.  Logits are read from the device
 // coherence point: they may have been written by workgroups on other XCDs.
+// With MFMA partial sums (a.part) the logits are formed here, and with
+// s_sraw the shared gate's input x . wsg of each token goes to s_sraw.
 template <int VPL>
-__device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val) {
+__device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val,
+                            float* s_sraw) {
   __shared__ int tmp_e[kWaves][MOE_MAX_TOPK];
   __shared__ float tmp_v[kWaves][MOE_MAX_TOPK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -73,11 +76,46 @@ __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, floa
     const float* lg = a.logits + (size_t)t * E;
     float v[VPL];
     uint32_t key[VPL];
+    if (a.part) {
+      // partial sums of the MFMA router (earlier launch): slices in order, then rb
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      v[i] = e < E ? ld_dev(lg + e) : 0.f;
-      key[i] = e < E ? order_key(v[i]) : 0u;
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        float s = 0.f;
+        if (e < E) {
+          s = a.part[(size_t)t * E + e];
+          for (int sp = 1; sp < a.ksplit; ++sp) s += a.part[((size_t)sp * a.T + t) * E + e];
+          s += a.rb ? a.rb[e] : 0.f;
+          if (a.logits) a.logits[(size_t)t * E + e] = s;
+        }
+        v[i] = s;
+        key[i] = e < E ? order_key(s) : 0u;
+      }
+      if (s_sraw) {
+        // shared gate input wsg . x[t], f32, lane-strided then one wave sum
+        float g = 0.f;
+        for (int h = lane * 8; h < a.H; h += kWave * 8) {
+          const uint4 q = ld16(a.x + (size_t)t * a.H + h);
+          const float4 w0 = ldf4(a.wsg + h), w1 = ldf4(a.wsg + h + 4);
+          g = fmaf(bf16_lo(q.x), w0.x, g);
+          g = fmaf(bf16_hi(q.x), w0.y, g);
+          g = fmaf(bf16_lo(q.y), w0.z, g);
+          g = fmaf(bf16_hi(q.y), w0.w, g);
+          g = fmaf(bf16_lo(q.z), w1.x, g);
+          g = fmaf(bf16_hi(q.z), w1.y, g);
+          g = fmaf(bf16_lo(q.w), w1.z, g);
+          g = fmaf(bf16_hi(q.w), w1.w, g);
+        }
+        g = group_sum(g, kWave);
+        if (lane == 0) s_sraw[t - t0] = g;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+        v[i] = e < E ? ld_dev(lg + e) : 0.f;
+        key[i] = e < E ? order_key(v[i]) : 0u;
+      }
     }
     wave_topk<VPL>(v, key, k, tmp_e[wave], tmp_v[wave], s_sel + (t - t0) * k,
                    s_val + (t - t0) * k);
@@ -87,7 +125,7 @@ __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, floa
 // Renormalised weights over the chosen k (= softmax over the chosen
 // logits: the full-softmax denominator cancels) and the shared gate.
 __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_sel,
-                              const float* s_val) {
+                              const float* s_val, const float* s_sraw) {
   const int k = a.k;
   for (int t = t0 + (int)threadIdx.x; t < t1; t += kThreads) {
     const int r = t - t0;
@@ -108,7 +146,8 @@ __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_s
         a.idx[(size_t)t * k + j] = s_sel[r * k + j];
       }
     }
-    if (a.sigma && a.wsg) a.sigma[t] = 1.0f / (1.0f + expf(-ld_dev(a.sigma + t)));
+    if (a.sigma && a.wsg)
+      a.sigma[t] = 1.0f / (1.0f + expf(-(s_sraw ? s_sraw[r] : ld_dev(a.sigma + t))));
     if (a.counts) {
       for (int j = 0; j < k; ++j) atomicAdd(a.counts + s_sel[r * k + j], 1);
     }
@@ -243,9 +282,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ float s_val[NT * MOE_MAX_TOPK];
   __shared__ int s_slot[NT * MOE_MAX_TOPK];
   __shared__ int s_first[1024];
-  topk_tokens<VPL>(a, 0, a.T, s_sel, s_val);
+  topk_tokens<VPL>(a, 0, a.T, s_sel, s_val, nullptr);
   __syncthreads();
-  write_weights(a, 0, a.T, s_sel, s_val);
+  write_weights(a, 0, a.T, s_sel, s_val, nullptr);
   if (a.n_slots) build_slots(a, s_sel, s_first, s_slot);
 }
 
@@ -254,11 +293,13 @@ template <int VPL>
 __global__ __launch_bounds__(kThreads) void topk_kernel(RouteArgs a) {
   __shared__ int s_sel[kWaves * MOE_MAX_TOPK];
   __shared__ float s_val[kWaves * MOE_MAX_TOPK];
+  __shared__ float s_sraw[kWaves];
   const int t0 = blockIdx.x * kWaves;
   const int t1 = min(a.T, t0 + kWaves);
-  topk_tokens<VPL>(a, t0, t1, s_sel, s_val);
+  float* sr = a.part && a.sigma && a.wsg ? s_sraw : nullptr;
+  topk_tokens<VPL>(a, t0, t1, s_sel, s_val, sr);
   __syncthreads();
-  write_weights(a, t0, t1, s_sel, s_val);
+  write_weights(a, t0, t1, s_sel, s_val, sr);
 }
 
 template <int NT>
