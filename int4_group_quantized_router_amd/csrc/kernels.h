@@ -78,13 +78,15 @@ bool decode_shape_supported(int H, int I, int Is, int bits);
 // MFMA GEMMs with dequant-to-bf16 weight tiles, fixed-order combine.
 constexpr int kPrefillBM = 96;   // rows per grouped-GEMM tile (routed experts average ~80 rows)
 
+constexpr int kSortChunks = 64;  // chunks of (token, choice) pairs in the prefill sort
+
 struct PrefillArgs {
   int T, H, I, Is, E, k, bits, hI;
   const uint16_t* x;            // bf16 [T, H]
   const int32_t* idx;           // [T, k]
   const float* w;               // [T, k]
   const float* sigma;           // [T]
-  int32_t* counts;              // [E]: rows per expert (filled by the top-k, reset by the scan)
+  int32_t* hist;                // [kSortChunks][E]: per-chunk expert counts, then offsets
   int32_t* row_off;             // [E + 2]: first sorted row of each group (group E = shared)
   int32_t* n_tiles;             // [1]
   int32_t* tile_group;          // [max_tiles]

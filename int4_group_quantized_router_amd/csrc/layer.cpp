@@ -49,7 +49,7 @@ struct moe_layer {
   int32_t* pf_idx;
   float* pf_w;
   float* pf_sigma;
-  int32_t* pf_counts;
+  int32_t* pf_hist;
   int32_t* pf_row_off;
   int32_t* pf_ntiles;
   int32_t* pf_tg;
@@ -323,7 +323,7 @@ int32_t ensure_prefill_ws(moe_layer* L, int T) {
       (size_t)T * k * 4,            // idx
       (size_t)T * k * 4,            // w
       (size_t)T * 4,                // sigma
-      (size_t)E * 4,                // counts
+      (size_t)kSortChunks * E * 4,  // hist
       (size_t)(E + 2) * 4,          // row_off
       4,                            // n_tiles
       (size_t)mt * 4,               // tile_group
@@ -356,7 +356,7 @@ int32_t ensure_prefill_ws(moe_layer* L, int T) {
   L->pf_idx = static_cast<int32_t*>(parts[2]);
   L->pf_w = static_cast<float*>(parts[3]);
   L->pf_sigma = static_cast<float*>(parts[4]);
-  L->pf_counts = static_cast<int32_t*>(parts[5]);
+  L->pf_hist = static_cast<int32_t*>(parts[5]);
   L->pf_row_off = static_cast<int32_t*>(parts[6]);
   L->pf_ntiles = static_cast<int32_t*>(parts[7]);
   L->pf_tg = static_cast<int32_t*>(parts[8]);
@@ -405,7 +405,6 @@ int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16
   r.idx = idx_out ? idx_out : L->pf_idx;
   r.w = w_out ? w_out : L->pf_w;
   r.sigma = L->pf_sigma;
-  r.counts = L->pf_counts;
   MOE_HIP_TRY(launch_topk_only(r, stream));
 
   PrefillArgs p{};
@@ -421,7 +420,7 @@ int32_t forward_prefill(moe_layer* L, const uint16_t* x, int T, uint16_t* y_bf16
   p.idx = r.idx;
   p.w = r.w;
   p.sigma = L->pf_sigma;
-  p.counts = L->pf_counts;
+  p.hist = L->pf_hist;
   p.row_off = L->pf_row_off;
   p.n_tiles = L->pf_ntiles;
   p.tile_group = L->pf_tg;

@@ -11,10 +11,10 @@
 //      MFMA with f32 accumulation computes exactly the products of the f32
 //      router; each 64-wide K group is accumulated separately and then added
 //      to the running total, which bounds the summation depth.
-//   2. sort: per-expert counts (atomic integer adds in the top-k), a scan to
-//      row offsets and a tile list, then a per-expert ballot compaction that
-//      keeps token order (stable).  The shared expert is one more group whose
-//      rows are all tokens.
+//   2. sort: per-chunk expert histograms (LDS), one scan to row offsets, chunk
+//      offsets and a tile list, a scatter at LDS cursors, then a per-expert
+//      sort of each expert's pairs, so rows keep (token, choice) order.  The
+//      shared expert is one more group whose rows are all tokens.
 //   3. gate/up grouped GEMM: one 128-row tile of an expert's rows x 64
 //      intermediate columns of BOTH gate and up per workgroup; the 128 x 64
 //      weight tile of each K group (one quantisation group) is dequantised
@@ -236,19 +236,60 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t
 
 // --------------------------------------------------------------- sort
 
-// One block: group sizes (group E = shared expert = all tokens) -> row
-// offsets and the tile list; resets the counts for the next call.
-__global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a) {
-  constexpr int kPer = 5;  // groups per thread: up to kThreads * kPer groups
-  __shared__ int s_wr[kThreads / kWave], s_wt[kThreads / kWave];
+// Per-chunk expert histograms: the T * k (token, choice) pairs are cut into
+// kSortChunks contiguous chunks; hist[c][e] = pairs of chunk c that chose e.
+__device__ __forceinline__ void sort_chunk(const PrefillArgs& a, int c, int* p0, int* p1) {
+  const int P = a.T * a.k, len = (P + kSortChunks - 1) / kSortChunks;
+  *p0 = min(P, c * len);
+  *p1 = min(P, *p0 + len);
+}
+
+__global__ __launch_bounds__(kThreads) void prefill_hist_kernel(PrefillArgs a) {
+  __shared__ int h[1024];
+  for (int e = threadIdx.x; e < a.E; e += kThreads) h[e] = 0;
+  __syncthreads();
+  int p0, p1;
+  sort_chunk(a, blockIdx.x, &p0, &p1);
+  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) atomicAdd(&h[a.idx[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += kThreads) a.hist[blockIdx.x * a.E + e] = h[e];
+}
+
+// One block: per expert, counts over the chunks and each chunk's offset
+// inside the expert's rows (hist rewritten in place as the exclusive prefix
+// over chunks); then group sizes (group E = shared expert = all tokens) ->
+// row offsets and the tile list.
+constexpr int kScanThreads = 1024;
+
+static_assert(kSortChunks % 16 == 0, "scan loads chunk counts 16 at a time");
+
+__global__ __launch_bounds__(kScanThreads) void prefill_scan_kernel(PrefillArgs a) {
+  constexpr int kPer = 2;  // groups per thread: up to 2048 groups
+  __shared__ int s_cnt[kPer * kScanThreads];
+  __shared__ int s_wr[kScanThreads / kWave], s_wt[kScanThreads / kWave];
   const int G = a.E + 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g0 = threadIdx.x * kPer;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < a.E) {
+    int run = 0;
+    for (int c0 = 0; c0 < kSortChunks; c0 += 16) {  // 16 loads in flight
+      int v[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) v[c] = a.hist[(c0 + c) * a.E + tid];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        a.hist[(c0 + c) * a.E + tid] = run;
+        run += v[c];
+      }
+    }
+    s_cnt[tid] = run;
+  }
+  if (tid == 0) s_cnt[a.E] = a.T;
+  __syncthreads();
+  const int g0 = tid * kPer;
   int c[kPer], r = 0, tl = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int g = g0 + i;
-    c[i] = g < a.E ? a.counts[g] : (g == a.E ? a.T : 0);
+    c[i] = g0 + i < G ? s_cnt[g0 + i] : 0;
     r += c[i];
     tl += (c[i] + BM - 1) / BM;
   }
@@ -284,7 +325,6 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a) {
           a.tile_m0[bt + j] = j * BM;
         }
       }
-      if (g < a.E) a.counts[g] = 0;  // cursors of the scatter
       if (g == G - 1) {
         a.row_off[G] = br + c[i];
         *a.n_tiles = bt + n;
@@ -295,14 +335,18 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a) {
   }
 }
 
-// Scatter every (token, choice) pair p = t * k + j to its expert's segment
-// at an atomic cursor (order inside a segment arbitrary; fixed by the sort).
-// perm_tok temporarily holds p.
+// Scatter every (token, choice) pair p = t * k + j of a chunk to its
+// expert's rows at an LDS cursor that starts at the chunk's offset (order
+// inside a chunk's share arbitrary; fixed by the sort).  perm_tok
+// temporarily holds p.
 __global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(PrefillArgs a) {
-  const int p = blockIdx.x * kThreads + threadIdx.x;
-  if (p >= a.T * a.k) return;
-  const int e = a.idx[p];
-  a.perm_tok[a.row_off[e] + atomicAdd(a.counts + e, 1)] = p;
+  __shared__ int cur[1024];
+  for (int e = threadIdx.x; e < a.E; e += kThreads)
+    cur[e] = a.row_off[e] + a.hist[blockIdx.x * a.E + e];
+  __syncthreads();
+  int p0, p1;
+  sort_chunk(a, blockIdx.x, &p0, &p1);
+  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) a.perm_tok[atomicAdd(&cur[a.idx[p]], 1)] = p;
 }
 
 constexpr int kSortMax = 8192;  // longest segment sorted in LDS
@@ -310,7 +354,7 @@ constexpr int kSortMax = 8192;  // longest segment sorted in LDS
 // One block per group: its rows in (token, choice) order, i.e. p ascending
 // (stable w.r.t. token order), then perm_tok = token, inv = row.  Segments
 // up to kSortMax long are sorted in LDS (bitonic); a longer segment is
-// rebuilt by a ballot compaction over all pairs.  Resets the counters.
+// rebuilt by a ballot compaction over all pairs.
 __global__ __launch_bounds__(kThreads) void prefill_segsort_kernel(PrefillArgs a) {
   __shared__ int keys[kSortMax];
   __shared__ int s_wcnt[kThreads / kWave];
@@ -367,7 +411,6 @@ __global__ __launch_bounds__(kThreads) void prefill_segsort_kernel(PrefillArgs a
       __syncthreads();
     }
   }
-  if (threadIdx.x == 0) a.counts[e] = 0;
 }
 
 // ------------------------------------------------------ grouped GEMMs
@@ -703,11 +746,13 @@ hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* w
 }
 
 hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_hist_kernel, dim3(kSortChunks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_scatter_kernel, dim3((a.T * a.k + kThreads - 1) / kThreads),
-                     dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_scatter_kernel, dim3(kSortChunks), dim3(kThreads), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_segsort_kernel, dim3(a.E + 1), dim3(kThreads), 0, s, a);
