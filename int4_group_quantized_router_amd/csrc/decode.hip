@@ -394,12 +394,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* blob, 
   const uint32_t sbw = reinterpret_cast<const uint32_t*>(blob + L.sb_off[which])
       [r * (cols / 64) + c0 / 64];
   const float s = bf16_lo(sbw), b = bf16_hi(sbw);
+  // the same f16-subnormal fma_mix arithmetic as the many-token GEMMs, so
+  // this entry point pins it bit for bit against s * q + b
+  float v[F::kPerWord];
+  if constexpr (BITS == 4)
+    dequant8_int4(w, s, b, v);
+  else
+    dequant4_int8(w, s, b, v);
 #pragma unroll
   for (int i = 0; i < F::kPerWord; ++i) {
-    const float qv = (float)((w >> (BITS * i)) & ((1u << BITS) - 1u));
-    const float v = fmaf(s, qv, b);
-    out_f32[e0 + i] = v;
-    if (out_bf16) out_bf16[e0 + i] = (uint16_t)f32_to_bf16(v);
+    out_f32[e0 + i] = v[i];
+    if (out_bf16) out_bf16[e0 + i] = (uint16_t)f32_to_bf16(v[i]);
   }
 }
 

@@ -32,6 +32,54 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Affine dequantisation s * q + b of packed integer fields without integer
+// to float conversions.  A field of up to 8 bits placed in the low bits of a
+// 16-bit half is an f16 subnormal, q * 2^-24 (f16 subnormals are kept: the
+// kernels run with f16/f64 denormals enabled); v_fma_mix_f32 widens it
+// exactly and computes fma(s * 2^24, q * 2^-24, b) = fma(s, q, b) with one
+// rounding, bit for bit what fmaf(s, (float)q, b) gives.  A field at bits
+// 4..7 of a half is q * 2^-20, taken with s * 2^20.
+__device__ __forceinline__ float fma_mix_lo(float s, uint32_t h, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(s), "v"(h), "v"(c));
+  return d;
+}
+__device__ __forceinline__ float fma_mix_hi(float s, uint32_t h, float c) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=v"(d)
+      : "v"(s), "v"(h), "v"(c));
+  return d;
+}
+__device__ __forceinline__ uint32_t and_lit(uint32_t w, uint32_t m) { return w & m; }
+
+// The 8 int4 fields of w (field i at bits 4i..4i+3), dequantised: f[i] =
+// fmaf(s, q_i, b).  17 VALU operations.
+__device__ __forceinline__ void dequant8_int4(uint32_t w, float s, float b, float* f) {
+  const float s24 = s * 16777216.0f, s20 = s * 1048576.0f;  // exact: powers of two
+  const uint32_t w8 = w >> 8;
+  const uint32_t a0 = w & 0x000F000Fu, a1 = w & 0x00F000F0u;    // fields 0, 4 / 1, 5
+  const uint32_t a2 = w8 & 0x000F000Fu, a3 = w8 & 0x00F000F0u;  // fields 2, 6 / 3, 7
+  f[0] = fma_mix_lo(s24, a0, b);
+  f[4] = fma_mix_hi(s24, a0, b);
+  f[1] = fma_mix_lo(s20, a1, b);
+  f[5] = fma_mix_hi(s20, a1, b);
+  f[2] = fma_mix_lo(s24, a2, b);
+  f[6] = fma_mix_hi(s24, a2, b);
+  f[3] = fma_mix_lo(s20, a3, b);
+  f[7] = fma_mix_hi(s20, a3, b);
+}
+
+// The 4 int8 fields of w (field i at bits 8i..8i+7): f[i] = fmaf(s, q_i, b).
+__device__ __forceinline__ void dequant4_int8(uint32_t w, float s, float b, float* f) {
+  const float s24 = s * 16777216.0f;
+  const uint32_t a0 = w & 0x00FF00FFu, a1 = (w >> 8) & 0x00FF00FFu;  // fields 0, 2 / 1, 3
+  f[0] = fma_mix_lo(s24, a0, b);
+  f[2] = fma_mix_hi(s24, a0, b);
+  f[1] = fma_mix_lo(s24, a1, b);
+  f[3] = fma_mix_hi(s24, a1, b);
+}
+
 // v_perm_b32: byte i of the result is byte sel[i] of {hi:lo} (0-3 from lo, 4-7 from hi).
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

@@ -79,23 +79,23 @@ __device__ __forceinline__ void tile_of_block(int nt_per_tile, int* tile, int* n
 }
 
 // One packed word -> bf16 values in natural order: 8 (int4, as a uint4) or
-// 4 (int8, low half of the uint4).
+// 4 (int8, low half of the uint4); each value is s * q + b in f32 (one
+// rounding), then rounded to nearest even.  s24 = s * 2^24 and s20 = s * 2^20
+// are hoisted by the caller (see dequant8_int4).
 template <int BITS>
-__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s, float b) {
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, float s24, float s20, float b) {
   if (BITS == 4) {
-    uint32_t lo, hi;
-    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(w));
-    asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(hi) : "v"(w >> 4));
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = pack_bf16(fmaf(s, (float)((lo >> (8 * i)) & 0xFFu), b),
-                       fmaf(s, (float)((hi >> (8 * i)) & 0xFFu), b));
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    const uint32_t w8 = w >> 8;
+    const uint32_t a0 = w & 0x000F000Fu, a1 = w & 0x00F000F0u;
+    const uint32_t a2 = w8 & 0x000F000Fu, a3 = w8 & 0x00F000F0u;
+    return make_uint4(pack_bf16(fma_mix_lo(s24, a0, b), fma_mix_lo(s20, a1, b)),
+                      pack_bf16(fma_mix_lo(s24, a2, b), fma_mix_lo(s20, a3, b)),
+                      pack_bf16(fma_mix_hi(s24, a0, b), fma_mix_hi(s20, a1, b)),
+                      pack_bf16(fma_mix_hi(s24, a2, b), fma_mix_hi(s20, a3, b)));
   } else {
-    const uint32_t o0 = pack_bf16(fmaf(s, (float)(w & 0xFFu), b), fmaf(s, (float)((w >> 8) & 0xFFu), b));
-    const uint32_t o1 = pack_bf16(fmaf(s, (float)((w >> 16) & 0xFFu), b), fmaf(s, (float)(w >> 24), b));
-    return make_uint4(o0, o1, 0u, 0u);
+    const uint32_t a0 = w & 0x00FF00FFu, a1 = (w >> 8) & 0x00FF00FFu;
+    return make_uint4(pack_bf16(fma_mix_lo(s24, a0, b), fma_mix_lo(s24, a1, b)),
+                      pack_bf16(fma_mix_hi(s24, a0, b), fma_mix_hi(s24, a1, b)), 0u, 0u);
   }
 }
 
@@ -415,42 +415,101 @@ __global__ __launch_bounds__(kThreads) void prefill_segsort_kernel(PrefillArgs a
 
 // ------------------------------------------------------ grouped GEMMs
 //
-// One kernel for both products.  Workgroup tile: 128 rows of one group x 256
-// weight rows -- for gate/up, 128 intermediate columns of gate and the same
-// 128 of up (so h = silu(g) * u is finished in registers); for down, 256
-// output columns.  Four waves, one per SIMD, two workgroups per CU.  Wave w
-// owns 64 weight rows (gate/up: 32 gate + the same 32 up; down: 64 outputs)
-// for all 128 rows: 4 x 2 MFMA 32x32x16 tiles, 128 f32 accumulators.
+// One workgroup = one tile of up to 96 rows of a group x 256 weight rows:
+// for gate/up, 128 intermediate columns of gate and the same 128 of up (so
+// h = silu(g) * u is finished in registers); for down, 256 output columns.
+// Four waves, one per SIMD, two workgroups per CU.  Wave w owns 64 weight
+// rows (gate/up: 32 gate + the same 32 up; down: 64 outputs) for all rows of
+// the tile: up to 3 x 2 MFMA 32x32x16 tiles.
 //
-// Per 64-wide K group (one quantisation group):
-// * A (128 gathered token rows of x, or rows of h) is staged in LDS, double
-//   buffered, from registers loaded two groups ahead;
-// * each lane's B operand for the four MFMA steps is 32 consecutive weights
-//   of one weight row -- 16 packed bytes (int4) -- loaded straight from HBM
-//   two groups ahead and dequantised in registers right before its MFMA
-//   step, so the VALU work of step s+1 overlaps the matrix core on step s.
-//   No weight goes through LDS and no weight is dequantised twice.
+// Every operand reaches LDS by direct-to-LDS loads (global_load_lds: lane i
+// of an instruction writes 16 bytes at the instruction's LDS base + 16 i), so
+// no staging registers and no LDS stores sit in the loop, and each load
+// instruction reads whole row segments (the L1 and address units then see
+// few distinct lines per instruction):
+// * A, per K group (one quantisation group), three-slot ring: the tile's 96
+//   rows (gathered token rows of x, or rows of h), 128 bytes each, 8 rows per
+//   instruction; 16-byte piece p of row r sits in slot p ^ f(r) with
+//   f(r) = (r ^ (r >> 3)) & 7, so the MFMA operand reads (32 rows, one piece
+//   each) hit distinct banks.
+// * B, per 64-byte slice of each weight row (two int4 groups or one int8
+//   group), two-slot ring: 16 rows x 64 bytes per instruction; piece p of row
+//   r in slot p ^ h(r), h(r) = ((r >> 1) ^ (r >> 3)) & 3, again conflict-free
+//   for the operand reads (lane (l, k) reads weights 32k..32k+31 of row l).
+// * (scale, bias) words, 16 bytes (four groups) of every weight row per
+//   instruction, two-slot ring; when K is not a multiple of 256 one word per
+//   row and group instead, three-slot ring.
+// The loads of group g + 2 (int8 weights: g + 1) are in flight while group g
+// computes.  Each lane dequantises its own weights to bf16 (s * q + b, round
+// to nearest even) right before the MFMA step that uses them, overlapping
+// the matrix core's previous step.  No weight is dequantised twice within a
+// tile.
 
 constexpr int kGemmThreads = 256;  // 4 waves
+constexpr int kAStage = BM * 128;  // 12,288 bytes
+
+template <int BITS>
+struct GemmCfg {
+  static constexpr int NQ = BITS == 4 ? 1 : 2;    // 16-byte pieces per lane per column block
+  static constexpr int GPC = BITS == 4 ? 2 : 1;   // K groups per 64-byte weight slice
+  static constexpr int kBOff = 3 * kAStage;       // A ring: 3 x 12,288
+  static constexpr int kBSlot = 4 * 2 * 2048;     // 4 waves x 2 column blocks x 32 rows x 64 B
+  static constexpr int kSbOff = kBOff + 2 * kBSlot;
+  static constexpr int kLds = kSbOff + 2 * 4096;  // 77,824 bytes: two workgroups per CU
+  static constexpr int kAOps = 3, kBOps = 4;      // load instructions per wave per A / B stage
+};
 
 template <int BITS>
 struct BRaw {  // one K group of packed weights for the lane's two weight rows
-  static constexpr int N = BITS == 4 ? 1 : 2;  // 16-byte loads per row
+  static constexpr int N = GemmCfg<BITS>::NQ;
   uint4 q[2][N];
   uint32_t sb[2];
 };
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
-struct ARow {  // one thread's three 16-byte A pieces of one K group (native
-  u32x4_t v0, v1, v2;  // vectors: a copy of HIP's uint4 struct from global
-};                     // memory would stay a memcpy into scratch)
+// Direct-to-LDS loads: lane i's 16 (4) bytes at src go to LDS address
+// m0 + 16 i (4 i).  Issued as plain instructions, they are invisible to the
+// compiler's wait-count bookkeeping; the loop below waits for them itself.
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t m0) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most n of this wave's loads are outstanding (n <= 15)
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: wait_vm_n<0>(); break;
+    case 1: wait_vm_n<1>(); break;
+    case 2: wait_vm_n<2>(); break;
+    case 3: wait_vm_n<3>(); break;
+    case 4: wait_vm_n<4>(); break;
+    case 5: wait_vm_n<5>(); break;
+    case 6: wait_vm_n<6>(); break;
+    case 7: wait_vm_n<7>(); break;
+    case 8: wait_vm_n<8>(); break;
+    case 9: wait_vm_n<9>(); break;
+    case 10: wait_vm_n<10>(); break;
+    case 11: wait_vm_n<11>(); break;
+    case 12: wait_vm_n<12>(); break;
+    default: wait_vm_n<0>(); break;
+  }
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BITS, bool GU>
+template <int BITS, bool GU, bool SB4>
 __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillArgs a,
                                                                        int nt_per_tile) {
-  __shared__ __align__(16) uint8_t As[2][BM * kLdsRow];
+  using C = GemmCfg<BITS>;
   using R = BRaw<BITS>;
+  extern __shared__ __align__(16) uint8_t smem[];
   int tile, nt;
   tile_of_block(nt_per_tile, &tile, &nt);
   if (tile >= *a.n_tiles) return;
@@ -470,80 +529,128 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = lane >> 5, l32 = lane & 31;
-  // gate/up waves whose 32 columns lie past a small intermediate size only
-  // help staging
+  // gate/up waves whose 32 columns lie past a small intermediate size load
+  // (clamped rows) but do not compute
   const bool wave_live = !GU || c0 + 32 * wave < inner;
+  const uint32_t lds0 = lds_addr(smem);
 
-  // A: thread stages 16 bytes (8 values) of rows tid / 8 + 32 i, i < 3, part
-  // tid % 8, so one load instruction covers 8 whole 128-byte row segments.
-  // Rows past the tile read a valid row and only feed accumulator rows that
-  // are never stored.
-  const int apart = tid & 7;
-  const uint16_t* abase = GU ? a.x : a.h;
-  uint32_t aoff[BM / 32];  // element offsets (x: T * H, h: rows * hI, both < 2^31)
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int rl = (tid >> 3) + 32 * i;
-    const int rr = rl < mrows ? rl : 0;
-    aoff[i] = GU ? (uint32_t)a.perm_tok[r0 + rr] * (uint32_t)a.H + apart * 8
-                 : (uint32_t)(r0 + rr) * (uint32_t)a.hI + apart * 8;
-  }
-  const int adst = (tid >> 3) * kLdsRow + apart * 16;
-
-  // B: the lane's weight row in each of its two column blocks, K slice
-  // [32 kh, 32 kh + 32) of every group
-  const uint8_t* bsrc[2];
-  const uint8_t* sbsrc[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    int m, wrow;
-    if (GU) {
-      m = cb;
-      wrow = min(c0 + 32 * wave + l32, inner - 1);  // past inner: never stored
-    } else {
-      m = 2;
-      wrow = c0 + 64 * wave + 32 * cb + l32;
-    }
-    const int64_t qo = m == 0 ? L.q_off[0] : m == 1 ? L.q_off[1] : L.q_off[2];
-    const int64_t so = m == 0 ? L.sb_off[0] : m == 1 ? L.sb_off[1] : L.sb_off[2];
-    bsrc[cb] = blob + qo + (int64_t)wrow * (K * BITS / 8) + kh * (32 * BITS / 8);
-    sbsrc[cb] = blob + so + (int64_t)wrow * (K / 64) * 4;
-  }
-
-  auto load_a = [&](ARow& r, int kg) __attribute__((always_inline)) {
-    const uint16_t* base = abase + kg * KG;
-    r.v0 = *reinterpret_cast<const u32x4_t*>(base + aoff[0]);
-    r.v1 = *reinterpret_cast<const u32x4_t*>(base + aoff[1]);
-    r.v2 = *reinterpret_cast<const u32x4_t*>(base + aoff[2]);
+  // weight row of column block cb, row r (0..31) of this wave
+  auto wrow = [&](int cb, int r) __attribute__((always_inline)) {
+    return GU ? min(c0 + 32 * wave + r, inner - 1) : c0 + 64 * wave + 32 * cb + r;
   };
-  auto store_a = [&](const ARow& r, int buf) __attribute__((always_inline)) {
-    uint8_t* d = &As[buf][adst];
-    *reinterpret_cast<u32x4_t*>(d) = r.v0;
-    *reinterpret_cast<u32x4_t*>(d + 32 * kLdsRow) = r.v1;
-    *reinterpret_cast<u32x4_t*>(d + 64 * kLdsRow) = r.v2;
+  auto qsec = [&](int cb) __attribute__((always_inline)) -> int64_t {
+    const int m = GU ? cb : 2;
+    return m == 0 ? L.q_off[0] : m == 1 ? L.q_off[1] : L.q_off[2];
   };
-  auto load_b = [&](R& r, int kg) __attribute__((always_inline)) {
+  auto sbsec = [&](int cb) __attribute__((always_inline)) -> int64_t {
+    const int m = GU ? cb : 2;
+    return m == 0 ? L.sb_off[0] : m == 1 ? L.sb_off[1] : L.sb_off[2];
+  };
+
+  // A loads: wave w fills 8-row chunks w, w + 4, w + 8; lane l takes row
+  // 8c + l / 8 and stores slot l % 8, i.e. global piece (l % 8) ^ f(row).
+  // Rows past the tile read the tile's first row and feed only accumulator
+  // rows that are never stored.
+  const uint8_t* asrc[3];
+  {
+    const uint16_t* abase = GU ? a.x : a.h;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-#pragma unroll
-      for (int i = 0; i < R::N; ++i) r.q[cb][i] = ld16(bsrc[cb] + kg * (KG * BITS / 8) + 16 * i);
-      r.sb[cb] = ldu32(sbsrc[cb] + kg * 4);
+    for (int i = 0; i < 3; ++i) {
+      const int rl = 8 * (wave + 4 * i) + (lane >> 3);
+      const int rr = rl < mrows ? rl : 0;
+      const int piece = (lane & 7) ^ ((rl ^ (rl >> 3)) & 7);
+      const int64_t row = GU ? (int64_t)a.perm_tok[r0 + rr] * a.H : (int64_t)(r0 + rr) * a.hI;
+      asrc[i] = reinterpret_cast<const uint8_t*>(abase + row + piece * 8);
     }
+  }
+  // B loads: instruction i of column block cb covers rows 16i .. 16i + 15;
+  // lane l takes row 16i + l / 4, slot l % 4 = global piece (l % 4) ^ h(row)
+  // of the row's 64-byte slice.  A slice of an odd last int4 group reads 32
+  // bytes past the row: the next row, or the next section of the blob.
+  const uint8_t* bsrc[2][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      const int piece = (lane & 3) ^ (((r >> 1) ^ (r >> 3)) & 3);
+      bsrc[cb][i] = blob + qsec(cb) + (int64_t)wrow(cb, r) * (K * BITS / 8) + piece * 16;
+    }
+  // (scale, bias) words: lane l loads those of column block l / 32, row l % 32
+  const uint8_t* sbsrc = blob + sbsec(kh) + (int64_t)wrow(kh, l32) * NK * 4;
+
+  const uint32_t ldsA = lds0, ldsB = lds0 + C::kBOff, ldsS = lds0 + C::kSbOff;
+  auto issue_a = [&](int kg) __attribute__((always_inline)) {
+    const uint32_t st = ldsA + (kg % 3) * kAStage;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dma16(asrc[i] + kg * (KG * 2), st + (wave + 4 * i) * 1024);
+  };
+  auto issue_b = [&](int c) __attribute__((always_inline)) {  // 64-byte slice c
+    const uint32_t st = ldsB + (c & 1) * C::kBSlot + wave * 4096;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16(bsrc[cb][i] + c * 64, st + cb * 2048 + i * 1024);
+  };
+  auto issue_sb = [&](int d) __attribute__((always_inline)) {  // SB4: groups 4d..4d+3; else group d
+    if (SB4)
+      dma16(sbsrc + d * 16, ldsS + (d & 1) * 4096 + wave * 1024);
+    else
+      dma4(sbsrc + d * 4, ldsS + (d % 3) * 1024 + wave * 256);
+  };
+
+  // A operand rows: row rb * 32 + l32, piece kh * 4 + s at slot
+  // (kh * 4 + s) ^ f(row) = ax[rb] ^ s
+  int ax[3];
+#pragma unroll
+  for (int rb = 0; rb < 3; ++rb) {
+    const int r = rb * 32 + l32;
+    ax[rb] = (kh * 4) ^ ((r ^ (r >> 3)) & 7);
+  }
+  const int bh = ((l32 >> 1) ^ (l32 >> 3)) & 3;  // h(l32)
+  auto a_frag = [&](const uint8_t* st, int rb, int s) __attribute__((always_inline)) -> uint4 {
+    return *reinterpret_cast<const uint4*>(st + (rb * 32 + l32) * 128 + ((ax[rb] ^ s) << 4));
   };
   // bf16 B operand of MFMA step s for column block cb: weights 8s..8s+7 of
   // the lane's 32
   auto b_operand = [&](const R& r, int cb, int s) __attribute__((always_inline)) -> uint4 {
     const float sc = bf16_lo(r.sb[cb]), bi = bf16_hi(r.sb[cb]);
+    const float s24 = sc * 16777216.0f, s20 = sc * 1048576.0f;
     if (BITS == 4) {
       const uint4 q = r.q[cb][0];
       const uint32_t w = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
-      return dequant_word<4>(w, sc, bi);
+      return dequant_word<4>(w, s24, s20, bi);
     } else {
       const uint4 q = r.q[cb][s >> 1];
       const uint32_t w0 = (s & 1) ? q.z : q.x, w1 = (s & 1) ? q.w : q.y;
-      const uint4 lo = dequant_word<8>(w0, sc, bi), hi = dequant_word<8>(w1, sc, bi);
+      const uint4 lo = dequant_word<8>(w0, s24, s20, bi), hi = dequant_word<8>(w1, s24, s20, bi);
       return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
+  };
+  // the lane's packed weights and (scale, bias) words of group kg, from LDS
+  auto read_b = [&](int kg) __attribute__((always_inline)) -> R {
+    R r;
+    const int c = kg / C::GPC;
+    const uint8_t* bs = smem + C::kBOff + (c & 1) * C::kBSlot + wave * 4096 + l32 * 64;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < C::NQ; ++i) {
+        const int piece = BITS == 4 ? ((kg & 1) << 1) | kh : 2 * kh + i;
+        r.q[cb][i] = *reinterpret_cast<const uint4*>(bs + cb * 2048 + ((piece ^ bh) << 4));
+      }
+    if (SB4) {
+      const uint8_t* ss = smem + C::kSbOff + ((kg >> 2) & 1) * 4096 + wave * 1024 + (kg & 3) * 4;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        r.sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 16);
+    } else {
+      const uint8_t* ss = smem + C::kSbOff + (kg % 3) * 1024 + wave * 256;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        r.sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 4);
+    }
+    return r;
   };
 
   f32x16_t acc[BM / 32][2];
@@ -552,42 +659,53 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  // one K group on A stage `buf` with packed weights `r`.  MFMA step s runs
-  // on operands prepared during step s-1 (A fragments read from LDS, B
+  // One K group, operands from the LDS rings.  MFMA step s runs on
+  // operands prepared during step s-1 (A fragments read from LDS, B
   // dequantised in registers); the scheduler is told to interleave each of
   // the step's MFMAs with a share of the next step's dequantisation, so the
-  // VALU works while the matrix core does.  NRB (row blocks with any live
-  // row) is a compile-time count.
-  auto compute = [&](auto nrb_c, int buf, const R& r) __attribute__((always_inline)) {
+  // VALU works while the matrix core does.  During the last step the lane
+  // reads the next group's packed weights (its own loads: a wait on its own
+  // counter, no barrier) and dequantises their step 0, so every step has
+  // VALU work and no group starts with an idle matrix core.  r / b0: the
+  // group's packed weights and step-0 operands on entry, the next group's on
+  // exit.  NRB (row blocks with any live row) is a compile-time count.
+  auto compute = [&](auto nrb_c, int kg, R& r, uint4* b0, int next_wait)
+                     __attribute__((always_inline)) {
     constexpr int NRB = decltype(nrb_c)::value;
-    if (!wave_live) return;
-    const uint8_t* st = As[buf];
+    const uint8_t* st = smem + (kg % 3) * kAStage;
     uint4 af[2][NRB], bo[2][2];
-    bo[0][0] = b_operand(r, 0, 0);
-    bo[0][1] = b_operand(r, 1, 0);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      af[0][rb] = *reinterpret_cast<const uint4*>(st + (rb * 32 + l32) * kLdsRow + kh * 64);
+    for (int rb = 0; rb < NRB; ++rb) af[0][rb] = a_frag(st, rb, 0);
+    bo[0][0] = b0[0];
+    bo[0][1] = b0[1];
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const int cur = s4 & 1, nxt = cur ^ 1;
+      if (s4 == 3 && next_wait >= 0 && next_wait < 16) wait_vm(next_wait);
       __builtin_amdgcn_sched_barrier(0);
       if (s4 < 3) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          af[nxt][rb] = *reinterpret_cast<const uint4*>(st + (rb * 32 + l32) * kLdsRow + kh * 64 +
-                                                        (s4 + 1) * 16);
+        for (int rb = 0; rb < NRB; ++rb) af[nxt][rb] = a_frag(st, rb, s4 + 1);
       }
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         acc[rb][0] = mfma(af[cur][rb], bo[cur][0], acc[rb][0]);
         acc[rb][1] = mfma(af[cur][rb], bo[cur][1], acc[rb][1]);
       }
-      if (s4 < 3) {
-        bo[nxt][0] = b_operand(r, 0, s4 + 1);
-        bo[nxt][1] = b_operand(r, 1, s4 + 1);
+      if (s4 < 3 || next_wait >= 0) {
+        if (s4 < 3) {
+          bo[nxt][0] = b_operand(r, 0, s4 + 1);
+          bo[nxt][1] = b_operand(r, 1, s4 + 1);
+        } else {
+          r = read_b(kg + 1);
+          b0[0] = b_operand(r, 0, 0);
+          b0[1] = b_operand(r, 1, 0);
+        }
         // LDS reads first, then one MFMA per share of the dequant VALU ops
-        __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+        if (s4 < 3)
+          __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NQ + 2, 0);
 #pragma unroll
         for (int i = 0; i < 2 * NRB; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -598,45 +716,68 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // the K pipeline for a compile-time row-block count.  Loads run two K
-  // groups ahead: group kg+2's A and B are requested before group kg+1's A
-  // (already in registers) is staged, so in-order completion never makes the
-  // staging wait for the newest requests.
+  // The K pipeline.  Group kg issues, right after the barrier that opens it
+  // (every wave has finished the previous group, so the ring slots being
+  // refilled are free): its B slice if kg starts a slice (the next slice),
+  // A of group kg + 2, and the (scale, bias) words ahead.  Before the
+  // barrier each wave waits until its own loads that group kg needs have
+  // landed: all but the ones issued during group kg - 1 (int8 weights: all
+  // but group kg - 1's A and (scale, bias) loads); group kg's packed
+  // weights and (scale, bias) words were already read during group kg - 1,
+  // after a wait for the wave's own loads issued since that slice.
   auto run = [&](auto nrb_c) __attribute__((always_inline)) {
-    ARow a0, a1;
-    R bq0, bq1;
-    load_a(a0, 0);
-    load_b(bq0, 0);
-    if (NK > 1) {
-      load_a(a1, 1);
-      load_b(bq1, 1);
-    }
-    store_a(a0, 0);
-    __syncthreads();
-    int kg = 0;
-    for (; kg + 2 < NK; kg += 2) {
-      // group kg on stage 0; a1 holds A of kg+1
-      compute(nrb_c, 0, bq0);
-      load_a(a0, kg + 2);
-      load_b(bq0, kg + 2);
-      store_a(a1, 1);
-      __syncthreads();
-      // group kg+1 on stage 1; a0 holds A of kg+2
-      compute(nrb_c, 1, bq1);
-      if (kg + 3 < NK) {
-        load_a(a1, kg + 3);
-        load_b(bq1, kg + 3);
+    constexpr int SBG = SB4 ? 4 : 1;  // groups per (scale, bias) load
+    const int nslice = (NK + C::GPC - 1) / C::GPC;
+    const int nsb = (NK + SBG - 1) / SBG;
+    issue_b(0);
+    issue_a(0);
+    issue_sb(0);
+    if (NK > 1) issue_a(1);
+    if (!SB4 && NK > 1) issue_sb(1);
+    int younger = 0;  // loads issued during the previous group that group kg may skip
+    int since_b = 0;  // loads issued after the most recent B slice
+    R r;
+    uint4 b0[2];
+    for (int kg = 0; kg < NK; ++kg) {
+      wait_vm(younger);
+      barrier();
+      int nb = 0, na = 0, ns = 0;
+      if (kg % C::GPC == 0 && kg / C::GPC + 1 < nslice) {
+        issue_b(kg / C::GPC + 1);
+        nb = C::kBOps;
+        since_b = 0;
       }
-      store_a(a0, 0);
-      __syncthreads();
-    }
-    if (kg < NK) {  // one or two groups left: kg (stage 0) and maybe kg + 1 (a1)
-      compute(nrb_c, 0, bq0);
+      if (kg + 2 < NK) {
+        issue_a(kg + 2);
+        na = C::kAOps;
+      }
+      if (SB4) {
+        if (kg % 4 == 0 && kg / 4 + 1 < nsb) {
+          issue_sb(kg / 4 + 1);
+          ns = 1;
+        }
+      } else if (kg + 2 < NK) {
+        issue_sb(kg + 2);
+        ns = 1;
+      }
+      since_b += na + ns;
+      // group kg + 1 needs this group's B slice when a slice is one group
+      younger = C::GPC == 1 ? na + ns : nb + na + ns;
+      if (kg == 0) {  // nothing carried in: the first group reads its own weights
+        r = read_b(0);
+        b0[0] = b_operand(r, 0, 0);
+        b0[1] = b_operand(r, 1, 0);
+      }
+      // wait before reading group kg + 1's weights: for its B slice when
+      // kg + 1 starts one (the newest slice; else it is this group's,
+      // complete), for its (scale, bias) word when one is loaded per group
+      // (issued during group kg - 1, before everything issued during kg)
+      int next_wait = -1;  // -1: no next group; 16: read without waiting
       if (kg + 1 < NK) {
-        store_a(a1, 1);
-        __syncthreads();
-        compute(nrb_c, 1, bq1);
+        next_wait = (kg + 1) % C::GPC == 0 ? since_b : 16;
+        if (!SB4) next_wait = min(next_wait, nb + na + ns);
       }
+      if (wave_live) compute(nrb_c, kg, r, b0, next_wait);
     }
   };
   static_assert(BM == 96, "row-block dispatch below");
@@ -759,13 +900,24 @@ hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BITS, bool GU>
-hipError_t launch_grouped(const PrefillArgs& a, hipStream_t s) {
+template <int BITS, bool GU, bool SB4>
+hipError_t launch_grouped_sb(const PrefillArgs& a, hipStream_t s) {
   const int nt = GU ? (std::max(a.I, a.Is) + 127) / 128 : a.H / 256;
   const int tiles8 = pad8(a.max_tiles);  // every XCD gets tiles8 / 8 tiles x nt blocks
-  hipLaunchKernelGGL((grouped_gemm_kernel<BITS, GU>), dim3(tiles8 * nt), dim3(kGemmThreads), 0,
-                     s, a, nt);
+  const size_t lds = GemmCfg<BITS>::kLds;
+  hipError_t e = allow_lds(grouped_gemm_kernel<BITS, GU, SB4>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((grouped_gemm_kernel<BITS, GU, SB4>), dim3(tiles8 * nt), dim3(kGemmThreads),
+                     lds, s, a, nt);
   return hipGetLastError();
+}
+
+// (scale, bias) words four groups at a time when every K of the launch is a
+// multiple of 256
+template <int BITS, bool GU>
+hipError_t launch_grouped(const PrefillArgs& a, hipStream_t s) {
+  const bool sb4 = GU ? a.H % 256 == 0 : a.I % 256 == 0 && a.Is % 256 == 0;
+  return sb4 ? launch_grouped_sb<BITS, GU, true>(a, s) : launch_grouped_sb<BITS, GU, false>(a, s);
 }
 
 hipError_t launch_prefill_gu(const PrefillArgs& a, hipStream_t s) {
