@@ -61,6 +61,44 @@ def test_dequant_bit_exact(torch, name, H, I):
         assert np.array_equal(b16.cpu().numpy().view(np.uint16), O.bf16_bits(O.round_bf16(W)))
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_dequant_rounding_wide_ranges(torch, bits):
+    """s * q + b over scales and biases whose exponents differ by up to 30
+    binades (either sign, some zero biases): the f32 result must be the exact
+    value rounded once to float32 (the exact value is a float64 here: at
+    most 16 + 8 significant bits over a span of under 53), the bf16 result
+    that f32 value rounded to nearest even."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd.weights import upload_blob
+    H, I = 256, 128
+    _print("dequant wide ranges", bits)
+    rng = np.random.default_rng(77)
+
+    def bf16_of(x):
+        return O.bf16_bits(O.round_bf16(np.asarray(x, np.float64)))
+
+    arr = {}
+    for mat, (rows, cols) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        words = rng.integers(0, 2**32, size=(rows, cols * bits // 32), dtype=np.uint64).astype(np.uint32)
+        g = cols // 64
+        s = np.ldexp(rng.uniform(1, 2, (rows, g)), rng.integers(-20, 11, (rows, g)))
+        s *= rng.choice([-1.0, 1.0], (rows, g))
+        b = s * np.ldexp(rng.uniform(1, 2, (rows, g)), rng.integers(-30, 31, (rows, g)))
+        b *= rng.choice([-1.0, 1.0], (rows, g))
+        b[rng.random((rows, g)) < 0.05] = 0.0
+        arr[mat] = (words, bf16_of(s), bf16_of(b))
+    blob = upload_blob(H, I, bits, arr)
+    for which, mat in enumerate(("gate", "up", "down")):
+        f32, b16 = m.moe_dequant(blob, H, I, bits, which)
+        torch.cuda.synchronize()
+        W = O.dequantize(*arr[mat], bits=bits, group=64)
+        want32 = W.astype(np.float32)
+        got32 = f32.cpu().numpy()
+        assert np.array_equal(got32.view(np.uint32), want32.view(np.uint32))
+        assert np.array_equal(b16.cpu().numpy().view(np.uint16),
+                              O.bf16_bits(O.round_bf16(want32.astype(np.float64))))
+
+
 # ------------------------------------------------------------------ router
 
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 8), ("decode35b", 1), ("decode35b", 8),
