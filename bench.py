@@ -36,8 +36,14 @@ HBM_PEAK_GBS = 8000.0
 # stack (profiles/decode35b_stack_decode_kernel.md), per launch, with the
 # factors that map a plain copy's counter readings onto its byte count.
 STACK_TRAFFIC = {
-    "decode35b": {"fetch_kib": 361948, "write_kib": 53786,
+    "decode35b": {"fetch_kib": 362065, "write_kib": 53786,
                   "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
+}
+# The same for the gate/up grouped GEMM of the 4096-token prefill layer
+# (profiles/prefill80b_grouped_gemm.md).
+PREFILL_TRAFFIC = {
+    "prefill80b": {"fetch_kib": 615322, "write_kib": 45056,
+                   "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
 }
 
 
@@ -455,6 +461,10 @@ def bench_prefill(args, cfg):
     for t in timers.values():
         m.moe_timer_destroy(t)
     gu_flops, dn_flops = prefill_flops(cfg, T)
+    traffic = None
+    if cfg.name in PREFILL_TRAFFIC and T == cfg.tokens:
+        t = PREFILL_TRAFFIC[cfg.name]
+        traffic = (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
     achieved = gu_flops / (ms["gate_up"] / 1e3) / 1e12
     both = (gu_flops + dn_flops) / ((ms["gate_up"] + ms["down"]) / 1e3) / 1e12
     tok_s = T * steps / t_all
@@ -475,9 +485,10 @@ def bench_prefill(args, cfg):
                    "gate_up_plus_down_TFLOPs": both,
                    "gate_up_plus_down_frac_of_bf16_peak": both / 2500.0,
                    "down_mean_us": ms["down"] * 1e3, "router_mean_us": ms["route"] * 1e3},
-        "roofline": {"kernel": "gu_gemm_kernel (grouped gate/up GEMM, dequant-to-bf16, MFMA)",
+        "roofline": {"kernel": "grouped_gemm_kernel<4, true, true> (grouped gate/up GEMM, "
+                               "dequant-to-bf16, MFMA)",
                      "bound": "mfma", "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": achieved / 2500.0, "traffic": None,
+                     "frac": achieved / 2500.0, "traffic": traffic,
                      "flops_per_launch": gu_flops, "mean_launch_us": ms["gate_up"] * 1e3},
         "cpu_baseline": cpu,
     }
