@@ -443,6 +443,52 @@ def test_prefill_reduced_experts(torch, name, T):
     dm.destroy()
 
 
+def test_prefill_shared_inter_differs(torch):
+    """Shared intermediate 64 != routed 128 (the shared group's down has one
+    K group and loads its (scale, bias) words one group at a time)."""
+    cfg = CONFIGS["tiny"].replace(inter=128, shared_inter=64, experts=32, top_k=4)
+    dm, *_ = _prefill_case(torch, cfg, 40)
+    dm.destroy()
+
+
+def test_prefill_int8_small_inter(torch):
+    """int8 weights with K = 128 for down (not a multiple of 256)."""
+    cfg = CONFIGS["decode80b_int8"].replace(layers=1, hidden=256, experts=32, top_k=4,
+                                            inter=128, shared_inter=128)
+    dm, *_ = _prefill_case(torch, cfg, 50)
+    dm.destroy()
+
+
+def test_prefill_pool_matches_resident_bitwise(torch):
+    """Many tokens with experts served from the slot pool (all misses, then
+    all hits) give exactly the resident result."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=1, experts=64, top_k=4)
+    _print("prefill pool", cfg.name)
+    dm = DeviceModel(cfg, layers=1)
+    store, _ = Wt.fill_store(dims_of(cfg), 1, lambda l, e: expert_arrays(cfg, l, e))
+    pool = m.slotpool_create(store, cfg.experts, 0)
+    try:
+        L_res = dm.make_layers()[0]
+        L_pool = dm.make_layers(pool=pool)[0]
+        xb = tokens_x(cfg, 0, 96)
+        want = _prefill_run(torch, m, L_res, cfg, xb)
+        for rnd in range(2):  # first call misses, second hits
+            got = _prefill_run(torch, m, L_pool, cfg, xb)
+            assert np.array_equal(got[0], want[0])
+            assert np.array_equal(got[1].view(np.uint32), want[1].view(np.uint32))
+            assert np.array_equal(got[2], want[2])
+            assert np.array_equal(got[3].view(np.uint32), want[3].view(np.uint32))
+        stats = m.slotpool_get_stats(pool)
+        assert stats["misses"] > 0 and stats["hits"] > 0, stats
+    finally:
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
 def test_prefill_token_permutation_is_bitwise(torch):
     import int4_group_quantized_router_amd as m
     cfg = CONFIGS["prefill80b"].replace(layers=1, experts=64, top_k=4)
