@@ -28,6 +28,11 @@ struct RouteArgs {
   int32_t* slot_expert;   // [T*k]
   int8_t* jmap;           // [T*k][kJmapStride]: j of token t in slot s, or -1
   int32_t* counts;        // [E] per-expert selection counts (atomic adds), or NULL
+  // host-visible copy of the distinct-expert list (pinned memory, or NULL):
+  // [1] = count, [2 + s] = expert of slot s, then [0] = host_epoch, stored
+  // last with system-scope release so the host may read [1..] once it sees it
+  int32_t* host_list;
+  int32_t host_epoch;
   // top-k over MFMA partial sums (launch_topk_only): logits = sum of
   // part[0..ksplit) in order + rb, written to `logits` when that is not
   // NULL; the shared gate is then sigmoid(x . wsg) computed per token here

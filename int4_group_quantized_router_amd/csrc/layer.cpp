@@ -8,6 +8,8 @@
 // pool filled from a host store.
 #include <algorithm>
 #include <cstring>
+#include <atomic>
+#include <chrono>
 #include <vector>
 
 #include "common.h"
@@ -36,8 +38,11 @@ struct moe_layer {
   uint16_t* h;
   float* y;
   int hI;
-  // pool path: pinned host mirror of `slots`, and the slot-pointer table
+  // pool path: pinned host copy of the distinct-expert list written by the
+  // router kernel ([0] call epoch, [1] count, [2..] experts), the call
+  // epoch, and the slot-pointer table
   int32_t* host_slots;
+  int32_t list_epoch;
   const uint8_t** host_ptrs;   // pinned [kMaxSlots]
   const uint8_t** dev_ptrs;    // device [kMaxSlots]
   // many-token path: workspace allocated on first use, grown with T
@@ -154,6 +159,10 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
   r.n_slots = L->slots;
   r.slot_expert = L->slots + 1;
   r.jmap = L->jmap;
+  if (L->pool) {
+    r.host_list = L->host_slots;
+    r.host_epoch = L->list_epoch = L->list_epoch == 0x7fffffff ? 1 : L->list_epoch + 1;
+  }
   timer_mark(MOE_KERNEL_ROUTE, true, stream);
   MOE_HIP_TRY(launch_route(r, stream));
   timer_mark(MOE_KERNEL_ROUTE, false, stream);
@@ -184,13 +193,31 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
 
   std::vector<int32_t> experts;
   if (L->pool) {
-    // The chosen experts are needed on the host to run the pool policy.
-    MOE_HIP_TRY(hipMemcpyAsync(L->host_slots, L->slots, sizeof(int32_t) * (1 + T * c.top_k),
-                               hipMemcpyDeviceToHost, stream));
-    MOE_HIP_TRY(hipStreamSynchronize(stream));
-    const int n = L->host_slots[0];
+    // The chosen experts are needed on the host to run the pool policy: the
+    // router kernel writes them to pinned memory and then the call's epoch;
+    // the host waits for the epoch (no stream synchronisation: the router
+    // has not finished when the list is complete).  Everything enqueued
+    // before the router, including the previous call's pointer upload, has
+    // run by then, so host_ptrs may be rewritten below.
+    const int32_t want = L->list_epoch;
+    const auto t_start = std::chrono::steady_clock::now();
+    volatile int32_t* flag = L->host_slots;
+    int spins = 0;
+    while (*flag != want) {
+      if (++spins % 1024 == 0) {
+        const hipError_t q = hipStreamQuery(stream);
+        if (q != hipSuccess && q != hipErrorNotReady)
+          return fail(MOE_E_HIP, "router failed: %s", hipGetErrorString(q));
+        if (q == hipSuccess && *flag != want)
+          return fail(MOE_E_HIP, "router finished without publishing its expert list");
+        if (std::chrono::steady_clock::now() - t_start > std::chrono::seconds(10))
+          return fail(MOE_E_HIP, "timed out waiting for the router's expert list");
+      }
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
+    const int n = L->host_slots[1];
     if (n < 0 || n > T * c.top_k) return fail(MOE_E_HIP, "router produced %d slots", n);
-    experts.assign(L->host_slots + 1, L->host_slots + 1 + n);
+    experts.assign(L->host_slots + 2, L->host_slots + 2 + n);
     const void* ptrs[kMaxSlots];
     int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, nullptr);
     if (st != MOE_OK) return st;
@@ -660,9 +687,12 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
   L->y = static_cast<float*>(parts[9]);
   L->dev_ptrs = static_cast<const uint8_t**>(parts[10]);
   he = hipMemset(L->ws, 0, total);
-  if (he == hipSuccess && pool)
-    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (1 + T * k) * sizeof(int32_t),
+  if (he == hipSuccess && pool) {
+    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (2 + T * k) * sizeof(int32_t),
                        hipHostMallocDefault);
+    if (he == hipSuccess) std::memset(L->host_slots, 0, (2 + T * k) * sizeof(int32_t));
+    L->list_epoch = 0;  // the first call publishes epoch 1
+  }
   if (he == hipSuccess && pool)
     he = hipHostMalloc(reinterpret_cast<void**>(&L->host_ptrs), kMaxSlots * sizeof(void*),
                        hipHostMallocDefault);

@@ -172,14 +172,28 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
       if (p < n) s_slot[p] = first ? base + __popcll(b & ((1ull << lane) - 1ull)) : -1;
       base += __popcll(b);
     }
-    if (lane == 0) *a.n_slots = base;
+    if (lane == 0) {
+      *a.n_slots = base;
+      if (a.host_list) a.host_list[1] = base;
+    }
   }
   __syncthreads();
   for (int p = threadIdx.x; p < n; p += kThreads) {
     const int e = s_sel[p];
     const int slot = s_slot[s_first[e]];
     a.jmap[slot * kJmapStride + p / k] = (int8_t)(p % k);
-    if (s_first[e] == p) a.slot_expert[slot] = e;
+    if (s_first[e] == p) {
+      a.slot_expert[slot] = e;
+      if (a.host_list) a.host_list[2 + slot] = e;
+    }
+  }
+  if (a.host_list) {
+    // the host polls word 0: everything above is visible before it changes
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __threadfence_system();
+      __hip_atomic_store(a.host_list, a.host_epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
