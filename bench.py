@@ -31,6 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Measured on one MI355X with `bench.py --calibrate-peaks`: a 1 GiB device
+# copy (read + write) and an 8192^3 bf16 torch.mm through the vendor BLAS.
+MEASURED_COPY_GBS = 5105.0
+MEASURED_BF16_MM_TFLOPS = 1213.0
 
 # HBM counters of the persistent stack kernel on the 40-layer 35B-shaped
 # stack (profiles/decode35b_stack_decode_kernel.md), per launch, with the
@@ -141,6 +145,42 @@ def calibrate_copy(nbytes):
                       "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
 
 
+def calibrate_peaks():
+    """Measured ceilings on this GPU: a plain device copy (read + write GB/s)
+    and a large bf16 matrix product from the vendor BLAS (TFLOP/s), the
+    references the roofline fractions can also be read against."""
+    import torch
+    torch.cuda.set_device(0)
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 20 / (time.perf_counter() - t0) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.mm(x, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        torch.mm(x, y)
+    torch.cuda.synchronize()
+    tflops = 2 * m ** 3 * reps / (time.perf_counter() - t0) / 1e12
+    print(json.dumps({"copy_GBps_read_plus_write": copy_gbs, "copy_bytes": n,
+                      "bf16_mm_TFLOPs": tflops, "mm_shape": [m, m, m],
+                      "vendor_peaks": {"hbm_GBps": HBM_PEAK_GBS, "bf16_TFLOPs": 2500.0}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +194,8 @@ def main():
                     help="stream80b / decode80b_int8: build only this many layers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 10 device-to-device copies of BYTES (reference for HBM counters)")
+    ap.add_argument("--calibrate-peaks", action="store_true",
+                    help="only measure a 1 GiB device copy and an 8192^3 bf16 matmul")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
@@ -164,6 +206,8 @@ def main():
     import torch
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
+    if args.calibrate_peaks:
+        return calibrate_peaks()
     import int4_group_quantized_router_amd as m
     from int4_group_quantized_router_amd import weights as W
     from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
@@ -272,6 +316,7 @@ def main():
             "bytes_per_token": per_token_bytes,
             "stack_GBps": per_token_bytes * tok_s / 1e9,
             "stack_frac_of_hbm_peak": per_token_bytes * tok_s / 1e9 / HBM_PEAK_GBS,
+            "stack_frac_of_measured_copy": per_token_bytes * tok_s / 1e9 / MEASURED_COPY_GBS,
             "layer_tokens_per_s": tok_s * cfg.layers,
         },
         "roofline": {
@@ -484,6 +529,7 @@ def bench_prefill(args, cfg):
                    "gemm_flops_per_call": gu_flops + dn_flops,
                    "gate_up_plus_down_TFLOPs": both,
                    "gate_up_plus_down_frac_of_bf16_peak": both / 2500.0,
+                   "gate_up_plus_down_frac_of_measured_bf16_mm": both / MEASURED_BF16_MM_TFLOPS,
                    "down_mean_us": ms["down"] * 1e3, "router_mean_us": ms["route"] * 1e3},
         "roofline": {"kernel": "grouped_gemm_kernel<4, true, true> (grouped gate/up GEMM, "
                                "dequant-to-bf16, MFMA)",
