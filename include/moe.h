@@ -122,7 +122,15 @@ int32_t moe_blob_pack(const moe_qshape* shape, const moe_qmatrix_host* gate,
  * idx: device int32 [T, k]; w: device f32 [T, k]; sigma: device f32 [T] or
  * NULL; logits: device f32 [T, E], required -- written, and used as the
  * kernels' scratch.  MOE_E_INVAL if k < 1, k > E, k > MOE_MAX_TOPK,
- * E > 1024, H not a positive multiple of 256, or T < 0 (T = 0 is a no-op).
+ * E > 1024, H not a positive multiple of 256 up to 4096, or T < 0 (T = 0
+ * is a no-op).
+ *
+ * T <= 8: one fused launch (f32 GEMV; the last workgroup runs the top-k).
+ * T > 8: the logits come from bf16 MFMA on Wr split exactly into three bf16
+ * planes (hi + mid + lo == Wr, so every product is exact in f32), with K cut
+ * into up to 4 slices whose partial sums the top-k adds in slice order, then
+ * rb; sigma is then x . wsg in f32 per token.  The planes and partial sums
+ * live in stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`).
  * ---------------------------------------------------------------------- */
 int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
                        const float* rb, int32_t E, int32_t k, const float* wsg,

@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   if (a.n_slots) build_slots(a, s_sel, s_first, s_slot);
 }
 
-// Top-k alone over logits written by an earlier launch: 4 tokens per block.
+// Top-k over logits written by an earlier launch (or formed here from the
+// MFMA router's partial sums), 4 tokens per block.
 template <int VPL>
 __global__ __launch_bounds__(kThreads) void topk_kernel(RouteArgs a) {
   __shared__ int s_sel[kWaves * MOE_MAX_TOPK];
