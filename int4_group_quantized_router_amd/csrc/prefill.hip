@@ -10,19 +10,20 @@
 //      hi + mid + lo == Wr exactly (8 + 8 + 8 significant bits), so bf16
 //      MFMA with f32 accumulation computes exactly the products of the f32
 //      router; each 64-wide K group is accumulated separately and then added
-//      to the running total, which bounds the summation depth.
+//      to the running total, which bounds the summation depth.  K is split
+//      into up to 4 slices (enough workgroups for the chip); the top-k adds
+//      the slices' partial sums in order, then rb.
 //   2. sort: per-chunk expert histograms (LDS), one scan to row offsets, chunk
 //      offsets and a tile list, a scatter at LDS cursors, then a per-expert
 //      sort of each expert's pairs, so rows keep (token, choice) order.  The
 //      shared expert is one more group whose rows are all tokens.
-//   3. gate/up grouped GEMM: one 128-row tile of an expert's rows x 64
-//      intermediate columns of BOTH gate and up per workgroup; the 128 x 64
-//      weight tile of each K group (one quantisation group) is dequantised
-//      once by the workgroup into LDS as bf16 (s*q + b, then round to nearest
-//      even) and read by four waves as MFMA 32x32x16 operands; token rows are
-//      gathered straight from x in HBM; epilogue h = bf16(silu(g) * u).
-//   4. down grouped GEMM: 128 rows x 128 output columns, same scheme; f32
-//      outputs per (token, choice) row.
+//   3. gate/up grouped GEMM: a tile of up to 96 rows of one group x 128
+//      intermediate columns of BOTH gate and up per workgroup; operands reach
+//      LDS by direct-to-LDS loads; each lane dequantises its own MFMA B
+//      operands (s*q + b in f32, then round to nearest even); epilogue
+//      h = bf16(silu(g) * u).
+//   4. down grouped GEMM: up to 96 rows x 256 output columns, same scheme;
+//      f32 outputs per (token, choice) row.
 //   5. combine: y[t] = sum_j w[t,j] y_j + sigma_t y_shared, j in order.
 //
 // MFMA K order: for MFMA step s of a 64-wide group, lanes 0-31 supply
@@ -31,8 +32,8 @@
 // the same order, so the product is unchanged.
 //
 // Blocks are numbered so that consecutive work items land on the same XCD
-// (the dispatcher deals blocks round-robin over the 8 XCDs): the 16 or 8
-// column tiles of one row tile then share its rows in that XCD's L2.
+// (the dispatcher deals blocks round-robin over the 8 XCDs): the column
+// tiles of one row tile then share its rows in that XCD's L2.
 #include <algorithm>
 #include <type_traits>
 
