@@ -127,6 +127,32 @@ def test_route_topk(torch, name, T):
     assert decided >= 0.9 * 2 * T
 
 
+@pytest.mark.parametrize("T", [1, 8, 300])
+def test_route_max_sizes(torch, T):
+    """The router at its largest supported shape: E = 1024, k = 16, H = 4096
+    (GEMV path for T <= 8; MFMA path with split K above)."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["stream80b"].replace(hidden=4096, experts=1024, top_k=16)
+    _print("route max", T)
+    Wr, rb, wsg = router_arrays(cfg, 0)
+    xb = tokens_x(cfg, 0, T)
+    out = m.moe_route_topk(torch.from_numpy(xb.view(np.int16)).cuda(),
+                           torch.from_numpy(Wr).cuda(), torch.from_numpy(rb).cuda(),
+                           cfg.top_k, wsg=torch.from_numpy(wsg).cuda())
+    torch.cuda.synchronize()
+    idx, w = out["idx"].cpu().numpy(), out["w"].cpu().numpy()
+    lg, sg = out["logits"].cpu().numpy(), out["sigma"].cpu().numpy()
+    depth = mfma_depth(cfg.hidden) if T > 8 else None
+    decided = 0
+    for t in range(T):
+        x = O.bf16_to_f64(xb[t])
+        decided += check_routing(idx[t], lg[t], x, Wr, rb, cfg.top_k, w[t], depth=depth)
+        assert abs(sg[t] - O.sigmoid(np.dot(wsg.astype(np.float64), x))) <= 1e-6
+    # with 1024 logits and k = 16 the k-th / (k+1)-th gap falls inside the f32
+    # bound more often; at least 3 tokens in 4 must still be decided exactly
+    assert decided >= 0.75 * T
+
+
 def test_route_edge_cases(torch):
     import int4_group_quantized_router_amd as m
     cfg = CONFIGS["tiny"]
