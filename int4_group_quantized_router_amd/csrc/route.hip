@@ -31,31 +31,68 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxIt = 8;  // 16-byte Wr loads per lane: H / (256 * waves per row) <= 8
 
-__device__ void stage_input(const RouteArgs& a, float* xs, float* red, int T) {
+// The layer input of up to NT tokens in LDS as f32: x, or bf16(y / rms(y))
+// of the previous layer.  Every thread requests all of its values before it
+// uses any (one memory round trip, not one per value).  The sums of squares
+// have a fixed order: thread t adds y[t + 256 m] over m, then a 64-lane sum
+// per wave, then ((w0 + w1) + w2) + w3 over the four waves.
+template <int NT>
+__device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[kWaves], int T) {
+  constexpr int MM = 8;  // values per thread and token: H <= 2048 on the stacked path
   const int tid = threadIdx.x;
   const int H = a.H;
   if (a.y_prev) {
-    for (int t = 0; t < T; ++t) {
-      const float* y = a.y_prev + (size_t)t * H;
+    float v[NT][MM];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int m = 0; m < MM; ++m) {
+        const int i = tid + m * kThreads;
+        v[t][m] = (t < T && i < H) ? a.y_prev[(size_t)t * H + i] : 0.f;
+      }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       float s = 0.f;
-      for (int i = tid; i < H; i += kThreads) s = fmaf(y[i], y[i], s);
+#pragma unroll
+      for (int m = 0; m < MM; ++m)
+        if (tid + m * kThreads < H) s = fmaf(v[t][m], v[t][m], s);
       s = group_sum(s, kWave);
-      __syncthreads();
-      if ((tid & 63) == 0) red[tid >> 6] = s;
-      __syncthreads();
-      const float tot = ((red[0] + red[1]) + red[2]) + red[3];
-      const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
-      for (int i = tid; i < H; i += kThreads) {
-        const uint32_t b = f32_to_bf16(y[i] * r);
-        xs[t * H + i] = bf16_to_f32(b);
-        if (blockIdx.x == 0 && a.x_out) a.x_out[(size_t)t * H + i] = (uint16_t)b;
+      if ((tid & 63) == 0) red[t][tid >> 6] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < T) {
+        const float tot = ((red[t][0] + red[t][1]) + red[t][2]) + red[t][3];
+        const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          const int i = tid + m * kThreads;
+          if (i < H) {
+            const uint32_t b = f32_to_bf16(v[t][m] * r);
+            xs[t * H + i] = bf16_to_f32(b);
+            if (blockIdx.x == 0 && a.x_out) a.x_out[(size_t)t * H + i] = (uint16_t)b;
+          }
+        }
       }
     }
   } else {
-    for (int i = tid; i < T * H; i += kThreads) {
-      const uint16_t b = a.x[i];
-      xs[i] = bf16_to_f32(b);
-      if (blockIdx.x == 0 && a.x_out) a.x_out[i] = b;
+    const int n = T * H;
+    for (int base = 0; base < n; base += kThreads * MM) {
+      uint16_t v[MM];
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        const int i = base + tid + u * kThreads;
+        v[u] = i < n ? a.x[i] : (uint16_t)0;
+      }
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        const int i = base + tid + u * kThreads;
+        if (i < n) {
+          xs[i] = bf16_to_f32(v[u]);
+          if (blockIdx.x == 0 && a.x_out) a.x_out[i] = v[u];
+        }
+      }
     }
   }
 }
@@ -202,7 +239,7 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
 template <int NT, int VPL>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   extern __shared__ __align__(16) float xs[];  // [NT][H]
-  __shared__ float red[kWaves];
+  __shared__ float red_t[NT][kWaves];
   __shared__ float halves[kWaves][NT];
   __shared__ int s_last;
 
@@ -229,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   if (a.x) b.x = a.x + (size_t)t0 * a.H;
   if (a.y_prev) b.y_prev = a.y_prev + (size_t)t0 * a.H;
   if (a.x_out) b.x_out = a.x_out + (size_t)t0 * a.H;
-  stage_input(b, xs, red, T);
+  stage_input<NT>(b, xs, red_t, T);
   __syncthreads();
 
   float acc[NT];
