@@ -157,8 +157,11 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------ down+combine
 
+constexpr int kDownThreads = 1024;
+constexpr int kDownWaves = kDownThreads / kWave;
+
 template <int BITS, int NT, int BATCH>
-__global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
+__global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, int R) {
   using F = Fmt<BITS>;
   extern __shared__ __align__(16) uint8_t smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -167,19 +170,35 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(smem);                     // [T][k+1][hI]
   float* hsum = reinterpret_cast<float*>(smem + (size_t)T * kp1 * hI * 2);  // [T][k+1][hI/EPC]
   float* part = hsum + (size_t)T * kp1 * nchunk_h;                         // [T][k+1][R]
+  int8_t* jm = reinterpret_cast<int8_t*>(part + (size_t)T * kp1 * R);       // [n_routed][NT]
 
   const int n_routed = a.n_slot_max ? *a.n_slots : 0;
   const bool has_shared = a.shared_blob != nullptr;
 
-  // stage h (written by the gate/up kernel) and its per-chunk sums
+  // stage h (written by the gate/up kernel) and its per-chunk sums; each
+  // thread requests 8 pieces before storing any (one round trip per 8)
   {
     const int n16 = T * kp1 * hI * 2 / 16;
     const uint4* src = reinterpret_cast<const uint4*>(a.h);
     uint4* dst = reinterpret_cast<uint4*>(hbuf);
-    for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+    for (int base = 0; base < n16; base += kDownThreads * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + threadIdx.x + u * kDownThreads;
+        v[u] = i < n16 ? ld16(src + i) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + threadIdx.x + u * kDownThreads;
+        if (i < n16) dst[i] = v[u];
+      }
+    }
   }
+  for (int i = threadIdx.x; i < n_routed * NT; i += kDownThreads)
+    jm[i] = a.jmap[(i / NT) * kJmapStride + i % NT];
   __syncthreads();
-  for (int i = threadIdx.x; i < T * kp1 * nchunk_h; i += kThreads) {
+  for (int i = threadIdx.x; i < T * kp1 * nchunk_h; i += kDownThreads) {
     const uint32_t* c = reinterpret_cast<const uint32_t*>(hbuf + (size_t)i * F::kEpc);
     float s = 0.f;
 #pragma unroll
@@ -194,13 +213,13 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
   const int NRPr = (R + RPPr - 1) / RPPr, NRPs = (R + RPPs - 1) / RPPs;
   const int n_items = n_routed * NRPr + (has_shared ? NRPs : 0);
 
-  for (int it0 = wave; it0 < n_items; it0 += kWaves * BATCH) {
+  for (int it0 = wave; it0 < n_items; it0 += kDownWaves * BATCH) {
     uint4 q[BATCH];
     uint32_t sbw[BATCH];
     int rloc[BATCH], slot[BATCH], ci[BATCH], lpr[BATCH];
 #pragma unroll
     for (int bi = 0; bi < BATCH; ++bi) {
-      const int it = it0 + bi * kWaves;
+      const int it = it0 + bi * kDownWaves;
       slot[bi] = -2;
       q[bi] = make_uint4(0, 0, 0, 0);
       sbw[bi] = 0;
@@ -245,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t >= T) continue;
-        const int j = slot[bi] < 0 ? k : (int)a.jmap[slot[bi] * kJmapStride + t];
+        const int j = slot[bi] < 0 ? k : (int)jm[slot[bi] * NT + t];
         if (j < 0) continue;
         const int hb = (t * kp1 + j);
         const uint4* hsrc = reinterpret_cast<const uint4*>(hbuf + (size_t)hb * hI + ci[bi] * F::kEpc);
@@ -267,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void down_kernel(DecodeArgs a, int R) {
   }
   __syncthreads();
 
-  for (int i = threadIdx.x; i < T * R; i += kThreads) {
+  for (int i = threadIdx.x; i < T * R; i += kDownThreads) {
     const int t = i / R, r = i % R, row = row0 + r;
     if (row >= a.H) continue;
     float y = a.accumulate ? a.y_f32[(size_t)t * a.H + row] : 0.f;
@@ -473,12 +492,12 @@ hipError_t down_bits_nt(const DecodeArgs& a, hipStream_t s) {
   const int kp1 = a.k + 1;
   const size_t lds = (size_t)a.T * kp1 * a.hI * 2 +
                      (size_t)a.T * kp1 * (a.hI / Fmt<BITS>::kEpc) * 4 +
-                     (size_t)a.T * kp1 * kDownRows * 4;
+                     (size_t)a.T * kp1 * kDownRows * 4 + (size_t)a.n_slot_max * NT;
   const int blocks = (a.H + kDownRows - 1) / kDownRows;
   hipError_t e = allow_lds(down_kernel<BITS, NT, kDownBatch>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((down_kernel<BITS, NT, kDownBatch>), dim3(blocks), dim3(kThreads), lds, s,
-                     a, kDownRows);
+  hipLaunchKernelGGL((down_kernel<BITS, NT, kDownBatch>), dim3(blocks), dim3(kDownThreads), lds,
+                     s, a, kDownRows);
   return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ int max_lds_per_block(int device) {
 size_t down_lds_bytes(int T, int k, int hI, int bits) {
   const int epc = 128 / bits;
   return (size_t)T * (k + 1) * hI * 2 + (size_t)T * (k + 1) * (hI / epc) * 4 +
-         (size_t)T * (k + 1) * 8 * 4;
+         (size_t)T * (k + 1) * 8 * 4 + (size_t)T * k * kJmapStride;
 }
 
 int32_t check_layer_cfg(const moe_layer_cfg& c) {
