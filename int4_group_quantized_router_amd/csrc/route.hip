@@ -6,16 +6,18 @@
 // unquantised in f32 (the pages list routers among the dense weights kept in
 // memory).
 //
-// Kernel shape (decode, T <= 8 tokens):
+// Kernel shape (decode, T <= 8 tokens; 256 threads for one token, 512 for
+// up to 8):
 //   * the layer input is staged once per workgroup in LDS as f32; for layer
 //     l > 0 of a stack it is bf16(y_{l-1} / rms(y_{l-1})), computed here;
 //   * one 64-lane wave streams half a row of Wr (or all of it for H < 512)
 //     with 16-byte loads and keeps all T token sums in registers, so Wr is
 //     read exactly once per call;
 //   * the last workgroup to finish (device-scope ticket) reads the E logits
-//     back and runs the top-k on one wave per token: k rounds of a
-//     lane-local best + a 6-step butterfly arg-max.  Selection compares
-//     logits (softmax is monotone); ties go to the lower expert index.
+//     back and runs the top-k on one wave per token (a bitwise search for
+//     the k-th largest key with ballot counts, see wave_topk).  Selection
+//     compares logits (softmax is monotone); ties go to the lower expert
+//     index.
 //   * the same workgroup builds the list of distinct experts of the call
 //     (first appearance order) and, per distinct expert, which slot j each
 //     token gave it -- the expert kernels read every chosen expert once.
@@ -34,42 +36,48 @@ constexpr int kMaxIt = 8;  // 16-byte Wr loads per lane: H / (256 * waves per ro
 // The layer input of up to NT tokens in LDS as f32: x, or bf16(y / rms(y))
 // of the previous layer.  Every thread requests all of its values before it
 // uses any (one memory round trip, not one per value).  The sums of squares
-// have a fixed order: thread t adds y[t + 256 m] over m, then a 64-lane sum
-// per wave, then ((w0 + w1) + w2) + w3 over the four waves.
-template <int NT>
-__device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[kWaves], int T) {
-  constexpr int MM = 8;  // values per thread and token: H <= 2048 on the stacked path
-  const int tid = threadIdx.x;
+// have a fixed order whatever the workgroup size: thread t of a group of 256
+// adds y[t + 256 m] over m, then a 64-lane sum per wave, then
+// ((w0 + w1) + w2) + w3 over the group's four waves; with THR = 512 the two
+// groups take tokens [0, NT/2) and [NT/2, NT).
+template <int NT, int THR>
+__device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[4], int T) {
+  constexpr int MM = 8;            // values per thread and token: H <= 2048 on the stacked path
+  constexpr int NG = THR / 256;    // token groups
+  constexpr int NTG = (NT + NG - 1) / NG;
+  const int tid = threadIdx.x & 255, grp = threadIdx.x >> 8;
   const int H = a.H;
   if (a.y_prev) {
-    float v[NT][MM];
+    float v[NTG][MM];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int tt = 0; tt < NTG; ++tt)
 #pragma unroll
       for (int m = 0; m < MM; ++m) {
-        const int i = tid + m * kThreads;
-        v[t][m] = (t < T && i < H) ? a.y_prev[(size_t)t * H + i] : 0.f;
+        const int t = grp * NTG + tt, i = tid + m * 256;
+        v[tt][m] = (t < T && i < H) ? a.y_prev[(size_t)t * H + i] : 0.f;
       }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int tt = 0; tt < NTG; ++tt) {
+      const int t = grp * NTG + tt;
       float s = 0.f;
 #pragma unroll
       for (int m = 0; m < MM; ++m)
-        if (tid + m * kThreads < H) s = fmaf(v[t][m], v[t][m], s);
+        if (tid + m * 256 < H) s = fmaf(v[tt][m], v[tt][m], s);
       s = group_sum(s, kWave);
-      if ((tid & 63) == 0) red[t][tid >> 6] = s;
+      if ((tid & 63) == 0 && t < NT) red[t][tid >> 6] = s;
     }
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int tt = 0; tt < NTG; ++tt) {
+      const int t = grp * NTG + tt;
       if (t < T) {
         const float tot = ((red[t][0] + red[t][1]) + red[t][2]) + red[t][3];
         const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
-          const int i = tid + m * kThreads;
+          const int i = tid + m * 256;
           if (i < H) {
-            const uint32_t b = f32_to_bf16(v[t][m] * r);
+            const uint32_t b = f32_to_bf16(v[tt][m] * r);
             xs[t * H + i] = bf16_to_f32(b);
             if (blockIdx.x == 0 && a.x_out) a.x_out[(size_t)t * H + i] = (uint16_t)b;
           }
@@ -78,16 +86,17 @@ __device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[kWaves],
     }
   } else {
     const int n = T * H;
-    for (int base = 0; base < n; base += kThreads * MM) {
+    const int th = threadIdx.x;
+    for (int base = 0; base < n; base += THR * MM) {
       uint16_t v[MM];
 #pragma unroll
       for (int u = 0; u < MM; ++u) {
-        const int i = base + tid + u * kThreads;
+        const int i = base + th + u * THR;
         v[u] = i < n ? a.x[i] : (uint16_t)0;
       }
 #pragma unroll
       for (int u = 0; u < MM; ++u) {
-        const int i = base + tid + u * kThreads;
+        const int i = base + th + u * THR;
         if (i < n) {
           xs[i] = bf16_to_f32(v[u]);
           if (blockIdx.x == 0 && a.x_out) a.x_out[i] = v[u];
@@ -102,14 +111,14 @@ __device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[kWaves],
 // coherence point: they may have been written by workgroups on other XCDs.
 // With MFMA partial sums (a.part) the logits are formed here, and with
 // s_sraw the shared gate's input x . wsg of each token goes to s_sraw.
-template <int VPL>
+template <int VPL, int NW>
 __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val,
                             float* s_sraw) {
-  __shared__ int tmp_e[kWaves][MOE_MAX_TOPK];
-  __shared__ float tmp_v[kWaves][MOE_MAX_TOPK];
+  __shared__ int tmp_e[NW][MOE_MAX_TOPK];
+  __shared__ float tmp_v[NW][MOE_MAX_TOPK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
-  for (int t = t0 + wave; t < t1; t += kWaves) {
+  for (int t = t0 + wave; t < t1; t += NW) {
     const float* lg = a.logits + (size_t)t * E;
     float v[VPL];
     uint32_t key[VPL];
@@ -161,10 +170,11 @@ __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, floa
 
 // Renormalised weights over the chosen k (= softmax over the chosen
 // logits: the full-softmax denominator cancels) and the shared gate.
+template <int THR>
 __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_sel,
                               const float* s_val, const float* s_sraw) {
   const int k = a.k;
-  for (int t = t0 + (int)threadIdx.x; t < t1; t += kThreads) {
+  for (int t = t0 + (int)threadIdx.x; t < t1; t += THR) {
     const int r = t - t0;
     const float m = s_val[r * k];
     float ex[MOE_MAX_TOPK];
@@ -192,13 +202,14 @@ __device__ void write_weights(const RouteArgs& a, int t0, int t1, const int* s_s
 }
 
 // Distinct experts of the call in first-appearance order (token-major).
+template <int THR>
 __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, int* s_slot) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = a.T * a.k, k = a.k;
-  for (int e = threadIdx.x; e < a.E; e += kThreads) s_first[e] = 0x7fffffff;
-  for (int i = threadIdx.x; i < n * kJmapStride; i += kThreads) a.jmap[i] = -1;
+  for (int e = threadIdx.x; e < a.E; e += THR) s_first[e] = 0x7fffffff;
+  for (int i = threadIdx.x; i < n * kJmapStride; i += THR) a.jmap[i] = -1;
   __syncthreads();
-  for (int p = threadIdx.x; p < n; p += kThreads) atomicMin(&s_first[s_sel[p]], p);
+  for (int p = threadIdx.x; p < n; p += THR) atomicMin(&s_first[s_sel[p]], p);
   __syncthreads();
   if (wave == 0) {
     int base = 0;
@@ -215,7 +226,7 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
     }
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < n; p += kThreads) {
+  for (int p = threadIdx.x; p < n; p += THR) {
     const int e = s_sel[p];
     const int slot = s_slot[s_first[e]];
     a.jmap[slot * kJmapStride + p / k] = (int8_t)(p % k);
@@ -235,12 +246,14 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
 }
 
 // GEMV over Wr (and wsg as row E) for up to NT tokens: blockIdx.y selects a
-// tile of NT tokens.  With a ticket counter the last block runs the top-k.
-template <int NT, int VPL>
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+// tile of NT tokens.  With a ticket counter the last block runs the top-k
+// (one wave per token: THR = 512 takes 8 tokens in one round).
+template <int NT, int VPL, int THR>
+__global__ __launch_bounds__(THR) void route_kernel(RouteArgs a) {
+  constexpr int NW = THR / kWave;
   extern __shared__ __align__(16) float xs[];  // [NT][H]
-  __shared__ float red_t[NT][kWaves];
-  __shared__ float halves[kWaves][NT];
+  __shared__ float red_t[NT][4];
+  __shared__ float halves[NW][NT];
   __shared__ int s_last;
 
   const int t0 = blockIdx.y * NT;
@@ -249,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int H = a.H, E = a.E;
   const int rows = E + (a.wsg && a.sigma ? 1 : 0);
   const int wpr = (H % 512 == 0) ? 2 : 1;
-  const int item = blockIdx.x * kWaves + wave;
+  const int item = blockIdx.x * NW + wave;
   const int row = item / wpr, part = item % wpr;
   const int span = H / wpr, c0 = part * span, nit = span / (4 * kWave);
 
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   if (a.x) b.x = a.x + (size_t)t0 * a.H;
   if (a.y_prev) b.y_prev = a.y_prev + (size_t)t0 * a.H;
   if (a.x_out) b.x_out = a.x_out + (size_t)t0 * a.H;
-  stage_input<NT>(b, xs, red_t, T);
+  stage_input<NT, THR>(b, xs, red_t, T);
   __syncthreads();
 
   float acc[NT];
@@ -333,10 +346,10 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ float s_val[NT * MOE_MAX_TOPK];
   __shared__ int s_slot[NT * MOE_MAX_TOPK];
   __shared__ int s_first[1024];
-  topk_tokens<VPL>(a, 0, a.T, s_sel, s_val, nullptr);
+  topk_tokens<VPL, NW>(a, 0, a.T, s_sel, s_val, nullptr);
   __syncthreads();
-  write_weights(a, 0, a.T, s_sel, s_val, nullptr);
-  if (a.n_slots) build_slots(a, s_sel, s_first, s_slot);
+  write_weights<THR>(a, 0, a.T, s_sel, s_val, nullptr);
+  if (a.n_slots) build_slots<THR>(a, s_sel, s_first, s_slot);
 }
 
 // Top-k over logits written by an earlier launch (or formed here from the
@@ -349,16 +362,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(RouteArgs a) {
   const int t0 = blockIdx.x * kWaves;
   const int t1 = min(a.T, t0 + kWaves);
   float* sr = a.part && a.sigma && a.wsg ? s_sraw : nullptr;
-  topk_tokens<VPL>(a, t0, t1, s_sel, s_val, sr);
+  topk_tokens<VPL, kWaves>(a, t0, t1, s_sel, s_val, sr);
   __syncthreads();
-  write_weights(a, t0, t1, s_sel, s_val, sr);
+  write_weights<kThreads>(a, t0, t1, s_sel, s_val, sr);
 }
 
 template <int NT>
 hipError_t launch_route_nt(const RouteArgs& a, hipStream_t s, bool fused) {
+  constexpr int THR = NT == 1 ? 256 : 512;
+  constexpr int NW = THR / kWave;
   const int rows = a.E + (a.wsg && a.sigma ? 1 : 0);
   const int wpr = (a.H % 512 == 0) ? 2 : 1;
-  dim3 grid((rows * wpr + kWaves - 1) / kWaves, fused ? 1 : (a.T + NT - 1) / NT);
+  dim3 grid((rows * wpr + NW - 1) / NW, fused ? 1 : (a.T + NT - 1) / NT);
   const size_t lds = (size_t)NT * a.H * sizeof(float);
   RouteArgs b = a;
   if (!fused) {
@@ -367,9 +382,9 @@ hipError_t launch_route_nt(const RouteArgs& a, hipStream_t s, bool fused) {
   const int vpl = (a.E + 63) / 64;
 #define MOE_ROUTE_CASE(V)                                                           \
   if (vpl <= V) {                                                                   \
-    hipError_t e = allow_lds(route_kernel<NT, V>, lds);                             \
+    hipError_t e = allow_lds(route_kernel<NT, V, THR>, lds);                        \
     if (e != hipSuccess) return e;                                                  \
-    hipLaunchKernelGGL((route_kernel<NT, V>), grid, dim3(kThreads), lds, s, b);     \
+    hipLaunchKernelGGL((route_kernel<NT, V, THR>), grid, dim3(THR), lds, s, b);     \
     return hipGetLastError();                                                       \
   }
   MOE_ROUTE_CASE(1)
