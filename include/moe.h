@@ -276,8 +276,10 @@ int32_t moe_layer_destroy(moe_layer* layer);
  * MoE layers, fused into layer l's router.  All layers share H and top_k.
  *
  * One-token calls (T == 1) on a stack whose layers are all resident and
- * share one shape run as ONE persistent kernel for the whole stack (one
- * workgroup per compute unit, cooperative launch): the pages find their
+ * share one shape run as ONE persistent kernel for the whole stack (256
+ * workgroups, needing a device with at least 256 compute units; all of them
+ * must be resident at once, so other work on the device during the call can
+ * make it time out): the pages find their
  * decode loop bound by dispatch, not IO ([ttj] "실무자가 따져볼 지점"), and
  * this removes the launches and dependency stalls between layers.  Its
  * outputs are bit-identical to the per-layer kernels'.  Workgroups hand

@@ -245,8 +245,9 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
 }
 
 // Sets up the persistent one-token path if every layer is resident, all
-// layers share one shape and the device runs cooperative launches.  A stack
-// that does not qualify keeps persistent_ok = false (not an error).
+// layers share one shape and the device has at least as many compute units
+// as the kernel has workgroups (so all of them can be resident at once).  A
+// stack that does not qualify keeps persistent_ok = false (not an error).
 int32_t setup_persistent(moe_stack* st) {
   st->persistent_ok = false;
   const moe_layer* L0 = st->layers[0];
@@ -260,11 +261,10 @@ int32_t setup_persistent(moe_stack* st) {
       return MOE_OK;
     if ((L->wsg != nullptr) != (L0->wsg != nullptr) || !L->shared_blob) return MOE_OK;
   }
-  int coop = 0, cus = 0, clk_khz = 0;
-  MOE_HIP_TRY(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, L0->device));
+  int cus = 0, clk_khz = 0;
   MOE_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L0->device));
   MOE_HIP_TRY(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, L0->device));
-  if (!coop || cus < 1 || clk_khz < 1 || n > kStackMaxLayers) return MOE_OK;
+  if (cus < 1 || clk_khz < 1 || n > kStackMaxLayers) return MOE_OK;
   const int H = c.hidden, E = c.experts, k = c.top_k;
   if (!stack_decode_supported(H, E, k, c.inter, c.shared_inter, c.bits, cus)) return MOE_OK;
   const int grid = kStackGrid;

@@ -10,9 +10,14 @@
 // and dependency stalls of three kernels, so this kernel runs every layer of
 // the stack in one launch:
 //
-// * one workgroup per compute unit, all resident (cooperative launch); the
-//   shape (bits, H, I, Is, k, top-k width) is compile-time, so all index
-//   arithmetic folds to constants;
+// * 256 workgroups, no more than the device has compute units, so on an
+//   otherwise idle device all are resident at once.  The launch is an
+//   ordinary one: the kernel uses no grid-wide primitive, and the
+//   cooperative launch path costs ~16 us more per call.  If work on another
+//   stream keeps some workgroups from starting, the bounded waits (below)
+//   turn that into a reported error, not a hang.  The shape (bits, H, I, Is,
+//   k, top-k width) is compile-time, so all index arithmetic folds to
+//   constants;
 // * a layer has three all-to-all hand-offs: its output y (every workgroup
 //   needs all of it for the next router and gate/up), the router logits
 //   (every workgroup runs the top-k itself) and the SwiGLU activations h
@@ -590,9 +595,8 @@ hipError_t launch_shape(const StackArgs& a, hipStream_t s) {
   const size_t lds = stack_lds_bytes(S::H, a.E, S::K, S::I, S::IS, S::BITS);
   hipError_t e = allow_lds(stack_decode_kernel<S, VPL>, lds);
   if (e != hipSuccess) return e;
-  void* args[] = {const_cast<StackArgs*>(&a)};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&stack_decode_kernel<S, VPL>),
-                                    dim3(kG), dim3(kNT), args, (unsigned)lds, s);
+  hipLaunchKernelGGL((stack_decode_kernel<S, VPL>), dim3(kG), dim3(kNT), lds, s, a);
+  return hipGetLastError();
 }
 
 // The instances: (bits, H, I, Is, k) x top-k width (64 * VPL >= E).
