@@ -190,6 +190,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true",
                     help="decode: three kernels per layer instead of one persistent kernel")
+    ap.add_argument("--store", choices=("memory", "file"), default="memory",
+                    help="stream80b: pinned-memory store, or a container file read with one "
+                         "pread per miss (written to --store-path first, then dropped from the "
+                         "OS cache)")
+    ap.add_argument("--store-path", default=None,
+                    help="file for --store file (default: $TMPDIR or /tmp, removed afterwards)")
     ap.add_argument("--layers", type=int, default=None,
                     help="stream80b / decode80b_int8: build only this many layers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -426,9 +432,17 @@ def bench_stream(args, cfg):
     warmup = 0 if args.warmup is None else args.warmup
     torch.cuda.set_device(0)
     dims = {"hidden": cfg.hidden, "experts": cfg.experts, "inter": cfg.inter, "bits": cfg.bits}
-    log(f"[bench] filling the pinned store: {cfg.layers} layers x {cfg.experts} experts")
     t_b = time.perf_counter()
-    store, stride = W.fill_store(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    path = None
+    if args.store == "file":
+        path = args.store_path or os.path.join(os.environ.get("TMPDIR", "/tmp"),
+                                               f"moe_store_{os.getpid()}.qpack")
+        log(f"[bench] writing the container file {path}: {cfg.layers} layers x {cfg.experts} experts")
+        store, stride = W.fill_file_store(path, dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+        log(f"[bench] store: {m.STORE_KINDS[m.expert_store_kind(store)]}")
+    else:
+        log(f"[bench] filling the pinned store: {cfg.layers} layers x {cfg.experts} experts")
+        store, stride = W.fill_store(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
     cap = int(cfg.pool_frac * cfg.layers * cfg.experts)
     pool = m.slotpool_create(store, cap, 0)
     layers, stack, keep = _build_stack(cfg, pool=pool)
@@ -444,6 +458,9 @@ def bench_stream(args, cfg):
     tok_s = steps / dt
     log(f"[bench] {tok_s:.1f} tok/s; hits {d['hits']} misses {d['misses']} "
         f"({d['hits'] / max(acc, 1):.3f} hit rate); {d['bytes_h2d'] / dt / 1e9:.2f} GB/s host->HBM")
+    if path:
+        log(f"[bench] file reads: {d['bytes_read'] / 1e9:.2f} GB in {d['read_ns'] / 1e9:.3f} s "
+            f"({d['read_ns'] / 1e3 / max(d['misses'], 1):.0f} us per miss)")
     out = {"metric": "MoE stack tokens/sec, batch-1 decode with expert streaming (30% HBM pool), 1 GPU",
            "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
            "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -455,12 +472,20 @@ def bench_stream(args, cfg):
                       "pool_hits": d["hits"], "pool_misses": d["misses"],
                       "pool_evictions": d["evictions"], "hit_rate": d["hits"] / max(acc, 1),
                       "bytes_h2d": d["bytes_h2d"], "h2d_GBps": d["bytes_h2d"] / dt / 1e9}}
+    if path:
+        out["metric"] = out["metric"].replace("expert streaming", "expert streaming from a file")
+        out["config"]["store"] = m.STORE_KINDS[m.expert_store_kind(store)]
+        out["config"]["file_read_s"] = d["read_ns"] / 1e9
+        out["config"]["file_read_us_per_miss"] = d["read_ns"] / 1e3 / max(d["misses"], 1)
+        out["config"]["file_read_GBps"] = d["bytes_read"] / max(d["read_ns"], 1)
     print(json.dumps(out), flush=True)
     m.moe_stack_destroy(stack)
     for L in layers:
         m.moe_layer_destroy(L)
     m.slotpool_destroy(pool)
     m.expert_store_destroy(store)
+    if path and not args.store_path:
+        os.remove(path)
 
 
 def bench_prefill(args, cfg):

@@ -43,7 +43,8 @@ enum {
   MOE_E_HIP = -3,            /* a HIP runtime call failed */
   MOE_E_RANGE = -4,          /* layer or expert index out of range */
   MOE_E_POOL_EXHAUSTED = -5, /* every slot is pinned; nothing can be evicted */
-  MOE_E_BUSY = -6            /* the slot is pinned by an in-flight acquire */
+  MOE_E_BUSY = -6,           /* the slot is pinned by an in-flight acquire */
+  MOE_E_IO = -7              /* a file operation of a file-backed store failed */
 };
 
 #define MOE_MAX_TOPK 16      /* largest k the router supports */
@@ -177,6 +178,30 @@ int32_t expert_store_host_ptr(const expert_store* store, int32_t layer,
                               int32_t expert, void** ptr);
 int32_t expert_store_destroy(expert_store* store);
 
+/* File-backed store: the container itself.  Blob (l, e) sits at byte offset
+ * (int64)(l*E + e)*stride of the file at `path` (no header), and a pool miss
+ * fetches it with ONE pread of `stride` bytes ([xix] how-it-works
+ * paragraph: one pread per expert from a fixed-stride container).  create
+ * != 0: create or truncate the file to L*E*stride bytes, writable through
+ * expert_store_write (pwrite); create == 0: open an existing file of at
+ * least that size, read-only.  Reads bypass the OS page cache (O_DIRECT)
+ * when the file system allows it, else go through it; expert_store_kind
+ * tells which.  MOE_E_IO (with the errno text in moe_last_error) if a file
+ * operation fails.  The store owns its descriptors until
+ * expert_store_destroy. */
+int32_t expert_store_open_file(const char* path, int32_t layers, int32_t experts,
+                               int64_t stride, int32_t create, expert_store** out);
+/* kind (out): 0 pinned memory, 1 file read with O_DIRECT, 2 file read
+ * through the OS page cache. */
+int32_t expert_store_kind(const expert_store* store, int32_t* kind);
+/* Copy blob (l, e) into dst (host, stride bytes) -- for a file store one
+ * pread (test hook). */
+int32_t expert_store_read(const expert_store* store, int32_t layer, int32_t expert,
+                          void* dst);
+/* File store: write back and drop the file's pages from the OS page cache,
+ * so that later reads come from the device.  No-op for a memory store. */
+int32_t expert_store_drop_cache(expert_store* store);
+
 /* ------------------------------------------------------------------------
  * Bounded HBM slot pool over a store ([xix] how-it-works paragraph:
  * popular experts cached in a bounded pool with LFU plus recency eviction;
@@ -186,7 +211,11 @@ int32_t expert_store_destroy(expert_store* store);
  * count and stamps the tick.  A miss takes the lowest-numbered free slot,
  * else evicts the unpinned resident slot with the smallest (use count, last
  * tick, layer, expert), and is filled by exactly one hipMemcpyAsync of
- * `stride` bytes from the store on the pool's own copy stream.  That copy
+ * `stride` bytes from the store on the pool's own copy stream (for a file
+ * store, after one pread of the blob -- with O_DIRECT into an ordinary
+ * page-aligned buffer, then copied to one of 8 pinned staging buffers;
+ * otherwise into the staging buffer itself; acquire blocks the calling
+ * thread for that read).  That copy
  * waits for the evicted slot's last reader (write-after-read) and the
  * compute stream waits for the copy (read-after-write) -- [lens]
  * "TurboFieldfareとの関係": explicit hazard management.  The policy decides
@@ -199,10 +228,14 @@ typedef struct slotpool_stats {
   int64_t misses;
   int64_t evictions;
   int64_t bytes_h2d;
+  int64_t bytes_read;  /* file store: bytes read from the file */
+  int64_t read_ns;     /* file store: host time spent in those reads */
 } slotpool_stats;
 
 /* capacity: number of slots (>= 1); device: HIP device ordinal.  Allocates
- * capacity * stride bytes of device memory and a copy stream. */
+ * capacity * stride bytes of device memory and a copy stream (and, over a
+ * file store, 8 x stride bytes of pinned staging and one stride-sized
+ * page-aligned buffer).  The store must outlive the pool. */
 int32_t slotpool_create(const expert_store* store, int64_t capacity,
                         int32_t device, slotpool** out);
 /* Make experts[0..n) of `layer` resident and pin them.  slot_ptrs (out, n

@@ -12,6 +12,7 @@ need a GPU, calling it does.
 from __future__ import annotations
 
 import ctypes as C
+import os
 
 import numpy as np
 
@@ -195,6 +196,35 @@ def expert_store_destroy(store) -> None:
     _check(_lib_().expert_store_destroy(_h(store)), "expert_store_destroy")
 
 
+def expert_store_open_file(path: str, layers: int, experts: int, stride: int,
+                           create: bool = False) -> Handle:
+    out = C.c_void_p()
+    _check(_lib_().expert_store_open_file(os.fsencode(path), layers, experts, stride,
+                                          1 if create else 0, C.byref(out)),
+           "expert_store_open_file")
+    return Handle(out.value)
+
+
+STORE_KINDS = {0: "pinned memory", 1: "file, O_DIRECT reads", 2: "file, reads through the OS cache"}
+
+
+def expert_store_kind(store) -> int:
+    out = C.c_int32()
+    _check(_lib_().expert_store_kind(_h(store), C.byref(out)), "expert_store_kind")
+    return out.value
+
+
+def expert_store_read(store, layer: int, expert: int, stride: int) -> np.ndarray:
+    out = np.empty(stride, dtype=np.uint8)
+    _check(_lib_().expert_store_read(_h(store), layer, expert, out.ctypes.data),
+           "expert_store_read")
+    return out
+
+
+def expert_store_drop_cache(store) -> None:
+    _check(_lib_().expert_store_drop_cache(_h(store)), "expert_store_drop_cache")
+
+
 def slotpool_create(store, capacity: int, device: int = 0) -> Handle:
     out = C.c_void_p()
     _check(_lib_().slotpool_create(_h(store), capacity, device, C.byref(out)), "slotpool_create")
@@ -230,7 +260,7 @@ def slotpool_get_stats(pool) -> dict:
     st = PoolStats()
     _check(_lib_().slotpool_get_stats(_h(pool), C.byref(st)), "slotpool_get_stats")
     return {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
-            "bytes_h2d": st.bytes_h2d}
+            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns}
 
 
 def slotpool_slot_of(pool, layer: int, expert: int) -> int:

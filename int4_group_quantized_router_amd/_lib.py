@@ -18,12 +18,14 @@ MOE_E_HIP = -3
 MOE_E_RANGE = -4
 MOE_E_POOL_EXHAUSTED = -5
 MOE_E_BUSY = -6
+MOE_E_IO = -7
 MOE_MAX_TOPK = 16
 MOE_KERNEL_ROUTE, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_STACK = 0, 1, 2, 3
 MOE_MAX_DECODE_T = 8
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_NOMEM", -3: "MOE_E_HIP",
-                -4: "MOE_E_RANGE", -5: "MOE_E_POOL_EXHAUSTED", -6: "MOE_E_BUSY"}
+                -4: "MOE_E_RANGE", -5: "MOE_E_POOL_EXHAUSTED", -6: "MOE_E_BUSY",
+                -7: "MOE_E_IO"}
 
 
 class QShape(C.Structure):
@@ -43,7 +45,8 @@ class QMatrixHost(C.Structure):
 
 class PoolStats(C.Structure):
     _fields_ = [("hits", C.c_int64), ("misses", C.c_int64),
-                ("evictions", C.c_int64), ("bytes_h2d", C.c_int64)]
+                ("evictions", C.c_int64), ("bytes_h2d", C.c_int64),
+                ("bytes_read", C.c_int64), ("read_ns", C.c_int64)]
 
 
 class LayerCfg(C.Structure):
@@ -68,6 +71,10 @@ SIGNATURES = {
     "expert_store_write": [_P, _I32, _I32, _P, _I64],
     "expert_store_host_ptr": [_P, _I32, _I32, C.POINTER(_P)],
     "expert_store_destroy": [_P],
+    "expert_store_open_file": [C.c_char_p, _I32, _I32, _I64, _I32, C.POINTER(_P)],
+    "expert_store_kind": [_P, C.POINTER(_I32)],
+    "expert_store_read": [_P, _I32, _I32, _P],
+    "expert_store_drop_cache": [_P],
     "slotpool_create": [_P, _I64, _I32, C.POINTER(_P)],
     "slotpool_acquire": [_P, _I32, _P, _I32, _P, _P, _P],
     "slotpool_release": [_P, _I32, _P, _I32, _P],

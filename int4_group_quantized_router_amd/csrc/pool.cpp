@@ -1,4 +1,5 @@
-// Fixed-stride pinned-host expert store and the bounded HBM slot pool.
+// Fixed-stride expert stores (pinned host memory, or a file read with one
+// pread per expert) and the bounded HBM slot pool.
 //
 // The pages keep only the dense core resident and stream routed experts on
 // demand: each expert is one fixed-stride blob fetched with a single read
@@ -14,6 +15,23 @@
 //     contents were last released on a compute stream (write after read);
 //   * the compute stream waits for the copy's event before any kernel reads
 //     the slot (read after write).
+// A file-backed store is the pages' container itself: blob (l, e) at byte
+// offset (l*E + e)*stride of one file, fetched by ONE pread of `stride`
+// bytes ([xix] how-it-works paragraph).  Reads use O_DIRECT where the file
+// system allows it (the OS page cache is bypassed, as the pages' reads of
+// the SSD are).  The kernel cannot DMA a direct read into HIP's pinned
+// memory (the read fails with EFAULT), so a direct read lands in an
+// ordinary page-aligned buffer and is copied into one of a ring of pinned
+// staging buffers; a buffered read goes straight into the staging buffer.
+// Each staging buffer is reused only after the host-to-device copy from it
+// has finished.
+#include <fcntl.h>
+#include <sys/stat.h>
+#include <unistd.h>
+
+#include <cerrno>
+#include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <set>
 #include <tuple>
@@ -26,7 +44,11 @@ struct expert_store {
   int32_t layers;
   int32_t experts;
   int64_t stride;
-  uint8_t* base;  // pinned host
+  uint8_t* base;      // pinned host memory (kind 0), else NULL
+  int32_t kind;       // 0 memory, 1 file read with O_DIRECT, 2 file read through the OS cache
+  int fd = -1;        // file: buffered descriptor (writes, cache control, kind-2 reads)
+  int fd_direct = -1; // file, kind 1: O_DIRECT read descriptor
+  bool writable = false;
 };
 
 namespace {
@@ -45,6 +67,44 @@ struct Slot {
 using VictimKey = std::tuple<int64_t, int64_t, int32_t, int32_t, int32_t>;  // count, tick, l, e, slot
 
 constexpr int kEventRing = 4096;
+constexpr int kStaging = 8;  // pinned staging buffers of a pool over a file store
+
+// pread until n bytes arrived; 0 or an errno value (EIO for a short file)
+int read_full(int fd, uint8_t* dst, int64_t n, int64_t off) {
+  while (n > 0) {
+    const ssize_t r = pread(fd, dst, (size_t)n, (off_t)off);
+    if (r < 0) {
+      if (errno == EINTR) continue;
+      return errno;
+    }
+    if (r == 0) return EIO;
+    dst += r;
+    off += r;
+    n -= r;
+  }
+  return 0;
+}
+
+int write_full(int fd, const uint8_t* src, int64_t n, int64_t off) {
+  while (n > 0) {
+    const ssize_t r = pwrite(fd, src, (size_t)n, (off_t)off);
+    if (r < 0) {
+      if (errno == EINTR) continue;
+      return errno;
+    }
+    src += r;
+    off += r;
+    n -= r;
+  }
+  return 0;
+}
+
+// One blob of a file store into dst (4096-aligned when the store reads
+// with O_DIRECT).
+int read_blob(const expert_store* st, int64_t key, uint8_t* dst) {
+  const int fd = st->kind == 1 ? st->fd_direct : st->fd;
+  return read_full(fd, dst, st->stride, key * st->stride);
+}
 
 }  // namespace
 
@@ -60,6 +120,12 @@ struct slotpool {
   std::set<int32_t> free_slots;
   std::vector<hipEvent_t> ring;                // release events, reused round-robin
   size_t ring_next = 0;
+  std::vector<uint8_t*> stage;                 // file store: pinned staging buffers
+  std::vector<hipEvent_t> stage_done;          // copy out of stage[i] finished
+  std::vector<bool> stage_used;
+  int stage_next = 0;
+  uint8_t* bounce = nullptr;                   // file store: page-aligned ordinary memory
+  bool read_via_bounce = false;
   int64_t tick = 0;
   slotpool_stats stats{};
 
@@ -110,7 +176,7 @@ int32_t expert_store_create(int32_t layers, int32_t experts, int64_t stride, exp
     return fail(MOE_E_NOMEM, "hipHostMalloc(%lld bytes): %s", (long long)bytes,
                 hipGetErrorString(e));
   expert_store* s = new (std::nothrow) expert_store{layers, experts, stride,
-                                                    static_cast<uint8_t*>(base)};
+                                                    static_cast<uint8_t*>(base), 0};
   if (!s) {
     (void)hipHostFree(base);
     return fail(MOE_E_NOMEM, "host allocation failed");
@@ -127,6 +193,13 @@ int32_t expert_store_write(expert_store* store, int32_t layer, int32_t expert, c
   if (st != MOE_OK) return st;
   MOE_REQUIRE(n >= 0 && n <= store->stride, "n = %lld exceeds stride %lld", (long long)n,
               (long long)store->stride);
+  if (!store->base) {
+    MOE_REQUIRE(store->writable, "file store was opened read-only");
+    const int err = write_full(store->fd, static_cast<const uint8_t*>(blob), n,
+                               ((int64_t)layer * store->experts + expert) * store->stride);
+    if (err) return fail(MOE_E_IO, "pwrite of blob (%d, %d): %s", layer, expert, strerror(err));
+    return MOE_OK;
+  }
   std::memcpy(store->base + ((int64_t)layer * store->experts + expert) * store->stride, blob,
               (size_t)n);
   return MOE_OK;
@@ -138,13 +211,111 @@ int32_t expert_store_host_ptr(const expert_store* store, int32_t layer, int32_t 
   MOE_REQUIRE(store && ptr, "null argument");
   int32_t st = check_le(store, layer, expert);
   if (st != MOE_OK) return st;
+  MOE_REQUIRE(store->base, "a file-backed store has no host address");
   *ptr = store->base + ((int64_t)layer * store->experts + expert) * store->stride;
+  return MOE_OK;
+}
+
+int32_t expert_store_open_file(const char* path, int32_t layers, int32_t experts, int64_t stride,
+                               int32_t create, expert_store** out) {
+  clear_error();
+  MOE_REQUIRE(path && out && layers >= 1 && experts >= 1, "bad argument");
+  MOE_REQUIRE(stride > 0 && stride % 4096 == 0, "stride must be a positive multiple of 4096");
+  const int64_t bytes = (int64_t)layers * experts * stride;
+  const int fd = open(path, create ? (O_RDWR | O_CREAT | O_TRUNC) : O_RDONLY, 0644);
+  if (fd < 0) return fail(MOE_E_IO, "open(%s): %s", path, strerror(errno));
+  if (create) {
+    if (ftruncate(fd, (off_t)bytes) != 0) {
+      const int err = errno;
+      close(fd);
+      return fail(MOE_E_IO, "ftruncate(%s, %lld): %s", path, (long long)bytes, strerror(err));
+    }
+  } else {
+    struct stat sb;
+    if (fstat(fd, &sb) != 0 || (int64_t)sb.st_size < bytes) {
+      close(fd);
+      return fail(MOE_E_INVAL, "%s holds fewer than %d x %d x %lld bytes", path, layers, experts,
+                  (long long)stride);
+    }
+  }
+  // O_DIRECT if the file system takes it for an aligned read of one page
+  int fdd = open(path, O_RDONLY | O_DIRECT);
+  if (fdd >= 0) {
+    void* probe = nullptr;
+    bool ok = posix_memalign(&probe, 4096, 4096) == 0;
+    if (ok) ok = pread(fdd, probe, 4096, 0) == 4096;
+    free(probe);
+    if (!ok) {
+      close(fdd);
+      fdd = -1;
+    }
+  }
+  expert_store* s = new (std::nothrow) expert_store{layers, experts, stride, nullptr,
+                                                    fdd >= 0 ? 1 : 2};
+  if (!s) {
+    if (fdd >= 0) close(fdd);
+    close(fd);
+    return fail(MOE_E_NOMEM, "host allocation failed");
+  }
+  s->fd = fd;
+  s->fd_direct = fdd;
+  s->writable = create != 0;
+  *out = s;
+  return MOE_OK;
+}
+
+int32_t expert_store_kind(const expert_store* store, int32_t* kind) {
+  clear_error();
+  MOE_REQUIRE(store && kind, "null argument");
+  *kind = store->kind;
+  return MOE_OK;
+}
+
+int32_t expert_store_read(const expert_store* store, int32_t layer, int32_t expert, void* dst) {
+  clear_error();
+  MOE_REQUIRE(store && dst, "null argument");
+  int32_t st = check_le(store, layer, expert);
+  if (st != MOE_OK) return st;
+  const int64_t key = (int64_t)layer * store->experts + expert;
+  if (store->base) {
+    std::memcpy(dst, store->base + key * store->stride, (size_t)store->stride);
+    return MOE_OK;
+  }
+  uint8_t* out = static_cast<uint8_t*>(dst);
+  void* bounce = nullptr;
+  if (store->kind == 1 && reinterpret_cast<uintptr_t>(dst) % 4096) {
+    if (posix_memalign(&bounce, 4096, (size_t)store->stride) != 0)
+      return fail(MOE_E_NOMEM, "bounce buffer of %lld bytes", (long long)store->stride);
+    out = static_cast<uint8_t*>(bounce);
+  }
+  const int err = read_blob(store, key, out);
+  if (!err && bounce) std::memcpy(dst, bounce, (size_t)store->stride);
+  free(bounce);
+  if (err) return fail(MOE_E_IO, "pread of blob (%d, %d): %s", layer, expert, strerror(err));
+  return MOE_OK;
+}
+
+int32_t expert_store_drop_cache(expert_store* store) {
+  clear_error();
+  MOE_REQUIRE(store, "null argument");
+  if (store->base) return MOE_OK;
+  if (store->writable && fdatasync(store->fd) != 0)
+    return fail(MOE_E_IO, "fdatasync: %s", strerror(errno));
+  const int err = posix_fadvise(store->fd, 0, 0, POSIX_FADV_DONTNEED);
+  if (err) return fail(MOE_E_IO, "posix_fadvise: %s", strerror(err));
   return MOE_OK;
 }
 
 int32_t expert_store_destroy(expert_store* store) {
   clear_error();
   if (!store) return MOE_OK;
+  if (!store->base) {
+    if (store->fd_direct >= 0) close(store->fd_direct);
+    const int rc = close(store->fd);
+    delete store;
+    if (rc != 0) return fail(MOE_E_IO, "close: %s", strerror(errno));
+    return MOE_OK;
+  }
   hipError_t e = hipHostFree(store->base);
   delete store;
   if (e != hipSuccess) return fail(MOE_E_HIP, "hipHostFree: %s", hipGetErrorString(e));
@@ -177,6 +348,22 @@ int32_t slotpool_create(const expert_store* store, int64_t capacity, int32_t dev
   p->ring.resize(kEventRing, nullptr);
   for (int i = 0; i < kEventRing && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&p->ring[i], hipEventDisableTiming);
+  if (!store->base) {
+    void* b = nullptr;
+    if (posix_memalign(&b, 4096, (size_t)store->stride) != 0) e = hipErrorOutOfMemory;
+    p->bounce = static_cast<uint8_t*>(b);
+    p->read_via_bounce = store->kind == 1;
+    p->stage.resize(kStaging, nullptr);
+    p->stage_done.resize(kStaging, nullptr);
+    p->stage_used.resize(kStaging, false);
+    for (int i = 0; i < kStaging && e == hipSuccess; ++i) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&p->stage[i]), (size_t)store->stride,
+                        hipHostMallocDefault);
+      if (e == hipSuccess && reinterpret_cast<uintptr_t>(p->stage[i]) % 4096)
+        e = hipErrorInvalidValue;  // O_DIRECT needs page-aligned buffers
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->stage_done[i], hipEventDisableTiming);
+    }
+  }
   if (e != hipSuccess) {
     slotpool_destroy(p);
     return fail(MOE_E_HIP, "slot pool setup: %s", hipGetErrorString(e));
@@ -234,12 +421,39 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
         pool->stats.evictions += 1;
       }
       s = *pool->free_slots.begin();
-      pool->free_slots.erase(pool->free_slots.begin());
       Slot& x = pool->slots[s];
+      const uint8_t* src = pool->store->base ? pool->store->base + k * stride : nullptr;
+      int si = -1;
+      if (!src) {
+        // file store: one pread of the blob into the next staging buffer
+        // once the copy out of that buffer has finished
+        si = pool->stage_next;
+        pool->stage_next = (si + 1) % kStaging;
+        if (pool->stage_used[si]) MOE_HIP_TRY(hipEventSynchronize(pool->stage_done[si]));
+        const auto t0 = std::chrono::steady_clock::now();
+        int err = pool->read_via_bounce ? EFAULT : read_blob(pool->store, k, pool->stage[si]);
+        if (err == EFAULT) {
+          pool->read_via_bounce = true;
+          err = read_blob(pool->store, k, pool->bounce);
+          if (!err) std::memcpy(pool->stage[si], pool->bounce, (size_t)stride);
+        }
+        pool->stats.read_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
+                                   std::chrono::steady_clock::now() - t0)
+                                   .count();
+        if (err) {
+          for (int32_t ps : pinned) unpin(pool, ps);
+          return fail(MOE_E_IO, "pread of blob (layer %d, expert %d): %s", layer, e,
+                      strerror(err));
+        }
+        pool->stats.bytes_read += stride;
+        src = pool->stage[si];
+        pool->stage_used[si] = true;
+      }
+      pool->free_slots.erase(pool->free_slots.begin());
       if (x.last_use) MOE_HIP_TRY(hipStreamWaitEvent(pool->copy, x.last_use, 0));
-      const uint8_t* src = pool->store->base + k * stride;
       MOE_HIP_TRY(hipMemcpyAsync(pool->dev + (int64_t)s * stride, src, (size_t)stride,
                                  hipMemcpyHostToDevice, pool->copy));
+      if (si >= 0) MOE_HIP_TRY(hipEventRecord(pool->stage_done[si], pool->copy));
       MOE_HIP_TRY(hipEventRecord(x.ready, pool->copy));
       MOE_HIP_TRY(hipStreamWaitEvent(compute, x.ready, 0));
       x.fill_pending = true;
@@ -328,6 +542,11 @@ int32_t slotpool_destroy(slotpool* pool) {
     if (x.ready) (void)hipEventDestroy(x.ready);
   for (hipEvent_t ev : pool->ring)
     if (ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : pool->stage_done)
+    if (ev) (void)hipEventDestroy(ev);
+  for (uint8_t* b : pool->stage)
+    if (b) (void)hipHostFree(b);
+  free(pool->bounce);
   if (pool->copy) (void)hipStreamDestroy(pool->copy);
   if (pool->dev) (void)hipFree(pool->dev);
   delete pool;

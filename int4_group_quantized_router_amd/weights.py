@@ -5,6 +5,8 @@
   blob (l, e) at byte (l*E + e)*stride.
 * ``fill_store``: the same blobs in the library's pinned-host expert store,
   for the slot-pool path.
+* ``fill_file_store``: the same blobs in a fixed-stride container file (blob
+  (l, e) at byte (l*E + e)*stride), read back with one pread per expert.
 
 The arrays come from caller-supplied functions, so this module knows nothing
 about where weights come from.  Packing runs on a thread pool (the C packer
@@ -17,7 +19,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from . import expert_store_create, expert_store_host_ptr, moe_blob_layout_get, moe_blob_pack
+from . import (expert_store_create, expert_store_drop_cache, expert_store_host_ptr,
+               expert_store_open_file, expert_store_write, moe_blob_layout_get, moe_blob_pack)
 
 
 def _threads(n):
@@ -66,4 +69,20 @@ def fill_store(dims: dict, layers: int, expert_fn, threads=None):
         view = np.ctypeslib.as_array((np.ctypeslib.ctypes.c_uint8 * (E * stride)).from_address(base))
         pack_experts(H, I, bits, lambda e, l=l: expert_fn(l, e), range(E),
                      view.reshape(E, stride), threads)
+    return store, stride
+
+
+def fill_file_store(path, dims: dict, layers: int, expert_fn, threads=None):
+    """Container file of all L*E routed blobs (created or truncated), opened as
+    a file-backed store; its pages are dropped from the OS cache afterwards so
+    that pool misses read the device.  expert_fn(l, e) -> arrays."""
+    H, E, I, bits = dims["hidden"], dims["experts"], dims["inter"], dims["bits"]
+    stride = moe_blob_layout_get(H, I, bits)["stride"]
+    store = expert_store_open_file(path, layers, E, stride, create=True)
+    host = np.empty((E, stride), dtype=np.uint8)
+    for l in range(layers):
+        pack_experts(H, I, bits, lambda e, l=l: expert_fn(l, e), range(E), host, threads)
+        for e in range(E):
+            expert_store_write(store, l, e, host[e])
+    expert_store_drop_cache(store)
     return store, stride

@@ -109,3 +109,53 @@ def test_argument_errors_without_gpu():
     assert st == _lib.MOE_E_INVAL
     st = lib.expert_store_create(1, 1, 1000, C.byref(out))
     assert st == _lib.MOE_E_INVAL
+
+
+def test_file_store_round_trip_without_gpu(tmp_path):
+    """A file-backed store puts blob (l, e) at byte (l*E + e)*stride of the
+    file and reads it back with one pread, through O_DIRECT or the OS cache;
+    reopened read-only it refuses writes; a short file is refused."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import _lib
+    _lib_or_skip()
+    L, E, stride = 2, 5, 8192
+    path = str(tmp_path / "experts.qpack")
+    rng = np.random.default_rng(11)
+    blobs = rng.integers(0, 256, size=(L, E, stride), dtype=np.uint8)
+    st = m.expert_store_open_file(path, L, E, stride, create=True)
+    try:
+        assert m.expert_store_kind(st) in (1, 2)
+        for l in range(L):
+            for e in range(E):
+                n = stride if (l + e) % 2 == 0 else stride - 100  # partial blobs: rest stays 0
+                m.expert_store_write(st, l, e, blobs[l, e, :n])
+        m.expert_store_drop_cache(st)
+        for l in range(L):
+            for e in range(E):
+                want = blobs[l, e].copy()
+                if (l + e) % 2:
+                    want[stride - 100:] = 0
+                assert np.array_equal(m.expert_store_read(st, l, e, stride), want)
+        with pytest.raises(m.MoEError) as ei:
+            m.expert_store_read(st, L, 0, stride)
+        assert ei.value.status == _lib.MOE_E_RANGE
+        with pytest.raises(m.MoEError):
+            m.expert_store_host_ptr(st, 0, 0)
+    finally:
+        m.expert_store_destroy(st)
+    raw = np.fromfile(path, dtype=np.uint8).reshape(L, E, stride)
+    assert np.array_equal(raw[1, 3], blobs[1, 3])  # offset (1*E + 3)*stride
+    ro = m.expert_store_open_file(path, L, E, stride)
+    try:
+        assert np.array_equal(m.expert_store_read(ro, 0, 2, stride), blobs[0, 2])
+        with pytest.raises(m.MoEError) as ei:
+            m.expert_store_write(ro, 0, 0, blobs[0, 0])
+        assert ei.value.status == _lib.MOE_E_INVAL
+    finally:
+        m.expert_store_destroy(ro)
+    with pytest.raises(m.MoEError) as ei:
+        m.expert_store_open_file(path, L + 1, E, stride)
+    assert ei.value.status == _lib.MOE_E_INVAL
+    with pytest.raises(m.MoEError) as ei:
+        m.expert_store_open_file(str(tmp_path / "missing" / "x.qpack"), L, E, stride)
+    assert ei.value.status == _lib.MOE_E_IO

@@ -382,7 +382,8 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
                     replay.acquire(l, ex)
                     replay.release(l, ex)
             stats = m.slotpool_get_stats(pool)
-            assert stats == replay.stats(), (stats, replay.stats())
+            assert {k: stats[k] for k in replay.stats()} == replay.stats(), (stats, replay.stats())
+            assert stats["bytes_read"] == 0  # a memory store reads no file
             for l in range(L):
                 for e in range(cfg.experts):
                     want = replay.slot_of[(l, e)] if replay.resident(l, e) else -1
@@ -405,6 +406,63 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
         with pytest.raises(m.MoEError) as ei:
             m.slotpool_acquire(pool, 0, list(range(cap + 1)))
         assert "POOL_EXHAUSTED" in str(ei.value)
+        torch.cuda.synchronize()
+    finally:
+        m.moe_stack_destroy(s_res)
+        m.moe_stack_destroy(s_pool)
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
+def test_file_store_pool_matches_resident_bitwise(torch, tmp_path):
+    """Experts fetched from the container file (one pread per miss into
+    pinned staging, then the copy to the slot) give exactly the resident
+    result, per token and layer, with hits and misses mixed."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from oracle.pool_replay import PoolReplay
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=2, experts=64)
+    _print("file store pool", cfg.name)
+    dm = DeviceModel(cfg)
+    store, stride = Wt.fill_file_store(str(tmp_path / "experts.qpack"), dims_of(cfg), cfg.layers,
+                                       lambda l, e: expert_arrays(cfg, l, e))
+    _print("store kind", m.STORE_KINDS[m.expert_store_kind(store)])
+    cap = 24
+    pool = m.slotpool_create(store, cap, 0)
+    res_layers = dm.make_layers()
+    pool_layers = dm.make_layers(pool=pool)
+    s_res, s_pool = m.moe_stack_create(res_layers), m.moe_stack_create(pool_layers)
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    replay = PoolReplay(cap, stride)
+    try:
+        for tok in range(12):
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            outs = []
+            for st in (s_res, s_pool):
+                yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                y = m.moe_stack_forward(st, x0, y_layers=yl, idx=idx)
+                torch.cuda.synchronize()
+                outs.append((y.cpu().numpy(), yl.cpu().numpy(), idx.cpu().numpy()))
+            assert np.array_equal(outs[0][0], outs[1][0])
+            assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+            for l in range(L):
+                ex = outs[1][2][l, 0].tolist()
+                replay.acquire(l, ex)
+                replay.release(l, ex)
+        stats = m.slotpool_get_stats(pool)
+        assert {k_: stats[k_] for k_ in replay.stats()} == replay.stats()
+        assert stats["misses"] > cap and stats["hits"] > 0 and stats["evictions"] > 0, stats
+        assert stats["bytes_read"] == stats["misses"] * stride and stats["read_ns"] > 0
+        # slot bytes equal the file's bytes (a hit: no copy in flight)
+        l, e = next(iter(replay.slot_of))
+        ptrs, miss = m.slotpool_acquire(pool, l, [e])
+        assert not miss[0]
+        torch.cuda.synchronize()
+        assert np.array_equal(_device_bytes(ptrs[0], stride), m.expert_store_read(store, l, e, stride))
+        m.slotpool_release(pool, l, [e])
         torch.cuda.synchronize()
     finally:
         m.moe_stack_destroy(s_res)
