@@ -29,11 +29,13 @@
 #include <sys/stat.h>
 #include <unistd.h>
 
+#include <atomic>
 #include <cerrno>
 #include <chrono>
 #include <cstdlib>
 #include <cstring>
 #include <set>
+#include <thread>
 #include <tuple>
 #include <unordered_map>
 #include <vector>
@@ -124,7 +126,7 @@ struct slotpool {
   std::vector<hipEvent_t> stage_done;          // copy out of stage[i] finished
   std::vector<bool> stage_used;
   int stage_next = 0;
-  uint8_t* bounce = nullptr;                   // file store: page-aligned ordinary memory
+  std::vector<uint8_t*> bounce;                // file store: page-aligned ordinary memory
   bool read_via_bounce = false;
   int64_t tick = 0;
   slotpool_stats stats{};
@@ -349,9 +351,12 @@ int32_t slotpool_create(const expert_store* store, int64_t capacity, int32_t dev
   for (int i = 0; i < kEventRing && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&p->ring[i], hipEventDisableTiming);
   if (!store->base) {
-    void* b = nullptr;
-    if (posix_memalign(&b, 4096, (size_t)store->stride) != 0) e = hipErrorOutOfMemory;
-    p->bounce = static_cast<uint8_t*>(b);
+    p->bounce.resize(kStaging, nullptr);
+    for (int i = 0; i < kStaging && e == hipSuccess; ++i) {
+      void* b = nullptr;
+      if (posix_memalign(&b, 4096, (size_t)store->stride) != 0) e = hipErrorOutOfMemory;
+      p->bounce[i] = static_cast<uint8_t*>(b);
+    }
     p->read_via_bounce = store->kind == 1;
     p->stage.resize(kStaging, nullptr);
     p->stage_done.resize(kStaging, nullptr);
@@ -383,6 +388,82 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
   std::vector<int32_t> pinned;
   pinned.reserve(n);
   const int64_t stride = pool->store->stride;
+  // misses of a file store whose reads have not run yet: (slot, key, staging buffer)
+  std::vector<std::tuple<int32_t, int64_t, int>> pend;
+
+  // Enqueue the fill of slot s from host bytes src: the copy waits for the
+  // slot's last reader, the compute stream waits for the copy.
+  auto fill = [&](int32_t s, const uint8_t* src, int si) -> int32_t {
+    Slot& x = pool->slots[s];
+    if (x.last_use) MOE_HIP_TRY(hipStreamWaitEvent(pool->copy, x.last_use, 0));
+    MOE_HIP_TRY(hipMemcpyAsync(pool->dev + (int64_t)s * stride, src, (size_t)stride,
+                               hipMemcpyHostToDevice, pool->copy));
+    if (si >= 0) MOE_HIP_TRY(hipEventRecord(pool->stage_done[si], pool->copy));
+    MOE_HIP_TRY(hipEventRecord(x.ready, pool->copy));
+    MOE_HIP_TRY(hipStreamWaitEvent(compute, x.ready, 0));
+    x.fill_pending = true;
+    pool->stats.bytes_h2d += stride;
+    return MOE_OK;
+  };
+
+  // Run the pending reads (one thread each when there are several), then
+  // enqueue their copies in order.  A failed read drops every pending slot
+  // and unpins the rest of the call.
+  auto flush = [&]() -> int32_t {
+    if (pend.empty()) return MOE_OK;
+    std::vector<int> errs(pend.size(), 0);
+    std::atomic<bool> efault{false};
+    const bool via_bounce = pool->read_via_bounce;
+    auto read_one = [&](size_t i) {
+      const int64_t k = std::get<1>(pend[i]);
+      const int si = std::get<2>(pend[i]);
+      int err = via_bounce ? EFAULT : read_blob(pool->store, k, pool->stage[si]);
+      if (err == EFAULT) {
+        if (!via_bounce) efault = true;
+        err = read_blob(pool->store, k, pool->bounce[si]);
+        if (!err) std::memcpy(pool->stage[si], pool->bounce[si], (size_t)stride);
+      }
+      errs[i] = err;
+    };
+    const auto t0 = std::chrono::steady_clock::now();
+    if (pend.size() == 1) {
+      read_one(0);
+    } else {
+      std::vector<std::thread> th;
+      th.reserve(pend.size());
+      for (size_t i = 0; i < pend.size(); ++i) th.emplace_back(read_one, i);
+      for (std::thread& t : th) t.join();
+    }
+    pool->stats.read_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
+                               std::chrono::steady_clock::now() - t0)
+                               .count();
+    if (efault) pool->read_via_bounce = true;
+    for (size_t i = 0; i < pend.size(); ++i) {
+      if (!errs[i]) continue;
+      const int64_t k_bad = std::get<1>(pend[i]);
+      std::set<int32_t> dropped;
+      for (const auto& q : pend) {
+        pool->slots[std::get<0>(q)].pins = 0;
+        drop(pool, std::get<0>(q));
+        dropped.insert(std::get<0>(q));
+      }
+      for (int32_t ps : pinned)
+        if (!dropped.count(ps)) unpin(pool, ps);
+      pend.clear();
+      return fail(MOE_E_IO, "pread of blob (layer %lld, expert %lld): %s",
+                  (long long)(k_bad / pool->store->experts),
+                  (long long)(k_bad % pool->store->experts), strerror(errs[i]));
+    }
+    for (const auto& [s, k, si] : pend) {
+      (void)k;
+      const int32_t st = fill(s, pool->stage[si], si);
+      if (st != MOE_OK) return st;
+      pool->stats.bytes_read += stride;
+    }
+    pend.clear();
+    return MOE_OK;
+  };
+
   for (int i = 0; i < n; ++i) {
     const int32_t e = experts[i];
     const int64_t k = pool->key(layer, e);
@@ -411,6 +492,9 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
     } else {
       if (pool->free_slots.empty()) {
         if (pool->victims.empty()) {
+          // experts admitted earlier in the call are filled, then unpinned
+          const int32_t st = flush();
+          if (st != MOE_OK) return st;
           for (int32_t ps : pinned) unpin(pool, ps);
           return fail(MOE_E_POOL_EXHAUSTED,
                       "all %lld slots pinned; cannot admit (layer %d, expert %d)",
@@ -421,42 +505,8 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
         pool->stats.evictions += 1;
       }
       s = *pool->free_slots.begin();
-      Slot& x = pool->slots[s];
-      const uint8_t* src = pool->store->base ? pool->store->base + k * stride : nullptr;
-      int si = -1;
-      if (!src) {
-        // file store: one pread of the blob into the next staging buffer
-        // once the copy out of that buffer has finished
-        si = pool->stage_next;
-        pool->stage_next = (si + 1) % kStaging;
-        if (pool->stage_used[si]) MOE_HIP_TRY(hipEventSynchronize(pool->stage_done[si]));
-        const auto t0 = std::chrono::steady_clock::now();
-        int err = pool->read_via_bounce ? EFAULT : read_blob(pool->store, k, pool->stage[si]);
-        if (err == EFAULT) {
-          pool->read_via_bounce = true;
-          err = read_blob(pool->store, k, pool->bounce);
-          if (!err) std::memcpy(pool->stage[si], pool->bounce, (size_t)stride);
-        }
-        pool->stats.read_ns += std::chrono::duration_cast<std::chrono::nanoseconds>(
-                                   std::chrono::steady_clock::now() - t0)
-                                   .count();
-        if (err) {
-          for (int32_t ps : pinned) unpin(pool, ps);
-          return fail(MOE_E_IO, "pread of blob (layer %d, expert %d): %s", layer, e,
-                      strerror(err));
-        }
-        pool->stats.bytes_read += stride;
-        src = pool->stage[si];
-        pool->stage_used[si] = true;
-      }
       pool->free_slots.erase(pool->free_slots.begin());
-      if (x.last_use) MOE_HIP_TRY(hipStreamWaitEvent(pool->copy, x.last_use, 0));
-      MOE_HIP_TRY(hipMemcpyAsync(pool->dev + (int64_t)s * stride, src, (size_t)stride,
-                                 hipMemcpyHostToDevice, pool->copy));
-      if (si >= 0) MOE_HIP_TRY(hipEventRecord(pool->stage_done[si], pool->copy));
-      MOE_HIP_TRY(hipEventRecord(x.ready, pool->copy));
-      MOE_HIP_TRY(hipStreamWaitEvent(compute, x.ready, 0));
-      x.fill_pending = true;
+      Slot& x = pool->slots[s];
       x.layer = layer;
       x.expert = e;
       x.count = 1;
@@ -464,14 +514,29 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
       x.pins = 1;
       pool->where[k] = s;
       pool->stats.misses += 1;
-      pool->stats.bytes_h2d += stride;
       miss = true;
+      if (pool->store->base) {
+        const int32_t st = fill(s, pool->store->base + k * stride, -1);
+        if (st != MOE_OK) return st;
+      } else {
+        // file store: the read waits in `pend` (at most one per staging
+        // buffer) until the call's misses are known
+        if ((int)pend.size() == kStaging) {
+          const int32_t st = flush();
+          if (st != MOE_OK) return st;
+        }
+        const int si = pool->stage_next;
+        pool->stage_next = (si + 1) % kStaging;
+        if (pool->stage_used[si]) MOE_HIP_TRY(hipEventSynchronize(pool->stage_done[si]));
+        pool->stage_used[si] = true;
+        pend.emplace_back(s, k, si);
+      }
     }
     pinned.push_back(s);
     slot_ptrs[i] = pool->dev + (int64_t)s * stride;
     if (was_miss) was_miss[i] = miss ? 1 : 0;
   }
-  return MOE_OK;
+  return flush();
 }
 
 int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
@@ -546,7 +611,7 @@ int32_t slotpool_destroy(slotpool* pool) {
     if (ev) (void)hipEventDestroy(ev);
   for (uint8_t* b : pool->stage)
     if (b) (void)hipHostFree(b);
-  free(pool->bounce);
+  for (uint8_t* b : pool->bounce) free(b);
   if (pool->copy) (void)hipStreamDestroy(pool->copy);
   if (pool->dev) (void)hipFree(pool->dev);
   delete pool;
