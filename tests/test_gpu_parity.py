@@ -256,6 +256,37 @@ def test_layer_full_shape(torch, name):
     _layer_case(torch, cfg, [[0], [1], list(range(2, 10)), [10, 11, 12], [13]])
 
 
+@pytest.mark.parametrize("name", ["decode80b_int8", "decode35b"])
+def test_layer_batch_repeated_tokens(torch, name):
+    """Batches of 8 in which tokens repeat (all 8 equal: every distinct
+    expert is shared by all tokens): each distinct expert is read once and
+    applied to every token that chose it, so equal tokens give bitwise equal
+    rows, and every row matches the oracle."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS[name].replace(layers=1)
+    _print("layer repeated tokens", name)
+    _layer_case(torch, cfg, [[3, 3, 5, 3, 7, 7, 3, 5], [4] * 8])
+    dm = DeviceModel(cfg, layers=1)
+    L = dm.make_layers()[0]
+    try:
+        for toks in ([3, 3, 5, 3, 7, 7, 3, 5], [4] * 8):
+            xb = np.stack([token_x(cfg, t) for t in toks])
+            y32 = torch.empty((8, cfg.hidden), dtype=torch.float32, device="cuda")
+            y16 = torch.empty((8, cfg.hidden), dtype=torch.int16, device="cuda")
+            idx = torch.empty((8, cfg.top_k), dtype=torch.int32, device="cuda")
+            w = torch.empty((8, cfg.top_k), dtype=torch.float32, device="cuda")
+            m.moe_layer_forward(L, torch.from_numpy(xb.view(np.int16)).cuda(), y16, y32, idx, w)
+            torch.cuda.synchronize()
+            y, ix, wv = y32.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+            for i in range(8):
+                j = toks.index(toks[i])
+                assert np.array_equal(ix[i], ix[j])
+                assert np.array_equal(wv[i].view(np.uint32), wv[j].view(np.uint32))
+                assert np.array_equal(y[i].view(np.uint32), y[j].view(np.uint32))
+    finally:
+        dm.destroy()
+
+
 def test_layer_shared_inter_differs(torch):
     cfg = CONFIGS["tiny"].replace(inter=128, shared_inter=64, experts=32, top_k=4)
     _print("layer I != Is")
