@@ -62,8 +62,9 @@ def algorithmic_bytes(cfg):
     gate_up = k * 2 * mat(I, H) + 2 * mat(Is, H) + H * 2 + (k * I + Is) * 2
     down = k * mat(H, I) + mat(H, Is) + (k * I + Is) * 2 + H * 4 + H * 2
     route = E * H * 4 + E * 4 + H * 4 + H * 4
+    quant = (k + 1) * 3 * mat(I, H) if I == Is else k * 3 * mat(I, H) + 3 * mat(Is, H)
     return {"route": route, "gate_up": gate_up, "down": down,
-            "layer": route + gate_up + down}
+            "layer": route + gate_up + down, "expert_quantized": quant}
 
 
 def prefill_flops(cfg, T):
@@ -274,6 +275,17 @@ def main():
     m.moe_timer_attach(None)
     gu_ms = m.moe_timer_read(timer)
     m.moe_timer_destroy(timer)
+    dn_ms = None
+    if not persistent:
+        # the same tokens again with the down kernel timed (the expert-kernel reading)
+        timer = m.moe_timer_create(m._lib.MOE_KERNEL_DOWN, args.steps * cfg.layers)
+        m.moe_timer_attach(timer)
+        for i in range(args.warmup, n_tok):
+            step(i)
+        torch.cuda.synchronize()
+        m.moe_timer_attach(None)
+        dn_ms = m.moe_timer_read(timer)
+        m.moe_timer_destroy(timer)
 
     tok_s = args.steps / elapsed
     ab = algorithmic_bytes(cfg)
@@ -339,6 +351,14 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if dn_ms is not None:
+        # quantised expert bytes over the two expert kernels' mean durations
+        t_exp = (float(np.mean(gu_ms)) + float(np.mean(dn_ms))) / 1e3
+        out["config"]["expert_kernels"] = {
+            "gate_up_mean_us": float(np.mean(gu_ms)) * 1e3, "down_mean_us": float(np.mean(dn_ms)) * 1e3,
+            "quantized_bytes_per_layer": ab["expert_quantized"],
+            "GBps": ab["expert_quantized"] / t_exp / 1e9,
+            "frac_of_hbm_peak": ab["expert_quantized"] / t_exp / 1e9 / HBM_PEAK_GBS}
     print(json.dumps(out), flush=True)
     m.moe_stack_destroy(stack)
     for L in layers:
