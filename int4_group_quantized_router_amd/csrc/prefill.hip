@@ -464,7 +464,7 @@ template <int BITS>
 struct BRaw {  // one K group of packed weights for the lane's two weight rows
   static constexpr int N = GemmCfg<BITS>::NQ;
   uint4 q[2][N];
-  uint32_t sb[2];
+  float s24[2], s20[2], bi[2];  // per column block: s * 2^24, s * 2^20, b
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -615,8 +615,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
   // bf16 B operand of MFMA step s for column block cb: weights 8s..8s+7 of
   // the lane's 32
   auto b_operand = [&](const R& r, int cb, int s) __attribute__((always_inline)) -> uint4 {
-    const float sc = bf16_lo(r.sb[cb]), bi = bf16_hi(r.sb[cb]);
-    const float s24 = sc * 16777216.0f, s20 = sc * 1048576.0f;
+    const float s24 = r.s24[cb], s20 = r.s20[cb], bi = r.bi[cb];
     if (BITS == 4) {
       const uint4 q = r.q[cb][0];
       const uint32_t w = s == 0 ? q.x : s == 1 ? q.y : s == 2 ? q.z : q.w;
@@ -640,16 +639,25 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
         const int piece = BITS == 4 ? ((kg & 1) << 1) | kh : 2 * kh + i;
         r.q[cb][i] = *reinterpret_cast<const uint4*>(bs + cb * 2048 + ((piece ^ bh) << 4));
       }
+    uint32_t sb[2];
     if (SB4) {
       const uint8_t* ss = smem + C::kSbOff + ((kg >> 2) & 1) * 4096 + wave * 1024 + (kg & 3) * 4;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        r.sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 16);
+        sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 16);
     } else {
       const uint8_t* ss = smem + C::kSbOff + (kg % 3) * 1024 + wave * 256;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        r.sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 4);
+        sb[cb] = *reinterpret_cast<const uint32_t*>(ss + (cb * 32 + l32) * 4);
+    }
+    // the group's scale and bias, once for its four MFMA steps
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float sc = bf16_lo(sb[cb]);
+      r.s24[cb] = sc * 16777216.0f;
+      r.s20[cb] = sc * 1048576.0f;
+      r.bi[cb] = bf16_hi(sb[cb]);
     }
     return r;
   };
