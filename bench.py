@@ -46,7 +46,7 @@ STACK_TRAFFIC = {
 # The same for the gate/up grouped GEMM of the 4096-token prefill layer
 # (profiles/prefill80b_grouped_gemm.md).
 PREFILL_TRAFFIC = {
-    "prefill80b": {"fetch_kib": 615322, "write_kib": 45056,
+    "prefill80b": {"fetch_kib": 617559, "write_kib": 45056,
                    "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
 }
 
