@@ -99,16 +99,12 @@ def cpu_baseline_prefill(cfg, budget_s=20.0):
                       f"bf16-weight mode; BLAS {blas} threads)"}
 
 
-def cpu_baseline(cfg, budget_s=20.0):
-    """Time the oracle on token 0 through as many layers as fit the budget."""
+def _oracle_layers(cfg, budget_s):
+    """Run the oracle on token 0 through the stack until the budget is spent:
+    (layers done, seconds)."""
     import numpy as np
     from moe_inputs import expert_arrays, router_arrays, shared_arrays, token_x
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
     x = token_x(cfg, 0)
     t0 = time.perf_counter()
     done = 0
@@ -120,13 +116,30 @@ def cpu_baseline(cfg, budget_s=20.0):
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
-    dt = time.perf_counter() - t0
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, budget_s=20.0, one_thread_budget_s=8.0):
+    """Time the oracle on token 0 through as many layers as fit the budget,
+    with the host's BLAS threads, then again on one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas, threadpool_limits = 1, None
+    done, dt = _oracle_layers(cfg, budget_s)
     per_layer = dt / done
-    return {"value": 1.0 / (per_layer * cfg.layers), "unit": "tokens/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"token 0 through {done} of {cfg.layers} layers in {dt:.1f} s "
-                      f"(NumPy float64; dequantisation single-threaded, BLAS {blas} threads); "
-                      f"tokens/s = 1 / (s per layer x {cfg.layers})"}
+    res = {"value": 1.0 / (per_layer * cfg.layers), "unit": "tokens/s", "cores": int(blas),
+           "kind": "oracle",
+           "sample": f"token 0 through {done} of {cfg.layers} layers in {dt:.1f} s "
+                     f"(NumPy float64; dequantisation single-threaded, BLAS {blas} threads); "
+                     f"tokens/s = 1 / (s per layer x {cfg.layers})"}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, t1 = _oracle_layers(cfg, one_thread_budget_s)
+        res["one_thread"] = {"value": 1.0 / (t1 / d1 * cfg.layers), "unit": "tokens/s",
+                             "sample": f"token 0 through {d1} layers in {t1:.1f} s, BLAS 1 thread"}
+    return res
 
 
 def calibrate_copy(nbytes):

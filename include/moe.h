@@ -293,10 +293,12 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr,
 
 /* x: device bf16 [T, H].  y_bf16: device bf16 [T, H] (required); y_f32:
  * device f32 [T, H] or NULL; idx_out: device int32 [T, k] or NULL; w_out:
- * device f32 [T, k] or NULL.  1 <= T <= MOE_MAX_DECODE_T takes the
- * per-token GEMV path; larger T takes the sorted grouped-GEMM path
- * (MOE_E_INVAL until that path is built).  With a pool, the call copies the
- * chosen expert ids to the host and waits for them (one sync per call). */
+ * device f32 [T, k] or NULL.  T == 0 returns MOE_OK and touches nothing
+ * (x and y_bf16 may then be NULL); 1 <= T <= MOE_MAX_DECODE_T takes the
+ * per-token GEMV path; larger T takes the sorted grouped-GEMM path.  With a
+ * pool, the call needs the chosen experts on the host: the router kernel
+ * publishes them to pinned host memory and the calling thread waits for
+ * them before it acquires slots (one host round trip per call). */
 int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T,
                           uint16_t* y_bf16, float* y_f32, int32_t* idx_out,
                           float* w_out, hipStream_t stream);

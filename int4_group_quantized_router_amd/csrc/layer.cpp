@@ -709,8 +709,10 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
 int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T, uint16_t* y_bf16,
                           float* y_f32, int32_t* idx_out, float* w_out, hipStream_t stream) {
   clear_error();
-  MOE_REQUIRE(layer && x && y_bf16, "null argument");
-  MOE_REQUIRE(T >= 1, "T must be >= 1");
+  MOE_REQUIRE(layer, "null argument");
+  MOE_REQUIRE(T >= 0, "T must be >= 0");
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(x && y_bf16, "null argument");
   if (T > MOE_MAX_DECODE_T)
     return forward_prefill(layer, x, T, y_bf16, y_f32, idx_out, w_out, stream);
   return forward_decode(layer, x, nullptr, nullptr, T, y_bf16, y_f32 ? y_f32 : layer->y, idx_out,

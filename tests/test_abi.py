@@ -109,6 +109,9 @@ def test_argument_errors_without_gpu():
     assert st == _lib.MOE_E_INVAL
     st = lib.expert_store_create(1, 1, 1000, C.byref(out))
     assert st == _lib.MOE_E_INVAL
+    # a layer call needs a layer, even for an empty batch
+    st = lib.moe_layer_forward(None, None, 0, None, None, None, None, None)
+    assert st == _lib.MOE_E_INVAL and b"null" in lib.moe_last_error()
 
 
 def test_file_store_round_trip_without_gpu(tmp_path):

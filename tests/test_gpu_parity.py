@@ -287,6 +287,54 @@ def test_layer_batch_repeated_tokens(torch, name):
         dm.destroy()
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode35b"])
+def test_layer_empty_and_zero_input(torch, name):
+    """Degenerate inputs on every layer path (1 token, a batch of 8, the
+    many-token path at 24): an empty batch is a no-op on a resident and on a
+    pooled layer (the pool sees no access); x = 0 makes every gate and up
+    product zero, so h = silu(0) * 0 = 0 and y = 0 exactly, while routing
+    ranks the router bias alone (ties to the lowest index, so experts
+    0..k-1 with weights 1/k when there is no bias)."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS[name].replace(layers=1)
+    _print("layer empty / zero input", name)
+    dm = DeviceModel(cfg, layers=1)
+    store, _ = Wt.fill_store(dims_of(cfg), 1, lambda l, e: expert_arrays(cfg, l, e))
+    pool = m.slotpool_create(store, cfg.experts, 0)
+    L, Lp = dm.make_layers()[0], dm.make_layers(pool=pool)[0]
+    H, k = cfg.hidden, cfg.top_k
+    try:
+        for layer in (L, Lp):
+            x = torch.zeros((0, H), dtype=torch.int16, device="cuda")
+            y16 = torch.empty((0, H), dtype=torch.int16, device="cuda")
+            m.moe_layer_forward(layer, x, y16)
+            torch.cuda.synchronize()
+        st = m.slotpool_get_stats(pool)
+        assert st["hits"] == 0 and st["misses"] == 0, st
+        _, rb, _ = router_arrays(cfg, 0)
+        want_idx = np.argsort(-rb.astype(np.float64), kind="stable")[:k]
+        lw = rb.astype(np.float64)[want_idx]
+        want_w = np.exp(lw - lw.max()) / np.exp(lw - lw.max()).sum()
+        for T in (1, 8, 24):
+            x = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+            y16 = torch.full((T, H), 7, dtype=torch.int16, device="cuda")
+            y32 = torch.full((T, H), 7.0, dtype=torch.float32, device="cuda")
+            idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+            m.moe_layer_forward(L, x, y16, y32, idx, w)
+            torch.cuda.synchronize()
+            assert np.all(y32.cpu().numpy() == 0.0), T
+            assert np.all(y16.cpu().numpy() == 0), T
+            assert (idx.cpu().numpy() == want_idx).all(), (T, idx.cpu().numpy()[0], want_idx)
+            assert np.allclose(w.cpu().numpy(), want_w, rtol=4e-6, atol=0), T
+    finally:
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
 def test_layer_shared_inter_differs(torch):
     cfg = CONFIGS["tiny"].replace(inter=128, shared_inter=64, experts=32, top_k=4)
     _print("layer I != Is")
