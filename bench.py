@@ -399,12 +399,14 @@ def _build_stack(cfg, pool=None):
     return layers, m.moe_stack_create(layers), keep
 
 
-def _run_tokens(m, stack, X, Y, T, warmup, steps):
+def _run_tokens(m, stack, X, Y, T, warmup, steps, after_warmup=None):
     import torch
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
     torch.cuda.synchronize()
+    if after_warmup is not None:
+        after_warmup()
     t0 = time.perf_counter()
     for i in range(warmup, warmup + steps):
         m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
@@ -461,8 +463,10 @@ def bench_stream(args, cfg):
     import int4_group_quantized_router_amd as m
     from int4_group_quantized_router_amd import weights as W
     from moe_inputs import expert_arrays, tokens_x
-    steps = 128 if args.steps is None else args.steps
-    warmup = 0 if args.warmup is None else args.warmup
+    # default: all of the workload's tokens, the first 64 as warm-up (the pool
+    # starts empty), so the timed tokens give the warm hit rate
+    warmup = min(64, cfg.tokens) if args.warmup is None else args.warmup
+    steps = cfg.tokens - warmup if args.steps is None else args.steps
     torch.cuda.set_device(0)
     dims = {"hidden": cfg.hidden, "experts": cfg.experts, "inter": cfg.inter, "bits": cfg.bits}
     t_b = time.perf_counter()
@@ -484,16 +488,35 @@ def bench_stream(args, cfg):
     X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
     Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
     s0 = m.slotpool_get_stats(pool)
-    dt = _run_tokens(m, stack, X, Y, 1, warmup, steps)
+    snap = {}
+    dt = _run_tokens(m, stack, X, Y, 1, warmup, steps,
+                     after_warmup=lambda: snap.update(m.slotpool_get_stats(pool)))
     s1 = m.slotpool_get_stats(pool)
-    d = {k: s1[k] - s0[k] for k in s1}
-    acc = d["hits"] + d["misses"]
+    d = {k: s1[k] - snap[k] for k in s1}          # timed tokens
+    d_all = {k: s1[k] - s0[k] for k in s1}        # warm-up and timed tokens
+    acc, acc_all = d["hits"] + d["misses"], d_all["hits"] + d_all["misses"]
     tok_s = steps / dt
-    log(f"[bench] {tok_s:.1f} tok/s; hits {d['hits']} misses {d['misses']} "
-        f"({d['hits'] / max(acc, 1):.3f} hit rate); {d['bytes_h2d'] / dt / 1e9:.2f} GB/s host->HBM")
+    log(f"[bench] {tok_s:.1f} tok/s; timed tokens: hits {d['hits']} misses {d['misses']} "
+        f"({d['hits'] / max(acc, 1):.4f} hit rate); all {warmup + steps} tokens: "
+        f"{d_all['hits'] / max(acc_all, 1):.4f} hit rate, {d_all['misses']} misses; "
+        f"{d['bytes_h2d'] / dt / 1e9:.2f} GB/s host->HBM")
     if path:
         log(f"[bench] file reads: {d['bytes_read'] / 1e9:.2f} GB in {d['read_ns'] / 1e9:.3f} s "
             f"({d['read_ns'] / 1e3 / max(d['misses'], 1):.0f} us per miss)")
+    # the same tokens again after a flush (every expert a miss on first use):
+    # outputs must equal those of the timed run, mostly served by hits, bit for bit
+    nchk = min(8, steps)
+    m.slotpool_flush(pool)
+    sf = m.slotpool_get_stats(pool)
+    Y2 = torch.empty((nchk, cfg.hidden), dtype=torch.int16, device="cuda")
+    for i in range(nchk):
+        m.moe_stack_forward(stack, X[warmup + i:warmup + i + 1], y_last=Y2[i:i + 1],
+                            stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    s2 = m.slotpool_get_stats(pool)
+    same = bool(torch.equal(Y2, Y[warmup:warmup + nchk]))
+    log(f"[bench] tokens {warmup}..{warmup + nchk - 1} rerun from a flushed pool "
+        f"({s2['misses'] - sf['misses']} misses): outputs bitwise equal: {same}")
     out = {"metric": "MoE stack tokens/sec, batch-1 decode with expert streaming (30% HBM pool), 1 GPU",
            "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
            "ms_per_step": dt / steps * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -502,9 +525,16 @@ def bench_stream(args, cfg):
            "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden {cfg.hidden}, "
                                   f"{cfg.experts} experts top-{cfg.top_k}, int{cfg.bits}, slot pool "
                                   f"{cap} = floor({cfg.pool_frac} x L x E), pool starts empty",
+                      "tokens": warmup + steps, "warmup_tokens": warmup,
                       "pool_hits": d["hits"], "pool_misses": d["misses"],
                       "pool_evictions": d["evictions"], "hit_rate": d["hits"] / max(acc, 1),
-                      "bytes_h2d": d["bytes_h2d"], "h2d_GBps": d["bytes_h2d"] / dt / 1e9}}
+                      "hit_rate_all_tokens": d_all["hits"] / max(acc_all, 1),
+                      "misses_all_tokens": d_all["misses"],
+                      "evictions_all_tokens": d_all["evictions"],
+                      "bytes_h2d": d["bytes_h2d"], "h2d_GBps": d["bytes_h2d"] / dt / 1e9,
+                      "flushed_rerun_tokens": nchk,
+                      "flushed_rerun_misses": s2["misses"] - sf["misses"],
+                      "flushed_rerun_bitwise_equal": same}}
     if path:
         out["metric"] = out["metric"].replace("expert streaming", "expert streaming from a file")
         out["config"]["store"] = m.STORE_KINDS[m.expert_store_kind(store)]
