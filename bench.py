@@ -421,25 +421,28 @@ def bench_decode_other(args, cfg):
     import torch
     import int4_group_quantized_router_amd as m
     from moe_inputs import tokens_x
-    steps = 64 if args.steps is None else args.steps
     warmup = 8 if args.warmup is None else args.warmup
+    # default: the workload's tokens one at a time, then 64 steps of 8 tokens
+    steps_of = {1: max(1, cfg.tokens - warmup) if args.steps is None else args.steps,
+                8: 64 if args.steps is None else args.steps}
     torch.cuda.set_device(0)
     log(f"[bench] building {cfg.name}: {cfg.layers} layers x {cfg.experts} experts, int{cfg.bits}")
     layers, stack, keep = _build_stack(cfg)
     ab = algorithmic_bytes(cfg)
     res = {}
     for T in (1, 8):
+        steps = steps_of[T]
         n = (warmup + steps) * T
         X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
         Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
         dt = _run_tokens(m, stack, X, Y, T, warmup, steps)
-        res[T] = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3,
+        res[T] = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3, "steps": steps,
                   "path": ("persistent stack kernel" if T == 1 and m.moe_stack_persistent_active(stack)
                            else "per-layer kernels")}
         log(f"[bench] T={T}: {res[T]['tokens_per_s']:.1f} tok/s ({res[T]['path']})")
     per_token = ab["layer"] * cfg.layers
     out = {"metric": f"MoE stack tokens/sec at batch 1 and 8, int{cfg.bits} experts, 1 GPU",
-           "value": res[1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "value": res[1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps_of[1],
            "warmup": warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": f"int{cfg.bits} weights, f32 accumulate, bf16 I/O",
            "data": "synthetic (seeded; random-init weights of the stated shape)",
