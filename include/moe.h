@@ -247,7 +247,9 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts,
                          int32_t n, hipStream_t compute, const void** slot_ptrs,
                          uint8_t* was_miss);
 /* Unpin; records on `compute` the event a later refill of these slots
- * waits for. */
+ * waits for.  Calls may use different compute streams: a release on a
+ * stream other than the previous release's first makes that stream wait
+ * for the previous release. */
 int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts,
                          int32_t n, hipStream_t compute);
 /* Drop (layer, expert) if resident.  MOE_E_BUSY if pinned. */

@@ -122,6 +122,8 @@ struct slotpool {
   std::set<int32_t> free_slots;
   std::vector<hipEvent_t> ring;                // release events, reused round-robin
   size_t ring_next = 0;
+  hipStream_t release_stream = nullptr;        // stream of the most recent release
+  hipEvent_t release_event = nullptr;          // and the event it recorded
   std::vector<uint8_t*> stage;                 // file store: pinned staging buffers
   std::vector<hipEvent_t> stage_done;          // copy out of stage[i] finished
   std::vector<bool> stage_used;
@@ -546,9 +548,17 @@ int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts, 
   if (n == 0) return MOE_OK;
   hipEvent_t ev = pool->ring[pool->ring_next];
   pool->ring_next = (pool->ring_next + 1) % pool->ring.size();
-  // A re-recorded ring event marks a later point of the same stream, so a
-  // slot still holding it only waits longer: ordering stays safe.
+  // A slot may still hold a ring event that is re-recorded here.  That is
+  // safe while every release comes from one stream: the event then marks a
+  // later point of the same stream and a refill only waits longer.  When
+  // the caller switches streams, the new stream first waits for the old
+  // stream's last release, so every later release point is also after
+  // every read released before it, whichever stream made it.
+  if (pool->release_event && compute != pool->release_stream)
+    MOE_HIP_TRY(hipStreamWaitEvent(compute, pool->release_event, 0));
   MOE_HIP_TRY(hipEventRecord(ev, compute));
+  pool->release_stream = compute;
+  pool->release_event = ev;
   for (int i = 0; i < n; ++i) {
     auto it = pool->where.find(pool->key(layer, experts[i]));
     if (it == pool->where.end()) continue;

@@ -494,6 +494,48 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
         m.expert_store_destroy(store)
 
 
+def test_pool_shared_by_two_streams_bitwise(torch):
+    """Two pooled layers on two compute streams share one small pool (every
+    few calls evict a slot the other stream read last): results equal the
+    resident layers bit for bit, with no synchronisation between calls."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS["tiny"].replace(layers=2)
+    _print("pool shared by two streams", cfg.name)
+    dm = DeviceModel(cfg)
+    store, _ = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    pool = m.slotpool_create(store, 3, 0)
+    res_layers = dm.make_layers()
+    pool_layers = dm.make_layers(pool=pool)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    H, n_tok = cfg.hidden, 12
+    try:
+        xs = [torch.from_numpy(token_x(cfg, t).view(np.int16)).cuda().view(1, H) for t in range(n_tok)]
+        torch.cuda.synchronize()
+        outs = {}
+        for t in range(n_tok):
+            for l in range(cfg.layers):
+                st = streams[l]
+                with torch.cuda.stream(st):
+                    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+                    m.moe_layer_forward(pool_layers[l], xs[t], None, y, stream=st)
+                outs[(t, l)] = y
+        torch.cuda.synchronize()
+        for t in range(n_tok):
+            for l in range(cfg.layers):
+                want = torch.empty((1, H), dtype=torch.float32, device="cuda")
+                m.moe_layer_forward(res_layers[l], xs[t], None, want)
+                torch.cuda.synchronize()
+                assert torch.equal(outs[(t, l)], want), (t, l)
+        st = m.slotpool_get_stats(pool)
+        assert st["evictions"] > 0, st
+    finally:
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
 def test_file_store_pool_matches_resident_bitwise(torch, tmp_path):
     """Experts fetched from the container file (one pread per miss into
     pinned staging, then the copy to the slot) give exactly the resident
