@@ -383,6 +383,55 @@ def test_stack_teacher_forced(torch):
         dm.destroy()
 
 
+def test_stack_full_depth_sampled(torch):
+    """The 35B-shaped stack at its full depth (40 layers), in the launch the
+    bench times (one persistent kernel per token): for two sampled tokens,
+    every layer's output against the oracle on the GPU's own input to that
+    layer, the rescale chain to one bf16 ulp, and the per-layer kernels
+    giving the same bits."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["decode35b"]
+    _print("stack full depth", cfg.name, cfg.layers)
+    dm = DeviceModel(cfg)
+    layers = dm.make_layers()
+    st = m.moe_stack_create(layers)
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    try:
+        for tok in (0, 131):
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            outs = []
+            for persistent in (True, False):
+                m.moe_stack_set_persistent(st, persistent)
+                assert m.moe_stack_persistent_active(st) == persistent
+                xl = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+                yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                ylast = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx)
+                torch.cuda.synchronize()
+                outs.append((ylast.cpu().numpy(), xl.cpu().numpy(), yl.cpu().numpy(),
+                             idx.cpu().numpy()))
+            for a, b in zip(outs[0], outs[1]):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), tok
+            ylast, xl_, yl_, ix = outs[0]
+            xl_ = xl_.view(np.uint16)
+            assert np.array_equal(xl_[0, 0], token_x(cfg, tok))
+            for l in range(L):
+                ref = oracle_layer(cfg, l, xl_[l, 0])
+                Wr, rb, _ = router_arrays(cfg, l)
+                check_routing(ix[l, 0], None, O.bf16_to_f64(xl_[l, 0]), Wr, rb, k)
+                if np.array_equal(ix[l, 0], ref["idx"]):
+                    assert rel_err(yl_[l, 0], ref["y"]) <= REL_TOL, (tok, l)
+                if l + 1 < L:
+                    nxt = O.rms_rescale(yl_[l, 0])
+                    diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
+                    assert diff.max() <= 1, (tok, l)
+            check_bf16_of_f32(ylast, yl_[L - 1])
+    finally:
+        m.moe_stack_set_persistent(st, True)
+        m.moe_stack_destroy(st)
+        dm.destroy()
+
+
 @pytest.mark.parametrize("name,L", [("tiny", 3), ("decode35b", 6), ("stream80b", 2),
                                     ("decode80b_int8", 2)])
 def test_stack_persistent_matches_per_layer(torch, name, L):
