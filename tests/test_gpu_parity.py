@@ -383,21 +383,22 @@ def test_stack_teacher_forced(torch):
         dm.destroy()
 
 
-def test_stack_full_depth_sampled(torch):
-    """The 35B-shaped stack at its full depth (40 layers), in the launch the
-    bench times (one persistent kernel per token): for two sampled tokens,
-    every layer's output against the oracle on the GPU's own input to that
-    layer, the rescale chain to one bf16 ulp, and the per-layer kernels
-    giving the same bits."""
+@pytest.mark.parametrize("name,tokens", [("decode35b", (0, 131)), ("decode80b_int8", (7,))])
+def test_stack_full_depth_sampled(torch, name, tokens):
+    """A resident stack at its full depth (35B-shaped int4: 40 layers;
+    80B-shaped int8: 48), in the launch the bench times (one persistent
+    kernel per token): for sampled tokens, every layer's output against the
+    oracle on the GPU's own input to that layer, the rescale chain to one
+    bf16 ulp, and the per-layer kernels giving the same bits."""
     import int4_group_quantized_router_amd as m
-    cfg = CONFIGS["decode35b"]
+    cfg = CONFIGS[name]
     _print("stack full depth", cfg.name, cfg.layers)
     dm = DeviceModel(cfg)
     layers = dm.make_layers()
     st = m.moe_stack_create(layers)
     H, k, L = cfg.hidden, cfg.top_k, cfg.layers
     try:
-        for tok in (0, 131):
+        for tok in tokens:
             x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
             outs = []
             for persistent in (True, False):
