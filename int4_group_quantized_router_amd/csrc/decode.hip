@@ -42,15 +42,21 @@ using namespace dev;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-__device__ __forceinline__ const uint8_t* slot_blob(const DecodeArgs& a, int s) {
+__device__ __forceinline__ const uint8_t* slot_blob(const DecodeArgs& a, const SlotArgs& sa,
+                                                    int s) {
   if (a.routed_base) return a.routed_base + (int64_t)a.slot_expert[s] * a.stride;
-  return a.slot_ptrs[s];
+  if (a.slot_ptrs) return a.slot_ptrs[s];
+  // select rather than index, so the argument block stays in registers
+  const uint8_t* p = sa.p[0];
+#pragma unroll
+  for (int i = 1; i < kSlotArgs; ++i) p = s == i ? sa.p[i] : p;
+  return p;
 }
 
 // ---------------------------------------------------------------- gate/up
 
 template <int BITS, int NT, int CPL, int PASSES>
-__global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a, SlotArgs sa) {
   using F = Fmt<BITS>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H;
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a) {
     }
   }
 
-  if (!shared) blob = slot_blob(a, slot);
+  if (!shared) blob = slot_blob(a, sa, slot);
   // weights for all passes: PASSES x 2 x CPL 16-byte loads in flight per lane
   uint4 q[2][PASSES][CPL];
   uint32_t sb[2][PASSES][CPL];
@@ -161,7 +167,7 @@ constexpr int kDownThreads = 1024;
 constexpr int kDownWaves = kDownThreads / kWave;
 
 template <int BITS, int NT, int BATCH>
-__global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, int R) {
+__global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, SlotArgs sa, int R) {
   using F = Fmt<BITS>;
   extern __shared__ __align__(16) uint8_t smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, int R)
       if (it < n_routed * NRPr) {
         slot[bi] = it / NRPr;
         rp = it % NRPr;
-        blob = slot_blob(a, slot[bi]);
+        blob = slot_blob(a, sa, slot[bi]);
         L = a.lr;
         C = Cr;
         RPP = RPPr;
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, int R)
 // workgroup's R output rows for each of its slots; partial row sums meet in
 // LDS and one thread per row combines them in j order, then the shared term.
 template <int BITS, int SPW, int NPMAX>
-__global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a, SlotArgs sa) {
   using F = Fmt<BITS>;
   constexpr int R = 8;
   __shared__ float part[(kWaves * SPW) * R];
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a) {
     const int s = wave + kWaves * si;
     if (s >= nsl) continue;
     const bool sh = s == k;
-    const uint8_t* blob = sh ? a.shared_blob : slot_blob(a, s);
+    const uint8_t* blob = sh ? a.shared_blob : slot_blob(a, sa, s);
     const QLayout L = sh ? a.ls : a.lr;
     const int inner = sh ? a.Is : a.I;
     const int ci = lane % C[si], RPP = kWave / C[si];
@@ -441,7 +447,7 @@ int chunks_per_lane(int H, int bits) {
 }
 
 template <int BITS, int NT>
-hipError_t gate_up_bits_nt(const DecodeArgs& a, hipStream_t s) {
+hipError_t gate_up_bits_nt(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
   const int cpl = chunks_per_lane(a.H, BITS);
   const int C = a.H / Fmt<BITS>::kEpc;
   const int rpp = kWave / (C / cpl);
@@ -452,7 +458,7 @@ hipError_t gate_up_bits_nt(const DecodeArgs& a, hipStream_t s) {
 #define MOE_GU_CASE(CP)                                                                 \
   if (cpl == CP) {                                                                      \
     hipLaunchKernelGGL((gate_up_kernel<BITS, NT, CP, kGuPasses>), dim3(blocks),         \
-                       dim3(kThreads), 0, s, a);                                        \
+                       dim3(kThreads), 0, s, a, sa);                                        \
     return hipGetLastError();                                                           \
   }
   MOE_GU_CASE(1)
@@ -462,33 +468,33 @@ hipError_t gate_up_bits_nt(const DecodeArgs& a, hipStream_t s) {
 }
 
 template <int BITS, int SPW, int NPMAX>
-hipError_t down1_launch(const DecodeArgs& a, hipStream_t s) {
+hipError_t down1_launch(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
   const int blocks = (a.H + 7) / 8;
-  hipLaunchKernelGGL((down1_kernel<BITS, SPW, NPMAX>), dim3(blocks), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((down1_kernel<BITS, SPW, NPMAX>), dim3(blocks), dim3(kThreads), 0, s, a, sa);
   return hipGetLastError();
 }
 
 template <int BITS, int SPW>
-hipError_t down1_spw(const DecodeArgs& a, hipStream_t s) {
+hipError_t down1_spw(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
   // row passes needed for 8 rows: 8 / (64 / chunks per row)
   const int cmax = std::max(a.I, a.shared_blob ? a.Is : 0) / Fmt<BITS>::kEpc;
   const int np = (8 * cmax + kWave - 1) / kWave;
-  if (np <= 2) return down1_launch<BITS, SPW, 2>(a, s);
-  if (np <= 4) return down1_launch<BITS, SPW, 4>(a, s);
-  return down1_launch<BITS, SPW, 8>(a, s);
+  if (np <= 2) return down1_launch<BITS, SPW, 2>(a, s, sa);
+  if (np <= 4) return down1_launch<BITS, SPW, 4>(a, s, sa);
+  return down1_launch<BITS, SPW, 8>(a, s, sa);
 }
 
 template <int BITS>
-hipError_t down1_bits(const DecodeArgs& a, hipStream_t s) {
+hipError_t down1_bits(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
   const int nsl = a.k + (a.shared_blob ? 1 : 0);
-  if (nsl <= 4) return down1_spw<BITS, 1>(a, s);
-  if (nsl <= 8) return down1_spw<BITS, 2>(a, s);
-  if (nsl <= 12) return down1_spw<BITS, 3>(a, s);
-  return down1_spw<BITS, 5>(a, s);
+  if (nsl <= 4) return down1_spw<BITS, 1>(a, s, sa);
+  if (nsl <= 8) return down1_spw<BITS, 2>(a, s, sa);
+  if (nsl <= 12) return down1_spw<BITS, 3>(a, s, sa);
+  return down1_spw<BITS, 5>(a, s, sa);
 }
 
 template <int BITS, int NT>
-hipError_t down_bits_nt(const DecodeArgs& a, hipStream_t s) {
+hipError_t down_bits_nt(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
   const int kp1 = a.k + 1;
   const size_t lds = (size_t)a.T * kp1 * a.hI * 2 +
                      (size_t)a.T * kp1 * (a.hI / Fmt<BITS>::kEpc) * 4 +
@@ -497,7 +503,7 @@ hipError_t down_bits_nt(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = allow_lds(down_kernel<BITS, NT, kDownBatch>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((down_kernel<BITS, NT, kDownBatch>), dim3(blocks), dim3(kDownThreads), lds,
-                     s, a, kDownRows);
+                     s, a, sa, kDownRows);
   return hipGetLastError();
 }
 
@@ -515,14 +521,14 @@ bool decode_shape_supported(int H, int I, int Is, int bits) {
   return true;
 }
 
-hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s) {
-  if (a.bits == 4) return a.T <= 1 ? gate_up_bits_nt<4, 1>(a, s) : gate_up_bits_nt<4, 8>(a, s);
-  return a.T <= 1 ? gate_up_bits_nt<8, 1>(a, s) : gate_up_bits_nt<8, 8>(a, s);
+hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
+  if (a.bits == 4) return a.T <= 1 ? gate_up_bits_nt<4, 1>(a, s, sa) : gate_up_bits_nt<4, 8>(a, s, sa);
+  return a.T <= 1 ? gate_up_bits_nt<8, 1>(a, s, sa) : gate_up_bits_nt<8, 8>(a, s, sa);
 }
 
-hipError_t launch_down(const DecodeArgs& a, hipStream_t s) {
-  if (a.T <= 1) return a.bits == 4 ? down1_bits<4>(a, s) : down1_bits<8>(a, s);
-  return a.bits == 4 ? down_bits_nt<4, 8>(a, s) : down_bits_nt<8, 8>(a, s);
+hipError_t launch_down(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa) {
+  if (a.T <= 1) return a.bits == 4 ? down1_bits<4>(a, s, sa) : down1_bits<8>(a, s, sa);
+  return a.bits == 4 ? down_bits_nt<4, 8>(a, s, sa) : down_bits_nt<8, 8>(a, s, sa);
 }
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols, int bits,

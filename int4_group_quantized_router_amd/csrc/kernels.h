@@ -53,6 +53,15 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 hipError_t launch_topk_only(const RouteArgs& a, hipStream_t s);  // logits already written
 
 // Decode (T <= 8) expert kernels.
+// Pool-mode blob addresses travel in the kernel arguments when a call has
+// at most this many distinct experts (one token with k <= 16), else in a
+// device table.  A separate argument block, so that DecodeArgs stays small
+// enough to live in registers.
+constexpr int kSlotArgs = 16;
+struct SlotArgs {
+  const uint8_t* p[kSlotArgs];
+};
+
 struct DecodeArgs {
   const uint16_t* x;          // bf16 [T,H] layer input
   int T, H, I, Is, k, bits;
@@ -65,7 +74,8 @@ struct DecodeArgs {
   const int32_t* slot_expert; // device [n_slot_max]
   const int8_t* jmap;         // device [n_slot_max][kJmapStride]
   const uint8_t* const* slot_ptrs;  // device [n_slot_max]: blob address per slot
-                                    // when routed_base is NULL (pool mode)
+                                    // when routed_base is NULL (pool mode), or
+                                    // NULL: then the SlotArgs hold them
   uint16_t* h;                // bf16 [T][k+1][hI], down-kernel order
   int hI;                     // max(I, Is)
   const float* w;             // [T,k] routing weights
@@ -75,8 +85,8 @@ struct DecodeArgs {
   int accumulate;             // y = y_f32_in + ... (y_f32 required)
 };
 
-hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_down(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa = SlotArgs{});
+hipError_t launch_down(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa = SlotArgs{});
 bool decode_shape_supported(int H, int I, int Is, int bits);
 
 // Many-token (prefill) path: sort (token, choice) pairs by expert, grouped

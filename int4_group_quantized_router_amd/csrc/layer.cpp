@@ -192,6 +192,7 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
   d.accumulate = 0;
 
   std::vector<int32_t> experts;
+  SlotArgs sa{};
   if (L->pool) {
     // The chosen experts are needed on the host to run the pool policy: the
     // router kernel writes them to pinned memory and then the call's epoch;
@@ -222,19 +223,26 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
     int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, nullptr);
     if (st != MOE_OK) return st;
     d.routed_base = nullptr;
-    for (int i = 0; i < n; ++i) L->host_ptrs[i] = static_cast<const uint8_t*>(ptrs[i]);
-    // host_ptrs is reused next call only after that call's stream sync
-    MOE_HIP_TRY(hipMemcpyAsync(L->dev_ptrs, L->host_ptrs, sizeof(void*) * n,
-                               hipMemcpyHostToDevice, stream));
-    d.slot_ptrs = L->dev_ptrs;
+    if (n <= kSlotArgs) {
+      // few slots: their addresses go in the kernel arguments (no upload)
+      for (int i = 0; i < n; ++i) sa.p[i] = static_cast<const uint8_t*>(ptrs[i]);
+      d.slot_ptrs = nullptr;
+    } else {
+      for (int i = 0; i < n; ++i) L->host_ptrs[i] = static_cast<const uint8_t*>(ptrs[i]);
+      // host_ptrs is rewritten only after the next call's router has run,
+      // i.e. after this upload
+      MOE_HIP_TRY(hipMemcpyAsync(L->dev_ptrs, L->host_ptrs, sizeof(void*) * n,
+                                 hipMemcpyHostToDevice, stream));
+      d.slot_ptrs = L->dev_ptrs;
+    }
   } else {
     d.routed_base = L->resident_base + (int64_t)c.layer_index * c.experts * L->lay_r.stride;
   }
   timer_mark(MOE_KERNEL_GATE_UP, true, stream);
-  hipError_t e1 = launch_gate_up(d, stream);
+  hipError_t e1 = launch_gate_up(d, stream, sa);
   timer_mark(MOE_KERNEL_GATE_UP, false, stream);
   timer_mark(MOE_KERNEL_DOWN, true, stream);
-  hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream) : e1;
+  hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream, sa) : e1;
   timer_mark(MOE_KERNEL_DOWN, false, stream);
   if (L->pool) {
     int32_t st = slotpool_release(L->pool, c.layer_index, experts.data(), (int)experts.size(), stream);
