@@ -35,6 +35,12 @@ inline QLayout to_qlayout(const moe_blob_layout& l) {
   return q;
 }
 
+// Slot pool internals the layer uses (pool.cpp): the device table row of
+// `layer` ((expert) -> slot address, NULL when not resident), and the wait a
+// stream needs before a kernel on it may read that table.
+const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer);
+int32_t pool_before_lookup(slotpool* p, hipStream_t stream);
+
 }  // namespace moe
 
 #define MOE_HIP_TRY(expr)                                                        \

@@ -57,6 +57,7 @@ __device__ __forceinline__ const uint8_t* slot_blob(const DecodeArgs& a, const S
 
 template <int BITS, int NT, int CPL, int PASSES>
 __global__ __launch_bounds__(kThreads) void gate_up_kernel(DecodeArgs a, SlotArgs sa) {
+  if (a.go && *a.go == 0) return;  // pool mode: an expert is not resident
   using F = Fmt<BITS>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int H = a.H;
@@ -168,6 +169,7 @@ constexpr int kDownWaves = kDownThreads / kWave;
 
 template <int BITS, int NT, int BATCH>
 __global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, SlotArgs sa, int R) {
+  if (a.go && *a.go == 0) return;  // pool mode: an expert is not resident
   using F = Fmt<BITS>;
   extern __shared__ __align__(16) uint8_t smem[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -312,6 +314,7 @@ __global__ __launch_bounds__(kDownThreads) void down_kernel(DecodeArgs a, SlotAr
 // LDS and one thread per row combines them in j order, then the shared term.
 template <int BITS, int SPW, int NPMAX>
 __global__ __launch_bounds__(kThreads) void down1_kernel(DecodeArgs a, SlotArgs sa) {
+  if (a.go && *a.go == 0) return;  // pool mode: an expert is not resident
   using F = Fmt<BITS>;
   constexpr int R = 8;
   __shared__ float part[(kWaves * SPW) * R];

@@ -33,6 +33,13 @@ struct RouteArgs {
   // last with system-scope release so the host may read [1..] once it sees it
   int32_t* host_list;
   int32_t host_epoch;
+  // pool mode: the layer's row of the pool's device table (expert -> slot
+  // address or NULL); the router then writes slot_addr[s] for every slot and
+  // *go = 1 when all are resident, else 0 (also to host_list[2 + T*k]), or
+  // NULL to skip
+  const uint8_t* const* res_tab;
+  const uint8_t** slot_addr;  // [T*k]
+  int32_t* go;                // [1]
   // top-k over MFMA partial sums (launch_topk_only): logits = sum of
   // part[0..ksplit) in order + rb, written to `logits` when that is not
   // NULL; the shared gate is then sigmoid(x . wsg) computed per token here
@@ -83,6 +90,7 @@ struct DecodeArgs {
   float* y_f32;               // [T,H] or NULL
   uint16_t* y_bf16;           // [T,H] or NULL
   int accumulate;             // y = y_f32_in + ... (y_f32 required)
+  const int32_t* go;          // device [1]: run only if *go != 0; NULL: always run
 };
 
 hipError_t launch_gate_up(const DecodeArgs& a, hipStream_t s, const SlotArgs& sa = SlotArgs{});

@@ -159,9 +159,16 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
   r.n_slots = L->slots;
   r.slot_expert = L->slots + 1;
   r.jmap = L->jmap;
+  int32_t* go = L->slots + 1 + MOE_MAX_DECODE_T * c.top_k;  // device flag
   if (L->pool) {
     r.host_list = L->host_slots;
     r.host_epoch = L->list_epoch = L->list_epoch == 0x7fffffff ? 1 : L->list_epoch + 1;
+    // the router looks the chosen experts up in the pool's device table
+    int32_t st = pool_before_lookup(L->pool, stream);
+    if (st != MOE_OK) return st;
+    r.res_tab = pool_device_table(L->pool, c.layer_index);
+    r.slot_addr = L->dev_ptrs;
+    r.go = go;
   }
   timer_mark(MOE_KERNEL_ROUTE, true, stream);
   MOE_HIP_TRY(launch_route(r, stream));
@@ -191,38 +198,79 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
   d.y_bf16 = y_bf16;
   d.accumulate = 0;
 
-  std::vector<int32_t> experts;
-  SlotArgs sa{};
-  if (L->pool) {
-    // The chosen experts are needed on the host to run the pool policy: the
-    // router kernel writes them to pinned memory and then the call's epoch;
-    // the host waits for the epoch (no stream synchronisation: the router
-    // has not finished when the list is complete).  Everything enqueued
-    // before the router, including the previous call's pointer upload, has
-    // run by then, so host_ptrs may be rewritten below.
-    const int32_t want = L->list_epoch;
-    const auto t_start = std::chrono::steady_clock::now();
-    volatile int32_t* flag = L->host_slots;
-    int spins = 0;
-    while (*flag != want) {
-      if (++spins % 1024 == 0) {
-        const hipError_t q = hipStreamQuery(stream);
-        if (q != hipSuccess && q != hipErrorNotReady)
-          return fail(MOE_E_HIP, "router failed: %s", hipGetErrorString(q));
-        if (q == hipSuccess && *flag != want)
-          return fail(MOE_E_HIP, "router finished without publishing its expert list");
-        if (std::chrono::steady_clock::now() - t_start > std::chrono::seconds(10))
-          return fail(MOE_E_HIP, "timed out waiting for the router's expert list");
-      }
+  if (!L->pool) {
+    d.routed_base = L->resident_base + (int64_t)c.layer_index * c.experts * L->lay_r.stride;
+    timer_mark(MOE_KERNEL_GATE_UP, true, stream);
+    hipError_t e1 = launch_gate_up(d, stream);
+    timer_mark(MOE_KERNEL_GATE_UP, false, stream);
+    timer_mark(MOE_KERNEL_DOWN, true, stream);
+    hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream) : e1;
+    timer_mark(MOE_KERNEL_DOWN, false, stream);
+    MOE_HIP_TRY(e2);
+    return MOE_OK;
+  }
+
+  // Pool: the expert kernels are enqueued right behind the router, reading
+  // the slot addresses the router found in the pool's device table; they
+  // run only if every chosen expert was resident (*go).  Meanwhile the host
+  // waits for the router's expert list and runs the pool policy on it; if
+  // an expert was missing, the kernels above did nothing, and after the
+  // misses are filled they are enqueued again with the acquired addresses.
+  d.routed_base = nullptr;
+  {
+    DecodeArgs ds = d;
+    ds.slot_ptrs = L->dev_ptrs;
+    ds.go = go;
+    timer_mark(MOE_KERNEL_GATE_UP, true, stream);
+    hipError_t e1 = launch_gate_up(ds, stream);
+    timer_mark(MOE_KERNEL_GATE_UP, false, stream);
+    timer_mark(MOE_KERNEL_DOWN, true, stream);
+    hipError_t e2 = e1 == hipSuccess ? launch_down(ds, stream) : e1;
+    timer_mark(MOE_KERNEL_DOWN, false, stream);
+    MOE_HIP_TRY(e2);
+  }
+  // The chosen experts are needed on the host to run the pool policy: the
+  // router kernel writes them to pinned memory and then the call's epoch;
+  // the host waits for the epoch (no stream synchronisation: the router
+  // has not finished when the list is complete).
+  const int32_t want = L->list_epoch;
+  const auto t_start = std::chrono::steady_clock::now();
+  volatile int32_t* flag = L->host_slots;
+  int spins = 0;
+  while (*flag != want) {
+    // the stream is queried only once the wait is long (a query costs
+    // microseconds and would delay noticing the list)
+    if (++spins % 1024 == 0 &&
+        std::chrono::steady_clock::now() - t_start > std::chrono::microseconds(500)) {
+      const hipError_t q = hipStreamQuery(stream);
+      if (q != hipSuccess && q != hipErrorNotReady)
+        return fail(MOE_E_HIP, "router failed: %s", hipGetErrorString(q));
+      if (q == hipSuccess && *flag != want)
+        return fail(MOE_E_HIP, "router finished without publishing its expert list");
+      if (std::chrono::steady_clock::now() - t_start > std::chrono::seconds(10))
+        return fail(MOE_E_HIP, "timed out waiting for the router's expert list");
     }
-    std::atomic_thread_fence(std::memory_order_acquire);
-    const int n = L->host_slots[1];
-    if (n < 0 || n > T * c.top_k) return fail(MOE_E_HIP, "router produced %d slots", n);
-    experts.assign(L->host_slots + 2, L->host_slots + 2 + n);
-    const void* ptrs[kMaxSlots];
-    int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, nullptr);
-    if (st != MOE_OK) return st;
-    d.routed_base = nullptr;
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  const int n = L->host_slots[1];
+  if (n < 0 || n > T * c.top_k) return fail(MOE_E_HIP, "router produced %d slots", n);
+  const bool dev_all_resident = L->host_slots[2 + T * c.top_k] != 0;
+  std::vector<int32_t> experts(L->host_slots + 2, L->host_slots + 2 + n);
+  const void* ptrs[kMaxSlots];
+  uint8_t was_miss[kMaxSlots];
+  int32_t st = slotpool_acquire(L->pool, c.layer_index, experts.data(), n, stream, ptrs, was_miss);
+  if (st != MOE_OK) return st;
+  bool any_miss = false;
+  for (int i = 0; i < n; ++i) any_miss = any_miss || was_miss[i];
+  if (dev_all_resident && any_miss) {
+    // cannot happen: the table changes only inside calls on the pool, in
+    // stream order with the kernels that read it
+    (void)slotpool_release(L->pool, c.layer_index, experts.data(), n, stream);
+    return fail(MOE_E_HIP, "pool table found an expert resident that the pool had not");
+  }
+  hipError_t e2 = hipSuccess;
+  if (!dev_all_resident) {
+    SlotArgs sa{};
     if (n <= kSlotArgs) {
       // few slots: their addresses go in the kernel arguments (no upload)
       for (int i = 0; i < n; ++i) sa.p[i] = static_cast<const uint8_t*>(ptrs[i]);
@@ -231,23 +279,15 @@ int32_t forward_decode(moe_layer* L, const uint16_t* x, const float* y_prev, uin
       for (int i = 0; i < n; ++i) L->host_ptrs[i] = static_cast<const uint8_t*>(ptrs[i]);
       // host_ptrs is rewritten only after the next call's router has run,
       // i.e. after this upload
-      MOE_HIP_TRY(hipMemcpyAsync(L->dev_ptrs, L->host_ptrs, sizeof(void*) * n,
-                                 hipMemcpyHostToDevice, stream));
+      e2 = hipMemcpyAsync(L->dev_ptrs, L->host_ptrs, sizeof(void*) * n, hipMemcpyHostToDevice,
+                          stream);
       d.slot_ptrs = L->dev_ptrs;
     }
-  } else {
-    d.routed_base = L->resident_base + (int64_t)c.layer_index * c.experts * L->lay_r.stride;
+    if (e2 == hipSuccess) e2 = launch_gate_up(d, stream, sa);
+    if (e2 == hipSuccess) e2 = launch_down(d, stream, sa);
   }
-  timer_mark(MOE_KERNEL_GATE_UP, true, stream);
-  hipError_t e1 = launch_gate_up(d, stream, sa);
-  timer_mark(MOE_KERNEL_GATE_UP, false, stream);
-  timer_mark(MOE_KERNEL_DOWN, true, stream);
-  hipError_t e2 = e1 == hipSuccess ? launch_down(d, stream, sa) : e1;
-  timer_mark(MOE_KERNEL_DOWN, false, stream);
-  if (L->pool) {
-    int32_t st = slotpool_release(L->pool, c.layer_index, experts.data(), (int)experts.size(), stream);
-    if (st != MOE_OK) return st;
-  }
+  st = slotpool_release(L->pool, c.layer_index, experts.data(), n, stream);
+  if (st != MOE_OK) return st;
   MOE_HIP_TRY(e2);
   return MOE_OK;
 }
@@ -663,7 +703,7 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
       (size_t)T * k * 4,                 // w
       (size_t)T * 4,                     // sigma
       4,                                 // counter
-      (size_t)(1 + T * k) * 4,           // slots
+      (size_t)(2 + T * k) * 4,           // slots: count, experts, go flag
       (size_t)T * k * kJmapStride,       // jmap
       (size_t)T * H * 2,                 // x_cur
       (size_t)T * (k + 1) * L->hI * 2,   // h
@@ -696,9 +736,9 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
   L->dev_ptrs = static_cast<const uint8_t**>(parts[10]);
   he = hipMemset(L->ws, 0, total);
   if (he == hipSuccess && pool) {
-    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (2 + T * k) * sizeof(int32_t),
+    he = hipHostMalloc(reinterpret_cast<void**>(&L->host_slots), (3 + T * k) * sizeof(int32_t),
                        hipHostMallocDefault);
-    if (he == hipSuccess) std::memset(L->host_slots, 0, (2 + T * k) * sizeof(int32_t));
+    if (he == hipSuccess) std::memset(L->host_slots, 0, (3 + T * k) * sizeof(int32_t));
     L->list_epoch = 0;  // the first call publishes epoch 1
   }
   if (he == hipSuccess && pool)

@@ -25,6 +25,12 @@
 // staging buffers; a buffered read goes straight into the staging buffer.
 // Each staging buffer is reused only after the host-to-device copy from it
 // has finished.
+// The pool also keeps a device table (layer, expert) -> slot address (NULL
+// when not resident) so that kernels can find resident experts without the
+// host.  The host changes a pinned mirror of it and, at the end of each call
+// that changed entries, copies those entries on the copy stream after the
+// fills; the compute stream waits for that, so a kernel enqueued after the
+// call never sees an address before its blob has landed, nor an evicted one.
 #include <fcntl.h>
 #include <sys/stat.h>
 #include <unistd.h>
@@ -124,6 +130,12 @@ struct slotpool {
   size_t ring_next = 0;
   hipStream_t release_stream = nullptr;        // stream of the most recent release
   hipEvent_t release_event = nullptr;          // and the event it recorded
+  const uint8_t** tab_dev = nullptr;           // device [L*E]: slot address or NULL
+  const uint8_t** tab_host = nullptr;          // pinned mirror of tab_dev
+  std::vector<int64_t> tab_changed;            // keys changed since the last push
+  hipEvent_t tab_ready = nullptr;              // recorded after the last push
+  bool tab_pushed = false;                     // tab_ready has been recorded
+  hipStream_t tab_stream = nullptr;            // last stream made to wait on tab_ready
   std::vector<uint8_t*> stage;                 // file store: pinned staging buffers
   std::vector<hipEvent_t> stage_done;          // copy out of stage[i] finished
   std::vector<bool> stage_used;
@@ -159,13 +171,55 @@ void unpin(slotpool* p, int32_t s) {
 void drop(slotpool* p, int32_t s) {
   Slot& x = p->slots[s];
   p->victims.erase(p->vkey(s));
-  p->where.erase(p->key(x.layer, x.expert));
+  const int64_t key = p->key(x.layer, x.expert);
+  p->where.erase(key);
+  if (p->tab_host) {
+    p->tab_host[key] = nullptr;
+    p->tab_changed.push_back(key);
+  }
   x.layer = x.expert = -1;
   x.count = x.last = 0;
   p->free_slots.insert(s);
 }
 
+// Copy the table entries changed since the last push (after everything
+// already on the copy stream, i.e. after the fills they describe) and make
+// `compute` wait for them; with compute NULL the host waits instead.
+int32_t push_table(slotpool* p, hipStream_t compute) {
+  if (p->tab_changed.empty()) return MOE_OK;
+  for (int64_t key : p->tab_changed)
+    MOE_HIP_TRY(hipMemcpyAsync(p->tab_dev + key, p->tab_host + key, sizeof(void*),
+                               hipMemcpyHostToDevice, p->copy));
+  p->tab_changed.clear();
+  MOE_HIP_TRY(hipEventRecord(p->tab_ready, p->copy));
+  p->tab_pushed = true;
+  if (compute) {
+    MOE_HIP_TRY(hipStreamWaitEvent(compute, p->tab_ready, 0));
+    p->tab_stream = compute;
+  } else {
+    MOE_HIP_TRY(hipEventSynchronize(p->tab_ready));
+  }
+  return MOE_OK;
+}
+
 }  // namespace
+
+namespace moe {
+
+const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer) {
+  return p->tab_dev + (int64_t)layer * p->store->experts;
+}
+
+int32_t pool_before_lookup(slotpool* p, hipStream_t stream) {
+  // a stream that has not waited for the latest table push does so now
+  if (p->tab_pushed && stream != p->tab_stream) {
+    MOE_HIP_TRY(hipStreamWaitEvent(stream, p->tab_ready, 0));
+    p->tab_stream = stream;
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -352,6 +406,13 @@ int32_t slotpool_create(const expert_store* store, int64_t capacity, int32_t dev
   p->ring.resize(kEventRing, nullptr);
   for (int i = 0; i < kEventRing && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&p->ring[i], hipEventDisableTiming);
+  const size_t tab_bytes = (size_t)store->layers * store->experts * sizeof(void*);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->tab_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&p->tab_dev), tab_bytes);
+  if (e == hipSuccess) e = hipMemset(p->tab_dev, 0, tab_bytes);
+  if (e == hipSuccess)
+    e = hipHostMalloc(reinterpret_cast<void**>(&p->tab_host), tab_bytes, hipHostMallocDefault);
+  if (e == hipSuccess) std::memset(p->tab_host, 0, tab_bytes);
   if (!store->base) {
     p->bounce.resize(kStaging, nullptr);
     for (int i = 0; i < kStaging && e == hipSuccess; ++i) {
@@ -379,10 +440,12 @@ int32_t slotpool_create(const expert_store* store, int64_t capacity, int32_t dev
   return MOE_OK;
 }
 
-int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
-                         hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss) {
-  clear_error();
-  MOE_REQUIRE(pool && (n == 0 || (experts && slot_ptrs)) && n >= 0, "bad argument");
+}  // extern "C"
+
+namespace {
+
+int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
+                     hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss) {
   for (int i = 0; i < n; ++i) {
     int32_t st = check_le(pool->store, layer, experts[i]);
     if (st != MOE_OK) return st;
@@ -515,6 +578,8 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
       x.last = pool->tick;
       x.pins = 1;
       pool->where[k] = s;
+      pool->tab_host[k] = pool->dev + (int64_t)s * stride;
+      pool->tab_changed.push_back(k);
       pool->stats.misses += 1;
       miss = true;
       if (pool->store->base) {
@@ -539,6 +604,21 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
     if (was_miss) was_miss[i] = miss ? 1 : 0;
   }
   return flush();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
+                         hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss) {
+  clear_error();
+  MOE_REQUIRE(pool && (n == 0 || (experts && slot_ptrs)) && n >= 0, "bad argument");
+  const int32_t st = acquire_impl(pool, layer, experts, n, compute, slot_ptrs, was_miss);
+  // the table follows every admission and eviction of the call, also on
+  // the error paths (entries dropped there are cleared)
+  const int32_t pt = push_table(pool, compute);
+  return st != MOE_OK ? st : pt;
 }
 
 int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
@@ -579,7 +659,7 @@ int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert) {
     return fail(MOE_E_BUSY, "(layer %d, expert %d) is pinned", layer, expert);
   drop(pool, it->second);
   pool->stats.evictions += 1;
-  return MOE_OK;
+  return push_table(pool, nullptr);
 }
 
 int32_t slotpool_flush(slotpool* pool) {
@@ -590,7 +670,7 @@ int32_t slotpool_flush(slotpool* pool) {
   std::vector<int32_t> res;
   for (const auto& kv : pool->where) res.push_back(kv.second);
   for (int32_t s : res) drop(pool, s);
-  return MOE_OK;
+  return push_table(pool, nullptr);
 }
 
 int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out) {
@@ -617,6 +697,9 @@ int32_t slotpool_destroy(slotpool* pool) {
     if (x.ready) (void)hipEventDestroy(x.ready);
   for (hipEvent_t ev : pool->ring)
     if (ev) (void)hipEventDestroy(ev);
+  if (pool->tab_ready) (void)hipEventDestroy(pool->tab_ready);
+  if (pool->tab_dev) (void)hipFree(pool->tab_dev);
+  if (pool->tab_host) (void)hipHostFree(pool->tab_host);
   for (hipEvent_t ev : pool->stage_done)
     if (ev) (void)hipEventDestroy(ev);
   for (uint8_t* b : pool->stage)

@@ -226,6 +226,9 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
     }
   }
   __syncthreads();
+  __shared__ int s_miss;
+  if (threadIdx.x == 0) s_miss = 0;
+  __syncthreads();
   for (int p = threadIdx.x; p < n; p += THR) {
     const int e = s_sel[p];
     const int slot = s_slot[s_first[e]];
@@ -233,6 +236,19 @@ __device__ void build_slots(const RouteArgs& a, const int* s_sel, int* s_first, 
     if (s_first[e] == p) {
       a.slot_expert[slot] = e;
       if (a.host_list) a.host_list[2 + slot] = e;
+      if (a.res_tab) {
+        const uint8_t* addr = a.res_tab[e];
+        a.slot_addr[slot] = addr;
+        if (!addr) s_miss = 1;
+      }
+    }
+  }
+  if (a.res_tab) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int go = s_miss ? 0 : 1;
+      *a.go = go;
+      if (a.host_list) a.host_list[2 + n] = go;
     }
   }
   if (a.host_list) {
