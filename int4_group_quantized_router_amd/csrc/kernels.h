@@ -47,11 +47,11 @@ struct RouteArgs {
   int ksplit;
 };
 
-// Kernels whose LDS (dynamic `bytes` plus up to 8 KiB static) may exceed
+// Kernels whose LDS (dynamic `bytes` plus up to 16 KiB static) may exceed
 // 64 KiB opt in to more dynamic LDS (gfx950 has 160 KiB per workgroup).
 template <typename Kernel>
 inline hipError_t allow_lds(Kernel kernel, size_t bytes) {
-  if (bytes + 8192 <= 65536) return hipSuccess;
+  if (bytes + 16384 <= 65536) return hipSuccess;
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
