@@ -220,6 +220,13 @@ int32_t expert_store_drop_cache(expert_store* store);
  * compute stream waits for the copy (read-after-write) -- [lens]
  * "TurboFieldfareとの関係": explicit hazard management.  The policy decides
  * hits only; results never depend on it.
+ *
+ * The pool also keeps a device table (layer, expert) -> slot address, NULL
+ * when not resident, that the layer's router kernel reads; it is updated on
+ * the copy stream after the fills of each acquire that changes it, and the
+ * compute stream waits for the update, so kernels enqueued after a call see
+ * the table as that call left it.  Evict and flush update it before they
+ * return.
  * ---------------------------------------------------------------------- */
 typedef struct slotpool slotpool;
 
@@ -298,9 +305,13 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr,
  * device f32 [T, k] or NULL.  T == 0 returns MOE_OK and touches nothing
  * (x and y_bf16 may then be NULL); 1 <= T <= MOE_MAX_DECODE_T takes the
  * per-token GEMV path; larger T takes the sorted grouped-GEMM path.  With a
- * pool, the call needs the chosen experts on the host: the router kernel
- * publishes them to pinned host memory and the calling thread waits for
- * them before it acquires slots (one host round trip per call). */
+ * pool (GEMV path), the router kernel looks the chosen experts up in the
+ * pool's device table and the expert kernels, enqueued right behind it, run
+ * only if all of them are resident; the router also publishes its expert
+ * list to pinned host memory, and the calling thread waits for it, runs the
+ * pool policy (slotpool_acquire / _release on the call's stream) and, after
+ * a miss, enqueues the expert kernels again once the misses are filled.
+ * One host round trip per call; the outputs never depend on hit or miss. */
 int32_t moe_layer_forward(moe_layer* layer, const uint16_t* x, int32_t T,
                           uint16_t* y_bf16, float* y_f32, int32_t* idx_out,
                           float* w_out, hipStream_t stream);
