@@ -187,9 +187,20 @@ void drop(slotpool* p, int32_t s) {
 // `compute` wait for them; with compute NULL the host waits instead.
 int32_t push_table(slotpool* p, hipStream_t compute) {
   if (p->tab_changed.empty()) return MOE_OK;
-  for (int64_t key : p->tab_changed)
-    MOE_HIP_TRY(hipMemcpyAsync(p->tab_dev + key, p->tab_host + key, sizeof(void*),
-                               hipMemcpyHostToDevice, p->copy));
+  // one copy per changed entry when few changed, else one per touched layer
+  // row (the mirror row as it is now: later values only move it forward)
+  const int64_t E = p->store->experts;
+  std::set<int64_t> rows;
+  for (int64_t key : p->tab_changed) rows.insert(key / E);
+  if ((int64_t)p->tab_changed.size() <= (int64_t)rows.size() * 2) {
+    for (int64_t key : p->tab_changed)
+      MOE_HIP_TRY(hipMemcpyAsync(p->tab_dev + key, p->tab_host + key, sizeof(void*),
+                                 hipMemcpyHostToDevice, p->copy));
+  } else {
+    for (int64_t row : rows)
+      MOE_HIP_TRY(hipMemcpyAsync(p->tab_dev + row * E, p->tab_host + row * E,
+                                 (size_t)E * sizeof(void*), hipMemcpyHostToDevice, p->copy));
+  }
   p->tab_changed.clear();
   MOE_HIP_TRY(hipEventRecord(p->tab_ready, p->copy));
   p->tab_pushed = true;
