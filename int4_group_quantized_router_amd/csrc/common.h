@@ -40,6 +40,11 @@ inline QLayout to_qlayout(const moe_blob_layout& l) {
 // stream needs before a kernel on it may read that table.
 const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer);
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream);
+// The policy updates of nl layer calls that found every expert resident
+// (each acquire + release of experts[l*k .. l*k+k) of layers[l], all hits,
+// in order), with one release point recorded on `stream` for all of them.
+int32_t pool_replay_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
+                         int32_t k, hipStream_t stream);
 
 }  // namespace moe
 

@@ -180,6 +180,16 @@ struct StackArgs {
   uint32_t* epochs;             // [grid]: calls completed, one counter per workgroup
   int32_t* err;                 // host-visible word set on a wait timeout
   int64_t timeout_ticks;        // wall-clock ticks a workgroup may wait in total
+  // pool mode: the pool's device table [L][E] -> slot address (NULL: not
+  // resident) replaces routed_base; every workgroup runs the same top-k, so
+  // all stop together at the first layer with a non-resident choice, and
+  // workgroup 0 writes that layer to *stop (left alone when all ran)
+  const uint8_t* const* res_tab;
+  int32_t* stop;
+  // first layer to run (0: input x0), and for l0 > 0 the previous layer's
+  // f32 output, from which layer l0's input is formed as usual
+  int l0;
+  const float* y_start;
 };
 
 // True if the persistent kernel has an instance for this shape on a device

@@ -78,6 +78,12 @@ struct moe_stack {
   void* ps_mem;                 // device: layer table, hand-off buffers, epochs
   int32_t* err_host;            // pinned, written by the kernel on a timeout
   moe::StackArgs ps;            // constant part of the kernel arguments
+  // pool mode of the persistent path (every layer on one pool)
+  slotpool* pool = nullptr;
+  int32_t* stop_host = nullptr;  // pinned: the layer the kernel stopped at
+  int32_t* idx_host = nullptr;   // pinned [L][k]: every layer's choices
+  uint16_t* xl_dev = nullptr;    // device [L][H]: layer inputs, to resume from
+  std::vector<int32_t> layer_ids;
 };
 
 struct moe_timer {
@@ -301,9 +307,11 @@ int32_t setup_persistent(moe_stack* st) {
   const moe_layer* L0 = st->layers[0];
   const moe_layer_cfg& c = L0->cfg;
   const int n = (int)st->layers.size();
+  // every layer resident, or every layer on the same pool
+  slotpool* pool = L0->pool;
   for (const moe_layer* L : st->layers) {
     const moe_layer_cfg& d = L->cfg;
-    if (L->pool || !L->resident_base || L->device != L0->device) return MOE_OK;
+    if (L->pool != pool || (!pool && !L->resident_base) || L->device != L0->device) return MOE_OK;
     if (d.hidden != c.hidden || d.experts != c.experts || d.top_k != c.top_k ||
         d.inter != c.inter || d.shared_inter != c.shared_inter || d.bits != c.bits)
       return MOE_OK;
@@ -343,7 +351,7 @@ int32_t setup_persistent(moe_stack* st) {
     descs[l].wsg = L->wsg;
     descs[l].shared_blob = L->shared_blob;
     descs[l].routed_base =
-        L->resident_base + (int64_t)L->cfg.layer_index * E * L->lay_r.stride;
+        pool ? nullptr : L->resident_base + (int64_t)L->cfg.layer_index * E * L->lay_r.stride;
   }
   // zeroed hand-off words carry tag 0, which no call uses
   e = hipMemset(st->ps_mem, 0, total);
@@ -352,9 +360,24 @@ int32_t setup_persistent(moe_stack* st) {
   if (e == hipSuccess)
     e = hipHostMalloc(reinterpret_cast<void**>(&st->err_host), sizeof(int32_t),
                       hipHostMallocDefault);
+  if (e == hipSuccess && pool) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&st->stop_host), sizeof(int32_t),
+                      hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipHostMalloc(reinterpret_cast<void**>(&st->idx_host), (size_t)n * k * sizeof(int32_t),
+                        hipHostMallocDefault);
+    if (e == hipSuccess)
+      e = hipMalloc(reinterpret_cast<void**>(&st->xl_dev), (size_t)n * H * sizeof(uint16_t));
+    for (const moe_layer* L : st->layers) st->layer_ids.push_back(L->cfg.layer_index);
+  }
   if (e != hipSuccess) {
     (void)hipFree(st->ps_mem);
     st->ps_mem = nullptr;
+    if (st->stop_host) (void)hipHostFree(st->stop_host);
+    if (st->idx_host) (void)hipHostFree(st->idx_host);
+    if (st->xl_dev) (void)hipFree(st->xl_dev);
+    st->stop_host = st->idx_host = nullptr;
+    st->xl_dev = nullptr;
     return fail(MOE_E_HIP, "stack setup: %s", hipGetErrorString(e));
   }
   *st->err_host = 0;
@@ -377,6 +400,11 @@ int32_t setup_persistent(moe_stack* st) {
   a.epochs = static_cast<uint32_t*>(parts[4]);
   a.err = st->err_host;
   a.timeout_ticks = (int64_t)clk_khz * 1000 * 2;  // 2 s
+  st->pool = pool;
+  if (pool) {
+    a.res_tab = pool_device_table(pool, 0);
+    a.stop = st->stop_host;
+  }
   st->grid = grid;
   st->persistent_ok = true;
   return MOE_OK;
@@ -822,13 +850,66 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     a.idx = idx;
     a.w = w;
     a.y_last = y_last;
-    timer_mark(MOE_KERNEL_STACK, true, stream);
     const moe_layer_cfg& c = stack->layers[0]->cfg;
-    hipError_t e =
-        launch_stack_decode(a, c.hidden, c.top_k, c.inter, c.shared_inter, c.bits, stream);
+    const int nl = (int)stack->layers.size(), H = c.hidden, k = c.top_k;
+    if (stack->pool) {
+      // the kernel reads the pool's table; it exports every layer's input
+      // (to resume from) and choices (for the pool policy)
+      a.x_layers = x_layers ? x_layers : stack->xl_dev;
+      a.idx = stack->idx_host;
+      *stack->stop_host = nl;
+      const int32_t st = pool_before_lookup(stack->pool, stream);
+      if (st != MOE_OK) return st;
+    }
+    timer_mark(MOE_KERNEL_STACK, true, stream);
+    hipError_t e = launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream);
     timer_mark(MOE_KERNEL_STACK, false, stream);
     MOE_HIP_TRY(e);
-    return MOE_OK;
+    if (!stack->pool) return MOE_OK;
+
+    // Pool mode: the host needs the layer the kernel stopped at (the first
+    // with a non-resident choice, or nl) before it can go on.  The policy
+    // then sees the layers the kernel ran as the per-layer path would have
+    // (each a call whose experts all hit, in order); the stopped layer runs
+    // on the per-layer path (its misses are filled there), and the kernel
+    // resumes from the next layer with that layer's output.
+    int l0 = 0;
+    for (;;) {
+      MOE_HIP_TRY(hipStreamSynchronize(stream));
+      if (*stack->err_host) {
+        *stack->err_host = 0;
+        return fail(MOE_E_HIP, "a persistent decode call on this stack timed out");
+      }
+      const int stop = *stack->stop_host;
+      if (stop < l0 || stop > nl)
+        return fail(MOE_E_HIP, "persistent decode stopped at layer %d", stop);
+      int32_t st = pool_replay_hits(stack->pool, stack->layer_ids.data() + l0,
+                                    stack->idx_host + (size_t)l0 * k, stop - l0, k, stream);
+      if (st != MOE_OK) return st;
+      if (idx && stop > l0)
+        MOE_HIP_TRY(hipMemcpyAsync(idx + (size_t)l0 * k, stack->idx_host + (size_t)l0 * k,
+                                   (size_t)(stop - l0) * k * sizeof(int32_t),
+                                   hipMemcpyHostToDevice, stream));
+      if (stop == nl) return MOE_OK;
+      moe_layer* L = stack->layers[stop];
+      float* yout = y_layers ? y_layers + (size_t)stop * H : L->y;
+      st = forward_decode(L, a.x_layers + (size_t)stop * H, nullptr, nullptr, 1,
+                          stop == nl - 1 ? y_last : nullptr, yout,
+                          idx ? idx + (size_t)stop * k : nullptr, w ? w + (size_t)stop * k : nullptr,
+                          stream);
+      if (st != MOE_OK) return st;
+      if (stop == nl - 1) return MOE_OK;
+      // the kernel that wrote the pinned words has finished (the sync
+      // above); the relaunch writes them again only after what was enqueued
+      // since, the copy of its choices included
+      l0 = stop + 1;
+      a.l0 = l0;
+      a.y_start = yout;
+      *stack->stop_host = nl;
+      st = pool_before_lookup(stack->pool, stream);
+      if (st != MOE_OK) return st;
+      MOE_HIP_TRY(launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream));
+    }
   }
   const int n = (int)stack->layers.size();
   const int H = stack->layers[0]->cfg.hidden, k = stack->layers[0]->cfg.top_k;
@@ -870,6 +951,9 @@ int32_t moe_stack_destroy(moe_stack* stack) {
     (void)hipFree(stack->ps_mem);
   }
   if (stack->err_host) (void)hipHostFree(stack->err_host);
+  if (stack->stop_host) (void)hipHostFree(stack->stop_host);
+  if (stack->idx_host) (void)hipHostFree(stack->idx_host);
+  if (stack->xl_dev) (void)hipFree(stack->xl_dev);
   delete stack;
   if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
   return MOE_OK;

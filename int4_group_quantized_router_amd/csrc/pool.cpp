@@ -221,6 +221,39 @@ const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer) {
   return p->tab_dev + (int64_t)layer * p->store->experts;
 }
 
+int32_t pool_replay_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
+                         int32_t k, hipStream_t stream) {
+  if (nl <= 0) return MOE_OK;
+  // one release point for every slot the calls read, as release() records
+  if (p->release_event && stream != p->release_stream)
+    MOE_HIP_TRY(hipStreamWaitEvent(stream, p->release_event, 0));
+  hipEvent_t ev = p->ring[p->ring_next];
+  p->ring_next = (p->ring_next + 1) % p->ring.size();
+  MOE_HIP_TRY(hipEventRecord(ev, stream));
+  p->release_stream = stream;
+  p->release_event = ev;
+  for (int32_t l = 0; l < nl; ++l) {
+    for (int32_t i = 0; i < k; ++i) {
+      const int32_t e = experts[(size_t)l * k + i];
+      const int64_t key = p->key(layers[l], e);
+      auto it = p->where.find(key);
+      if (it == p->where.end())
+        return fail(MOE_E_HIP, "replayed access (layer %d, expert %d) is not resident", layers[l],
+                    e);
+      const int32_t sl = it->second;
+      Slot& x = p->slots[sl];
+      ++p->tick;
+      if (x.pins == 0) p->victims.erase(p->vkey(sl));
+      x.count += 1;
+      x.last = p->tick;
+      x.last_use = ev;
+      p->stats.hits += 1;
+      if (x.pins == 0) p->victims.insert(p->vkey(sl));
+    }
+  }
+  return MOE_OK;
+}
+
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream) {
   // a stream that has not waited for the latest table push does so now
   if (p->tab_pushed && stream != p->tab_stream) {

@@ -184,7 +184,10 @@ struct Shape {
   static_assert(H <= 2048 && H % 256 == 0, "router row in one wave");
 };
 
-template <class S, int VPL>
+// POOL: routed blobs come from the pool's device table (a.res_tab) and the
+// call may start at a.l0 > 0; the resident instance reads routed_base and
+// always starts at layer 0.
+template <class S, int VPL, bool POOL>
 __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   using F = typename S::F;
   constexpr int BITS = S::BITS, H = S::H, I = S::I, IS = S::IS, K = S::K, R = S::R;
@@ -197,6 +200,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   __shared__ float s_w[MOE_MAX_TOPK + 1];
   __shared__ int tmp_e[MOE_MAX_TOPK];
   __shared__ float tmp_v[MOE_MAX_TOPK];
+  __shared__ const uint8_t* s_addr[POOL ? MOE_MAX_TOPK : 1];  // pool mode: blob of choice j
+  __shared__ int s_stop;
   __shared__ StackLayerDesc s_layers[kStackMaxLayers];
   __shared__ float part[(K + 1) * R];
   __shared__ float hsum[S::HW / S::EPC];
@@ -232,20 +237,22 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
 
   // router row of each wave (E = the shared gate), requested one layer ahead
   const int rrow = blk + kG * wave;
+  const int l0 = POOL ? a.l0 : 0;
   float4 wv[kWrN];
   float rbv = 0.f;
   if (rrow < e_rows) {
-    const float* wr = rrow < E ? s_layers[0].Wr + (size_t)rrow * H : s_layers[0].wsg;
+    const StackLayerDesc& D0 = s_layers[l0];
+    const float* wr = rrow < E ? D0.Wr + (size_t)rrow * H : D0.wsg;
 #pragma unroll
     for (int m = 0; m < kWrN; ++m) wv[m] = ldf4(wr + m * 256 + lane * 4);
-    if (rrow < E && s_layers[0].rb) rbv = ldf(s_layers[0].rb + rrow);
+    if (rrow < E && D0.rb) rbv = ldf(D0.rb + rrow);
   }
 
-  for (int l = 0; l < a.L && !failed; ++l) {
+  for (int l = l0; l < a.L && !failed; ++l) {
     const StackLayerDesc D = s_layers[l];
 
     // ---- layer input: x0, or bf16(y / rms(y)) of the previous layer
-    if (l == 0) {
+    if (l == 0) {  // (a call starting later than layer 0 begins from y_start)
       for (int i = tid; i < H; i += kNT) {
         const uint16_t v = a.x0[i];
         xb[i] = v;
@@ -255,7 +262,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       __syncthreads();
     } else {
       float yv[H / 256];
-      if (!poll_y<H>(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, tag, yv, deadline)) {
+      if (POOL && l == l0) {
+        if (tid < 256) {
+#pragma unroll
+          for (int m = 0; m < H / 256; ++m) yv[m] = a.y_start[tid + m * 256];
+        }
+      } else if (!poll_y<H>(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, tag, yv, deadline)) {
         failed = true;
         break;
       }
@@ -420,6 +432,13 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           if (blk == 0 && a.idx) a.idx[(size_t)l * K + lane] = s_sel[lane];
         }
         if (lane == 0) s_w[K] = a.has_wsg ? 1.0f / (1.0f + expf(-vs)) : 0.f;
+        if (POOL) {  // pool mode: the chosen blobs, if all resident
+          const uint8_t* addr =
+              lane < K ? a.res_tab[(size_t)l * E + s_sel[lane]] : nullptr;
+          if (lane < K) s_addr[lane] = addr;
+          const bool miss = __ballot(lane < K && addr == nullptr) != 0ull;
+          if (lane == 0) s_stop = miss ? 1 : 0;
+        }
       }
       if (lane == 0) s_abort = timed_out ? 1 : 0;
     } else {
@@ -442,6 +461,10 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       failed = true;
       break;
     }
+    if (POOL && s_stop) {  // the same decision in every workgroup
+      if (blk == 0 && tid == 0) *a.stop = l;
+      break;
+    }
     // the shared h (published while the logits were in flight) is requested
     // after the first routed gate/up pass and looked at after the last
     const uint64_t* hrep = reinterpret_cast<const uint64_t*>(hb + (size_t)rep * S::HW);
@@ -458,7 +481,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         if (pr < K * S::PR) {
           const int j = pr / S::PR;
           const uint8_t* blob =
-              D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
+              POOL ? s_addr[j]
+                        : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
           gu_load(blob, a.lq, a.lsb, (pr % S::PR) * RPP + rsub, gq[n % DEPTH], gsb[n % DEPTH]);
         }
       };
@@ -483,7 +507,9 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       if (it < K * S::NIR) {
         const int j = it / S::NIR, pp = it % S::NIR;
         const int ci = lane % S::CR, rloc = pp * S::RPPR + lane / S::CR;
-        const uint8_t* blob = D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
+        const uint8_t* blob =
+            POOL ? s_addr[j]
+                      : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
         dq[n] = make_uint4(0, 0, 0, 0);
         dsb[n] = 0;
         if (rloc < R) {
@@ -590,13 +616,18 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   }
 }
 
+template <class S, int VPL, bool POOL>
+hipError_t launch_mode(const StackArgs& a, hipStream_t s) {
+  const size_t lds = stack_lds_bytes(S::H, a.E, S::K, S::I, S::IS, S::BITS);
+  hipError_t e = allow_lds(stack_decode_kernel<S, VPL, POOL>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stack_decode_kernel<S, VPL, POOL>), dim3(kG), dim3(kNT), lds, s, a);
+  return hipGetLastError();
+}
+
 template <class S, int VPL>
 hipError_t launch_shape(const StackArgs& a, hipStream_t s) {
-  const size_t lds = stack_lds_bytes(S::H, a.E, S::K, S::I, S::IS, S::BITS);
-  hipError_t e = allow_lds(stack_decode_kernel<S, VPL>, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((stack_decode_kernel<S, VPL>), dim3(kG), dim3(kNT), lds, s, a);
-  return hipGetLastError();
+  return a.res_tab ? launch_mode<S, VPL, true>(a, s) : launch_mode<S, VPL, false>(a, s);
 }
 
 // The instances: (bits, H, I, Is, k) x top-k width (64 * VPL >= E).
