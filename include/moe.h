@@ -323,8 +323,9 @@ int32_t moe_layer_destroy(moe_layer* layer);
  * weightless stand-in for the residual and norm layers between the pages'
  * MoE layers, fused into layer l's router.  All layers share H and top_k.
  *
- * One-token calls (T == 1) on a stack whose layers are all resident and
- * share one shape run as ONE persistent kernel for the whole stack (256
+ * One-token calls (T == 1) on a stack whose layers share one shape and are
+ * either all resident or all on the same slot pool run as ONE persistent
+ * kernel for the whole stack (256
  * workgroups, needing a device with at least 256 compute units; all of them
  * must be resident at once, so other work on the device during the call can
  * make it time out): the pages find their
@@ -335,6 +336,16 @@ int32_t moe_layer_destroy(moe_layer* layer);
  * on one stack must not overlap (use one stream).  Every wait inside the
  * kernel is bounded (2 s); a call that ran out of time is reported as
  * MOE_E_HIP by the next moe_stack_forward on the same stack.
+ *
+ * On a pool the kernel reads each chosen expert's address from the pool's
+ * device table and stops at the first layer with a non-resident choice
+ * (all workgroups see the same top-k, so all stop there).  The calling
+ * thread waits for the kernel, replays the hits of the layers that ran into
+ * the pool policy in access order, runs the stopped layer as a pooled
+ * moe_layer_forward (which fills its misses) and relaunches from the next
+ * layer.  Such a call returns with its work complete on `stream`; the pool
+ * sees the same accesses, in the same order, as per-layer calls would give,
+ * and the outputs equal the resident stack's bit for bit.
  * ---------------------------------------------------------------------- */
 typedef struct moe_stack moe_stack;
 
