@@ -343,9 +343,11 @@ int32_t moe_layer_destroy(moe_layer* layer);
  * thread waits for the kernel, replays the hits of the layers that ran into
  * the pool policy in access order, runs the stopped layer as a pooled
  * moe_layer_forward (which fills its misses) and relaunches from the next
- * layer.  Such a call returns with its work complete on `stream`; the pool
- * sees the same accesses, in the same order, as per-layer calls would give,
- * and the outputs equal the resident stack's bit for bit.
+ * layer.  The calling thread thus waits for every persistent launch of the
+ * call (work after the last one may still be queued on `stream` when it
+ * returns); the pool sees the same accesses, in the same order, as
+ * per-layer calls would give, and the outputs equal the resident stack's
+ * bit for bit.
  * ---------------------------------------------------------------------- */
 typedef struct moe_stack moe_stack;
 

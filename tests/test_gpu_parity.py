@@ -544,6 +544,60 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
         m.expert_store_destroy(store)
 
 
+@pytest.mark.parametrize("cap", [24, 44])
+def test_pool_stack_persistent_equals_per_layer(torch, cap):
+    """A pooled stack run through the persistent kernel (stopping at the first
+    layer with a miss, the host filling it and resuming) gives the per-layer
+    pooled stack's outputs and exports bit for bit and leaves its pool in the
+    same state: the same hits, misses, evictions and slot of every expert, so
+    the replay of the hits keeps the policy's access order."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=4)
+    _print("pooled stack persistent vs per-layer", cfg.name)
+    dm = DeviceModel(cfg)
+    store, _ = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    # 24 < 4 layers x top-10: every token stops somewhere; 44 holds a whole
+    # token, so a repeated token runs all layers in one launch
+    pools = [m.slotpool_create(store, cap, 0), m.slotpool_create(store, cap, 0)]
+    stacks = [m.moe_stack_create(dm.make_layers(pool=p)) for p in pools]
+    m.moe_stack_set_persistent(stacks[1], False)
+    assert m.moe_stack_persistent_active(stacks[0])
+    assert not m.moe_stack_persistent_active(stacks[1])
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    try:
+        for tok in [0, 0, 1, 2, 0, 0, 3, 1, 4, 4, 2]:
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            outs = []
+            for st in stacks:
+                xl = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+                yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                w = torch.empty((L, 1, k), dtype=torch.float32, device="cuda")
+                y = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx, w=w)
+                torch.cuda.synchronize()
+                outs.append([t.cpu().numpy() for t in (y, xl, yl, idx, w)])
+            for a, b in zip(*outs):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), tok
+            st0, st1 = ({k: v for k, v in m.slotpool_get_stats(p).items() if k != "read_ns"}
+                        for p in pools)
+            assert st0 == st1, (tok, st0, st1)
+        # at 24 slots the 40 accesses per token cycle through the pool and all
+        # miss (the kernel stops at every layer); at 44 repeats hit
+        assert st0["evictions"] > 0 and (cap < 40 or st0["hits"] > 0), st0
+        for l in range(L):
+            for e in range(cfg.experts):
+                assert m.slotpool_slot_of(pools[0], l, e) == m.slotpool_slot_of(pools[1], l, e)
+    finally:
+        for st in stacks:
+            m.moe_stack_destroy(st)
+        dm.destroy()
+        for p in pools:
+            m.slotpool_destroy(p)
+        m.expert_store_destroy(store)
+
+
 def test_pool_shared_by_two_streams_bitwise(torch):
     """Two pooled layers on two compute streams share one small pool (every
     few calls evict a slot the other stream read last): results equal the
