@@ -42,9 +42,13 @@ const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer);
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream);
 // The policy updates of nl layer calls that found every expert resident
 // (each acquire + release of experts[l*k .. l*k+k) of layers[l], all hits,
-// in order), with one release point recorded on `stream` for all of them.
-int32_t pool_replay_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
-                         int32_t k, hipStream_t stream);
+// in order), with one release point recorded on `stream` for all of them
+// now.  The updates themselves are held in the pool and applied, in order,
+// by pool_apply_pending, which every public pool call runs first: nothing
+// can observe or change the policy before they are in.
+int32_t pool_defer_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
+                        int32_t k, hipStream_t stream);
+int32_t pool_apply_pending(slotpool* p);
 
 }  // namespace moe
 

@@ -866,13 +866,17 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     timer_mark(MOE_KERNEL_STACK, false, stream);
     MOE_HIP_TRY(e);
     if (!stack->pool) return MOE_OK;
+    // the previous call's hits enter the policy while this kernel runs
+    int32_t pst = pool_apply_pending(stack->pool);
+    if (pst != MOE_OK) return pst;
 
     // Pool mode: the host needs the layer the kernel stopped at (the first
     // with a non-resident choice, or nl) before it can go on.  The policy
     // then sees the layers the kernel ran as the per-layer path would have
-    // (each a call whose experts all hit, in order); the stopped layer runs
-    // on the per-layer path (its misses are filled there), and the kernel
-    // resumes from the next layer with that layer's output.
+    // (each a call whose experts all hit, in order; held in the pool and
+    // applied before its next use); the stopped layer runs on the per-layer
+    // path (its misses are filled there), and the kernel resumes from the
+    // next layer with that layer's output.
     int l0 = 0;
     for (;;) {
       MOE_HIP_TRY(hipStreamSynchronize(stream));
@@ -883,8 +887,8 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
       const int stop = *stack->stop_host;
       if (stop < l0 || stop > nl)
         return fail(MOE_E_HIP, "persistent decode stopped at layer %d", stop);
-      int32_t st = pool_replay_hits(stack->pool, stack->layer_ids.data() + l0,
-                                    stack->idx_host + (size_t)l0 * k, stop - l0, k, stream);
+      int32_t st = pool_defer_hits(stack->pool, stack->layer_ids.data() + l0,
+                                   stack->idx_host + (size_t)l0 * k, stop - l0, k, stream);
       if (st != MOE_OK) return st;
       if (idx && stop > l0)
         MOE_HIP_TRY(hipMemcpyAsync(idx + (size_t)l0 * k, stack->idx_host + (size_t)l0 * k,

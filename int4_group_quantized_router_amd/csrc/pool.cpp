@@ -136,6 +136,11 @@ struct slotpool {
   hipEvent_t tab_ready = nullptr;              // recorded after the last push
   bool tab_pushed = false;                     // tab_ready has been recorded
   hipStream_t tab_stream = nullptr;            // last stream made to wait on tab_ready
+  // hits a stack call found through the device table, not yet applied to
+  // the policy: (layer, expert) pairs in access order, and per batch the
+  // end offset and the release event recorded for it
+  std::vector<int32_t> pend;
+  std::vector<std::pair<size_t, hipEvent_t>> pend_marks;
   std::vector<uint8_t*> stage;                 // file store: pinned staging buffers
   std::vector<hipEvent_t> stage_done;          // copy out of stage[i] finished
   std::vector<bool> stage_used;
@@ -221,8 +226,8 @@ const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer) {
   return p->tab_dev + (int64_t)layer * p->store->experts;
 }
 
-int32_t pool_replay_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
-                         int32_t k, hipStream_t stream) {
+int32_t pool_defer_hits(slotpool* p, const int32_t* layers, const int32_t* experts, int32_t nl,
+                        int32_t k, hipStream_t stream) {
   if (nl <= 0) return MOE_OK;
   // one release point for every slot the calls read, as release() records
   if (p->release_event && stream != p->release_stream)
@@ -232,26 +237,40 @@ int32_t pool_replay_hits(slotpool* p, const int32_t* layers, const int32_t* expe
   MOE_HIP_TRY(hipEventRecord(ev, stream));
   p->release_stream = stream;
   p->release_event = ev;
-  for (int32_t l = 0; l < nl; ++l) {
+  for (int32_t l = 0; l < nl; ++l)
     for (int32_t i = 0; i < k; ++i) {
-      const int32_t e = experts[(size_t)l * k + i];
-      const int64_t key = p->key(layers[l], e);
-      auto it = p->where.find(key);
-      if (it == p->where.end())
-        return fail(MOE_E_HIP, "replayed access (layer %d, expert %d) is not resident", layers[l],
-                    e);
+      p->pend.push_back(layers[l]);
+      p->pend.push_back(experts[(size_t)l * k + i]);
+    }
+  p->pend_marks.emplace_back(p->pend.size(), ev);
+  return MOE_OK;
+}
+
+int32_t pool_apply_pending(slotpool* p) {
+  size_t i = 0;
+  int32_t st = MOE_OK;
+  for (const auto& mk : p->pend_marks) {
+    for (; i < mk.first && st == MOE_OK; i += 2) {
+      const int32_t layer = p->pend[i], e = p->pend[i + 1];
+      auto it = p->where.find(p->key(layer, e));
+      if (it == p->where.end()) {
+        st = fail(MOE_E_HIP, "replayed access (layer %d, expert %d) is not resident", layer, e);
+        break;
+      }
       const int32_t sl = it->second;
       Slot& x = p->slots[sl];
       ++p->tick;
       if (x.pins == 0) p->victims.erase(p->vkey(sl));
       x.count += 1;
       x.last = p->tick;
-      x.last_use = ev;
+      x.last_use = mk.second;
       p->stats.hits += 1;
       if (x.pins == 0) p->victims.insert(p->vkey(sl));
     }
   }
-  return MOE_OK;
+  p->pend.clear();
+  p->pend_marks.clear();
+  return st;
 }
 
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream) {
@@ -652,12 +671,21 @@ int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int3
 
 }  // namespace
 
+// every public call that reads or changes the policy first applies the hits
+// a stack call held back (pool_defer_hits), so all see one access order
+#define MOE_POOL_APPLY(p)                                 \
+  do {                                                    \
+    const int32_t pst_ = moe::pool_apply_pending(p);      \
+    if (pst_ != MOE_OK) return pst_;                      \
+  } while (0)
+
 extern "C" {
 
 int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
                          hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss) {
   clear_error();
   MOE_REQUIRE(pool && (n == 0 || (experts && slot_ptrs)) && n >= 0, "bad argument");
+  MOE_POOL_APPLY(pool);
   const int32_t st = acquire_impl(pool, layer, experts, n, compute, slot_ptrs, was_miss);
   // the table follows every admission and eviction of the call, also on
   // the error paths (entries dropped there are cleared)
@@ -670,6 +698,7 @@ int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts, 
   clear_error();
   MOE_REQUIRE(pool && (n == 0 || experts) && n >= 0, "bad argument");
   if (n == 0) return MOE_OK;
+  MOE_POOL_APPLY(pool);
   hipEvent_t ev = pool->ring[pool->ring_next];
   pool->ring_next = (pool->ring_next + 1) % pool->ring.size();
   // A slot may still hold a ring event that is re-recorded here.  That is
@@ -697,6 +726,7 @@ int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert) {
   MOE_REQUIRE(pool, "null argument");
   int32_t st = check_le(pool->store, layer, expert);
   if (st != MOE_OK) return st;
+  MOE_POOL_APPLY(pool);
   auto it = pool->where.find(pool->key(layer, expert));
   if (it == pool->where.end()) return MOE_OK;
   if (pool->slots[it->second].pins)
@@ -709,6 +739,7 @@ int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert) {
 int32_t slotpool_flush(slotpool* pool) {
   clear_error();
   MOE_REQUIRE(pool, "null argument");
+  MOE_POOL_APPLY(pool);
   for (const auto& kv : pool->where)
     if (pool->slots[kv.second].pins) return fail(MOE_E_BUSY, "flush with pinned slots");
   std::vector<int32_t> res;
@@ -720,6 +751,8 @@ int32_t slotpool_flush(slotpool* pool) {
 int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out) {
   clear_error();
   MOE_REQUIRE(pool && out, "null argument");
+  // hits held back by a stack call are part of the pool's logical state
+  MOE_POOL_APPLY(const_cast<slotpool*>(pool));
   *out = pool->stats;
   return MOE_OK;
 }
@@ -727,6 +760,7 @@ int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out) {
 int32_t slotpool_slot_of(const slotpool* pool, int32_t layer, int32_t expert, int32_t* slot) {
   clear_error();
   MOE_REQUIRE(pool && slot, "null argument");
+  MOE_POOL_APPLY(const_cast<slotpool*>(pool));
   auto it = pool->where.find(pool->key(layer, expert));
   *slot = it == pool->where.end() ? -1 : it->second;
   return MOE_OK;
