@@ -121,12 +121,14 @@ int32_t moe_blob_pack(const moe_qshape* shape, const moe_qmatrix_host* gate,
  * x: device bf16 [T, H]; Wr: device f32 [E, H]; rb: device f32 [E] or
  * NULL (zero bias); wsg: device f32 [H] or NULL (then sigma is not written).
  * idx: device int32 [T, k]; w: device f32 [T, k]; sigma: device f32 [T] or
- * NULL; logits: device f32 [T, E], required -- written, and used as the
- * kernels' scratch.  MOE_E_INVAL if k < 1, k > E, k > MOE_MAX_TOPK,
- * E > 1024, H not a positive multiple of 256 up to 4096, or T < 0 (T = 0
- * is a no-op).
+ * NULL; logits: device f32 [T, E] or NULL (then not exported; the
+ * per-token path keeps them in stream-ordered scratch, hipMallocAsync /
+ * hipFreeAsync on `stream`).  MOE_E_INVAL if k < 1, k > E,
+ * k > MOE_MAX_TOPK, E > 1024, H not a positive multiple of 256 up to 4096,
+ * or T < 0 (T = 0 is a no-op).
  *
- * T <= 8: one fused launch (f32 GEMV; the last workgroup runs the top-k).
+ * T <= 8: an f32 GEMV launch, then the top-k launch (a layer's own router
+ * fuses the two: its last workgroup runs the top-k).
  * T > 8: the logits come from bf16 MFMA on Wr split exactly into three bf16
  * planes (hi + mid + lo == Wr, so every product is exact in f32), with K cut
  * into up to 4 slices whose partial sums the top-k adds in slice order, then
@@ -140,20 +142,29 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
 
 /* ------------------------------------------------------------------------
  * Dequantise one matrix of a device blob (test hook for the bit-exact
- * dequant check).  which: 0 gate, 1 up, 2 down.  out_f32: device f32
+ * dequant check): the MLX-style affine group dequantisation the pages name
+ * for the expert weights ([xix] lineage paragraph: MLX-style int4/int8
+ * group quantisation; [lens] "TurboFieldfareとの関係"), W = s*q + b per
+ * group of 64 inputs.  which: 0 gate, 1 up, 2 down.  out_f32: device f32
  * [out, in] with s*q + b computed in f32 (exact for the supported value
  * ranges); out_bf16: device bf16 [out, in] (round to nearest even of the
- * f32 value) or NULL.
+ * f32 value) or NULL.  blob: device expert blob of `shape` (read only).
+ * MOE_E_INVAL on a null pointer, a bad `which` or an unsupported shape.
  * ---------------------------------------------------------------------- */
 int32_t moe_dequant(const void* blob, const moe_qshape* shape, int32_t which,
                     float* out_f32, uint16_t* out_bf16, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * One SwiGLU expert on T tokens, accumulated:
+ * One SwiGLU expert on T tokens, accumulated -- the unit the pages' layer
+ * runs for each chosen routed expert and for the shared expert, straight
+ * from the quantised weights ([xix] how-it-works paragraph; [lens]
+ * "エキスパートストリーミングの仕組み"):
  *   h = bf16(silu(Wg x) * (Wu x)),   y_accum[t] += coef[t] * (Wd h)
- * x: device bf16 [T, H]; blob: device expert blob; coef: device f32 [T];
- * y_accum: device f32 [T, H] (read and written).  1 <= T <= MOE_MAX_DECODE_T.
- * Uses stream-ordered scratch (hipMallocAsync) for h.
+ * x: device bf16 [T, H]; blob: device expert blob (read only); coef: device
+ * f32 [T]; y_accum: device f32 [T, H] (read and written).
+ * 1 <= T <= MOE_MAX_DECODE_T, else MOE_E_INVAL (also for an unsupported
+ * shape or a null pointer).  Uses stream-ordered scratch (hipMallocAsync /
+ * hipFreeAsync on `stream`) for h, T * inter bf16 values.
  * ---------------------------------------------------------------------- */
 int32_t moe_expert_forward(const uint16_t* x, int32_t T, const moe_qshape* shape,
                            const void* blob, const float* coef, float* y_accum,
@@ -230,14 +241,14 @@ int32_t expert_store_drop_cache(expert_store* store);
  * ---------------------------------------------------------------------- */
 typedef struct slotpool slotpool;
 
-typedef struct slotpool_stats {
+typedef struct slotpool_counters {
   int64_t hits;
   int64_t misses;
   int64_t evictions;
   int64_t bytes_h2d;
   int64_t bytes_read;  /* file store: bytes read from the file */
   int64_t read_ns;     /* file store: host time spent in those reads */
-} slotpool_stats;
+} slotpool_counters;
 
 /* capacity: number of slots (>= 1); device: HIP device ordinal.  Allocates
  * capacity * stride bytes of device memory and a copy stream (and, over a
@@ -264,7 +275,10 @@ int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert);
 /* Drop every resident expert (next accesses all miss); MOE_E_BUSY if any
  * slot is pinned.  Counters are kept. */
 int32_t slotpool_flush(slotpool* pool);
-int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out);
+/* The pool's counters (hits, misses, evictions, bytes copied and read). */
+int32_t slotpool_stats(const slotpool* pool, slotpool_counters* out);
+/* The same as slotpool_stats (earlier name). */
+int32_t slotpool_get_stats(const slotpool* pool, slotpool_counters* out);
 /* Slot index of (layer, expert), or -1 if not resident (test hook). */
 int32_t slotpool_slot_of(const slotpool* pool, int32_t layer, int32_t expert,
                          int32_t* slot);
@@ -294,7 +308,9 @@ typedef struct moe_layer moe_layer;
 /* Wr f32 [E,H], rb f32 [E] (nullable), wsg f32 [H], shared_blob: device
  * blob of shape (H, shared_inter).  Exactly one of resident_base (device
  * base of the L*E routed blobs, blob (l,e) at (l*E+e)*stride) and pool is
- * non-NULL.  Allocates the layer's device workspace. */
+ * non-NULL.  With a pool, the pool's store must hold layer_index (< its
+ * layers), exactly `experts` experts per layer and blobs of this layer's
+ * stride, else MOE_E_INVAL.  Allocates the layer's device workspace. */
 int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr,
                          const float* rb, const void* shared_blob,
                          const float* wsg, const void* resident_base,
@@ -363,10 +379,27 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T,
                           uint16_t* x_layers, float* y_layers, int32_t* idx,
                           float* w, uint16_t* y_last, hipStream_t stream);
 /* enable != 0 (the default): T == 1 calls take the persistent kernel when
- * the stack qualifies; 0: always the per-layer kernels (for comparisons). */
+ * the stack qualifies; 0: always the per-layer kernels (for comparisons).
+ *
+ * A call that runs out of time writes NaN to the rows of y_last (and of
+ * y_layers from the layer that failed on) that the stalled workgroups own,
+ * so its outputs never look valid; the error is returned by that call
+ * (pooled stacks, which wait for the kernel) or by the next call on the
+ * stack (resident stacks, which do not). */
 int32_t moe_stack_set_persistent(moe_stack* stack, int32_t enable);
 /* *active = 1 if the next T == 1 call runs the persistent kernel. */
 int32_t moe_stack_persistent_active(const moe_stack* stack, int32_t* active);
+/* Test hooks of the persistent path.  moe_stack_epoch: launches of the
+ * persistent kernel so far (each tags its hand-off words with it).
+ * moe_stack_advance_epoch: synchronises the device and advances the
+ * launch count by n, as n launches that wrote nothing would; the host keeps
+ * every hand-off word that could carry a later launch's tag out of reach,
+ * whatever the count.  moe_stack_set_timeout: the bound on a workgroup's
+ * waits (default 2 s); 0 makes every wait that is not already satisfied
+ * time out at once.  MOE_E_INVAL if the stack has no persistent path. */
+int32_t moe_stack_epoch(const moe_stack* stack, uint32_t* epoch);
+int32_t moe_stack_advance_epoch(moe_stack* stack, uint32_t n);
+int32_t moe_stack_set_timeout(moe_stack* stack, int64_t microseconds);
 int32_t moe_stack_destroy(moe_stack* stack);
 
 /* ------------------------------------------------------------------------

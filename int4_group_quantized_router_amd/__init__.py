@@ -125,8 +125,9 @@ def moe_blob_pack(hidden: int, inter: int, bits: int, arrays: dict, out=None,
 # ------------------------------------------------------------------ compute
 
 def moe_route_topk(x, Wr, rb, k: int, wsg=None, with_sigma: bool = True, idx=None, w=None,
-                   sigma=None, logits=None, stream=None) -> dict:
-    """Router on x (bf16 [T,H]); returns {'idx','w','sigma','logits'} device tensors."""
+                   sigma=None, logits=None, stream=None, with_logits: bool = True) -> dict:
+    """Router on x (bf16 [T,H]); returns {'idx','w','sigma','logits'} device tensors
+    (``logits`` None when ``with_logits`` is false and none is given: not exported)."""
     import torch
     T, H = x.shape
     E = Wr.shape[0]
@@ -135,7 +136,8 @@ def moe_route_topk(x, Wr, rb, k: int, wsg=None, with_sigma: bool = True, idx=Non
     w = w if w is not None else torch.empty((T, k), dtype=torch.float32, device=dev)
     if with_sigma and wsg is not None and sigma is None:
         sigma = torch.empty((T,), dtype=torch.float32, device=dev)
-    logits = logits if logits is not None else torch.empty((T, E), dtype=torch.float32, device=dev)
+    if logits is None and with_logits:
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     _check(_lib_().moe_route_topk(
         _dptr(x, _bf16_types(), "x"), T, H, _dptr(Wr, (torch.float32,), "Wr"),
         _dptr(rb, (torch.float32,), "rb"), E, int(k), _dptr(wsg, (torch.float32,), "wsg"),
@@ -256,6 +258,13 @@ def slotpool_flush(pool) -> None:
     _check(_lib_().slotpool_flush(_h(pool)), "slotpool_flush")
 
 
+def slotpool_stats(pool) -> dict:
+    st = PoolStats()
+    _check(_lib_().slotpool_stats(_h(pool), C.byref(st)), "slotpool_stats")
+    return {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
+            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns}
+
+
 def slotpool_get_stats(pool) -> dict:
     st = PoolStats()
     _check(_lib_().slotpool_get_stats(_h(pool), C.byref(st)), "slotpool_get_stats")
@@ -337,6 +346,20 @@ def moe_stack_persistent_active(stack) -> bool:
     _check(_lib_().moe_stack_persistent_active(_h(stack), C.byref(out)),
            "moe_stack_persistent_active")
     return bool(out.value)
+
+
+def moe_stack_epoch(stack) -> int:
+    out = C.c_uint32()
+    _check(_lib_().moe_stack_epoch(_h(stack), C.byref(out)), "moe_stack_epoch")
+    return out.value
+
+
+def moe_stack_advance_epoch(stack, n: int) -> None:
+    _check(_lib_().moe_stack_advance_epoch(_h(stack), int(n)), "moe_stack_advance_epoch")
+
+
+def moe_stack_set_timeout(stack, microseconds: int) -> None:
+    _check(_lib_().moe_stack_set_timeout(_h(stack), int(microseconds)), "moe_stack_set_timeout")
 
 
 def moe_stack_destroy(stack) -> None:

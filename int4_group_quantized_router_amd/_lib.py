@@ -80,6 +80,7 @@ SIGNATURES = {
     "slotpool_release": [_P, _I32, _P, _I32, _P],
     "slotpool_evict": [_P, _I32, _I32],
     "slotpool_flush": [_P],
+    "slotpool_stats": [_P, C.POINTER(PoolStats)],
     "slotpool_get_stats": [_P, C.POINTER(PoolStats)],
     "slotpool_slot_of": [_P, _I32, _I32, C.POINTER(_I32)],
     "slotpool_destroy": [_P],
@@ -90,6 +91,9 @@ SIGNATURES = {
     "moe_stack_forward": [_P, _P, _I32, _P, _P, _P, _P, _P, _P],
     "moe_stack_set_persistent": [_P, _I32],
     "moe_stack_persistent_active": [_P, C.POINTER(_I32)],
+    "moe_stack_epoch": [_P, C.POINTER(C.c_uint32)],
+    "moe_stack_advance_epoch": [_P, C.c_uint32],
+    "moe_stack_set_timeout": [_P, _I64],
     "moe_stack_destroy": [_P],
     "moe_timer_create": [_I32, _I32, C.POINTER(_P)],
     "moe_timer_attach": [_P],

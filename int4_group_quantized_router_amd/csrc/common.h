@@ -40,6 +40,10 @@ inline QLayout to_qlayout(const moe_blob_layout& l) {
 // stream needs before a kernel on it may read that table.
 const uint8_t* const* pool_device_table(const slotpool* p, int32_t layer);
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream);
+// MOE_OK if a layer with `experts` routed experts at store layer
+// `layer_index`, blob stride `stride`, can draw on pool p's store; else
+// MOE_E_INVAL with the mismatch in the error message.
+int32_t pool_check_layer(const slotpool* p, int32_t layer_index, int32_t experts, int64_t stride);
 // The policy updates of nl layer calls that found every expert resident
 // (each acquire + release of experts[l*k .. l*k+k) of layers[l], all hits,
 // in order), with one release point recorded on `stream` for all of them

@@ -157,7 +157,9 @@ struct StackLayerDesc {
   const float* rb;              // f32 [E] or NULL
   const float* wsg;             // f32 [H] or NULL
   const uint8_t* shared_blob;   // shared expert
-  const uint8_t* routed_base;   // device address of blob (l, 0)
+  const uint8_t* routed_base;   // device address of blob (l, 0) (resident), or NULL
+  const uint8_t* const* res_row;  // pool mode: the pool's device-table row of this
+                                  // layer's index (expert -> slot address or NULL)
 };
 
 struct StackArgs {
@@ -180,11 +182,12 @@ struct StackArgs {
   uint32_t* epochs;             // [grid]: calls completed, one counter per workgroup
   int32_t* err;                 // host-visible word set on a wait timeout
   int64_t timeout_ticks;        // wall-clock ticks a workgroup may wait in total
-  // pool mode: the pool's device table [L][E] -> slot address (NULL: not
-  // resident) replaces routed_base; every workgroup runs the same top-k, so
-  // all stop together at the first layer with a non-resident choice, and
-  // workgroup 0 writes that layer to *stop (left alone when all ran)
-  const uint8_t* const* res_tab;
+  // pool mode (pool != 0): each layer's row of the pool's device table
+  // (StackLayerDesc::res_row, expert -> slot address, NULL: not resident)
+  // replaces routed_base; every workgroup runs the same top-k, so all stop
+  // together at the first layer with a non-resident choice, and workgroup 0
+  // writes that layer to *stop (left alone when all ran)
+  int pool;
   int32_t* stop;
   // first layer to run (0: input x0), and for l0 > 0 the previous layer's
   // f32 output, from which layer l0's input is formed as usual
@@ -198,6 +201,9 @@ bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cu
 size_t stack_lds_bytes(int H, int E, int k, int I, int Is, int bits);
 hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,
                                hipStream_t s);
+// Zero `bytes` (a multiple of 4) of device memory with a kernel (usable
+// where a memset node would not be, e.g. under stream capture).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 hipError_t launch_dequant(const uint8_t* blob, const QLayout& lay, int rows, int cols,
                           int bits, int which, float* out_f32, uint16_t* out_bf16,

@@ -84,6 +84,12 @@ struct moe_stack {
   int32_t* idx_host = nullptr;   // pinned [L][k]: every layer's choices
   uint16_t* xl_dev = nullptr;    // device [L][H]: layer inputs, to resume from
   std::vector<int32_t> layer_ids;
+  // launches so far (the device's per-workgroup call counters hold the
+  // same value), and per layer a lower bound on the launch that wrote any
+  // word still in that layer's hand-off buffers
+  uint32_t epoch = 0;
+  std::vector<uint32_t> fresh;
+  int64_t clk_khz = 0;
 };
 
 struct moe_timer {
@@ -352,6 +358,7 @@ int32_t setup_persistent(moe_stack* st) {
     descs[l].shared_blob = L->shared_blob;
     descs[l].routed_base =
         pool ? nullptr : L->resident_base + (int64_t)L->cfg.layer_index * E * L->lay_r.stride;
+    descs[l].res_row = pool ? pool_device_table(pool, L->cfg.layer_index) : nullptr;
   }
   // zeroed hand-off words carry tag 0, which no call uses
   e = hipMemset(st->ps_mem, 0, total);
@@ -402,12 +409,52 @@ int32_t setup_persistent(moe_stack* st) {
   a.timeout_ticks = (int64_t)clk_khz * 1000 * 2;  // 2 s
   st->pool = pool;
   if (pool) {
-    a.res_tab = pool_device_table(pool, 0);
+    a.pool = 1;
     a.stop = st->stop_host;
   }
+  st->clk_khz = clk_khz;
+  st->epoch = 0;
+  st->fresh.assign(n, 0u);
   st->grid = grid;
   st->persistent_ok = true;
   return MOE_OK;
+}
+
+// A hand-off word carries the tag of the launch that wrote it: 32 bits for
+// y and the logits, 15 bits for h (a bf16 shares its 32-bit word), so an h
+// word left behind kTagSpan launches earlier carries the tag of the next
+// launch.  A layer's words are rewritten by every launch that runs the
+// layer to its end; a pooled launch that stops at a layer, or starts after
+// it, leaves the layer's words as they were.  Before a launch, every layer
+// it may run whose oldest word could be that old is zeroed (tag 0 matches
+// no launch).
+constexpr uint32_t kTagSpan = 32768;
+
+int32_t stack_clear_stale(moe_stack* st, int l0, hipStream_t stream) {
+  const moe_layer_cfg& c = st->layers[0]->cfg;
+  const int n = (int)st->layers.size();
+  const size_t yb = (size_t)kStackReplicas * c.hidden * 8;
+  const size_t lb = (size_t)kStackReplicas * (c.experts + 1) * 8;
+  const size_t hb = (size_t)kStackReplicas * (c.top_k * c.inter + c.shared_inter) * 4;
+  for (int l = l0; l < n; ++l) {
+    if (st->epoch - st->fresh[l] < kTagSpan) continue;
+    MOE_HIP_TRY(launch_fill_zero(st->ps.ybuf + (size_t)l * yb / 8, yb, stream));
+    MOE_HIP_TRY(launch_fill_zero(st->ps.lbuf + (size_t)l * lb / 8, lb, stream));
+    MOE_HIP_TRY(launch_fill_zero(st->ps.hbuf + (size_t)l * hb / 4, hb, stream));
+    st->fresh[l] = st->epoch;
+  }
+  return MOE_OK;
+}
+
+// After a launch (epoch st->epoch) that ran layers [l0, l1) to their end.
+void stack_launched(moe_stack* st, int l0, int l1) {
+  for (int l = l0; l < l1; ++l) st->fresh[l] = st->epoch;
+  st->epoch += 1;
+}
+
+// A launch failed part-way: any layer may hold words of any earlier launch.
+void stack_forget(moe_stack* st) {
+  for (uint32_t& f : st->fresh) f = st->epoch - kTagSpan;
 }
 
 int max_tiles_for(int T, int k, int E) {
@@ -590,7 +637,7 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
   clear_error();
   MOE_REQUIRE(T >= 0, "T must be >= 0");
   if (T == 0) return MOE_OK;
-  MOE_REQUIRE(x && Wr && idx && w && logits, "null argument");
+  MOE_REQUIRE(x && Wr && idx && w, "null argument");
   MOE_REQUIRE(H > 0 && H % 256 == 0 && H <= 4096, "H must be a multiple of 256 in [256, 4096]");
   MOE_REQUIRE(E >= 1 && E <= 1024, "E must be in [1, 1024]");
   MOE_REQUIRE(k >= 1 && k <= E && k <= MOE_MAX_TOPK, "k must be in [1, min(E, %d)]",
@@ -609,8 +656,21 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
   r.w = w;
   r.sigma = sigma;
   if (T <= MOE_MAX_DECODE_T) {
-    MOE_HIP_TRY(launch_route(r, stream));
-  } else {
+    // the GEMV writes the logits and the top-k reads them: without a caller
+    // buffer they go to stream-ordered scratch
+    float* scratch = nullptr;
+    if (!logits) {
+      MOE_HIP_TRY(hipMallocAsync(reinterpret_cast<void**>(&scratch), (size_t)T * E * 4, stream));
+      r.logits = scratch;
+    }
+    hipError_t e = launch_route(r, stream);
+    if (e == hipSuccess) e = launch_topk_only(r, stream);
+    const hipError_t e2 = scratch ? hipFreeAsync(scratch, stream) : hipSuccess;
+    MOE_HIP_TRY(e);
+    MOE_HIP_TRY(e2);
+    return MOE_OK;
+  }
+  {
     // many tokens: router on bf16 MFMA with Wr split into three exact planes;
     // the top-k sums the K slices' partials and computes the shared gate
     const int ks = router_splits(T, E, H);
@@ -630,8 +690,6 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
     MOE_HIP_TRY(e3);
     return MOE_OK;
   }
-  MOE_HIP_TRY(launch_topk_only(r, stream));
-  return MOE_OK;
 }
 
 int32_t moe_dequant(const void* blob, const moe_qshape* shape, int32_t which, float* out_f32,
@@ -702,6 +760,15 @@ int32_t moe_layer_create(const moe_layer_cfg* cfg, const float* Wr, const float*
   if (st != MOE_OK) return st;
   moe_qshape sr{cfg->hidden, cfg->inter, cfg->group, cfg->bits};
   moe_qshape ss{cfg->hidden, cfg->shared_inter, cfg->group, cfg->bits};
+  if (pool) {
+    // the layer reads blob (layer_index, e) of the pool's store, in its own
+    // blob layout: the store must hold that layer and this many experts at
+    // this layout's stride
+    moe_blob_layout lr;
+    blob_layout(sr, &lr);
+    st = pool_check_layer(pool, cfg->layer_index, cfg->experts, lr.stride);
+    if (st != MOE_OK) return st;
+  }
   moe_layer* L = new (std::nothrow) moe_layer{};
   if (!L) return fail(MOE_E_NOMEM, "host allocation failed");
   L->cfg = *cfg;
@@ -840,6 +907,7 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
   MOE_REQUIRE(T >= 1 && T <= MOE_MAX_DECODE_T, "T must be in [1, %d]", MOE_MAX_DECODE_T);
   if (stack->err_host && *stack->err_host) {
     *stack->err_host = 0;
+    stack_forget(stack);
     return fail(MOE_E_HIP, "an earlier persistent decode call on this stack timed out");
   }
   if (T == 1 && stack->persistent_ok && stack->persistent_enabled) {
@@ -861,11 +929,16 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
       const int32_t st = pool_before_lookup(stack->pool, stream);
       if (st != MOE_OK) return st;
     }
+    int32_t cst = stack_clear_stale(stack, 0, stream);
+    if (cst != MOE_OK) return cst;
     timer_mark(MOE_KERNEL_STACK, true, stream);
     hipError_t e = launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream);
     timer_mark(MOE_KERNEL_STACK, false, stream);
     MOE_HIP_TRY(e);
-    if (!stack->pool) return MOE_OK;
+    if (!stack->pool) {
+      stack_launched(stack, 0, nl);
+      return MOE_OK;
+    }
     // the previous call's hits enter the policy while this kernel runs
     int32_t pst = pool_apply_pending(stack->pool);
     if (pst != MOE_OK) return pst;
@@ -879,14 +952,25 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     // next layer with that layer's output.
     int l0 = 0;
     for (;;) {
-      MOE_HIP_TRY(hipStreamSynchronize(stream));
+      const hipError_t se = hipStreamSynchronize(stream);
+      if (se != hipSuccess) {
+        stack_forget(stack);
+        stack->epoch += 1;
+        return fail(MOE_E_HIP, "persistent decode: %s", hipGetErrorString(se));
+      }
       if (*stack->err_host) {
         *stack->err_host = 0;
+        stack->epoch += 1;
+        stack_forget(stack);
         return fail(MOE_E_HIP, "a persistent decode call on this stack timed out");
       }
       const int stop = *stack->stop_host;
-      if (stop < l0 || stop > nl)
+      if (stop < l0 || stop > nl) {
+        stack->epoch += 1;
+        stack_forget(stack);
         return fail(MOE_E_HIP, "persistent decode stopped at layer %d", stop);
+      }
+      stack_launched(stack, l0, stop);
       int32_t st = pool_defer_hits(stack->pool, stack->layer_ids.data() + l0,
                                    stack->idx_host + (size_t)l0 * k, stop - l0, k, stream);
       if (st != MOE_OK) return st;
@@ -911,6 +995,8 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
       a.y_start = yout;
       *stack->stop_host = nl;
       st = pool_before_lookup(stack->pool, stream);
+      if (st != MOE_OK) return st;
+      st = stack_clear_stale(stack, l0, stream);
       if (st != MOE_OK) return st;
       MOE_HIP_TRY(launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream));
     }
@@ -943,6 +1029,37 @@ int32_t moe_stack_persistent_active(const moe_stack* stack, int32_t* active) {
   clear_error();
   MOE_REQUIRE(stack && active, "null argument");
   *active = (stack->persistent_ok && stack->persistent_enabled) ? 1 : 0;
+  return MOE_OK;
+}
+
+int32_t moe_stack_epoch(const moe_stack* stack, uint32_t* epoch) {
+  clear_error();
+  MOE_REQUIRE(stack && epoch, "null argument");
+  *epoch = stack->epoch;
+  return MOE_OK;
+}
+
+int32_t moe_stack_advance_epoch(moe_stack* stack, uint32_t n) {
+  clear_error();
+  MOE_REQUIRE(stack, "null argument");
+  MOE_REQUIRE(stack->ps_mem, "the stack has no persistent path");
+  MOE_HIP_TRY(hipDeviceSynchronize());
+  std::vector<uint32_t> ep(stack->grid);
+  MOE_HIP_TRY(hipMemcpy(ep.data(), stack->ps.epochs, ep.size() * 4, hipMemcpyDeviceToHost));
+  for (uint32_t& v : ep) {
+    if (v != stack->epoch) return fail(MOE_E_HIP, "device call counter %u, host %u", v, stack->epoch);
+    v += n;
+  }
+  MOE_HIP_TRY(hipMemcpy(stack->ps.epochs, ep.data(), ep.size() * 4, hipMemcpyHostToDevice));
+  stack->epoch += n;
+  return MOE_OK;
+}
+
+int32_t moe_stack_set_timeout(moe_stack* stack, int64_t microseconds) {
+  clear_error();
+  MOE_REQUIRE(stack && microseconds >= 0, "bad argument");
+  MOE_REQUIRE(stack->ps_mem, "the stack has no persistent path");
+  stack->ps.timeout_ticks = stack->clk_khz * microseconds / 1000;
   return MOE_OK;
 }
 

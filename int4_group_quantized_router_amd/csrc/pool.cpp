@@ -148,7 +148,7 @@ struct slotpool {
   std::vector<uint8_t*> bounce;                // file store: page-aligned ordinary memory
   bool read_via_bounce = false;
   int64_t tick = 0;
-  slotpool_stats stats{};
+  slotpool_counters stats{};
 
   int64_t key(int32_t l, int32_t e) const { return (int64_t)l * store->experts + e; }
   VictimKey vkey(int32_t s) const {
@@ -271,6 +271,20 @@ int32_t pool_apply_pending(slotpool* p) {
   p->pend.clear();
   p->pend_marks.clear();
   return st;
+}
+
+int32_t pool_check_layer(const slotpool* p, int32_t layer_index, int32_t experts,
+                         int64_t stride) {
+  const expert_store* st = p->store;
+  if (layer_index < 0 || layer_index >= st->layers)
+    return fail(MOE_E_INVAL, "layer_index %d outside the pool's store of %d layers", layer_index,
+                st->layers);
+  if (experts != st->experts)
+    return fail(MOE_E_INVAL, "layer has %d experts, the pool's store %d", experts, st->experts);
+  if (stride != st->stride)
+    return fail(MOE_E_INVAL, "layer's blob stride %lld differs from the pool's store stride %lld",
+                (long long)stride, (long long)st->stride);
+  return MOE_OK;
 }
 
 int32_t pool_before_lookup(slotpool* p, hipStream_t stream) {
@@ -748,13 +762,17 @@ int32_t slotpool_flush(slotpool* pool) {
   return push_table(pool, nullptr);
 }
 
-int32_t slotpool_get_stats(const slotpool* pool, slotpool_stats* out) {
+int32_t slotpool_stats(const slotpool* pool, slotpool_counters* out) {
   clear_error();
   MOE_REQUIRE(pool && out, "null argument");
   // hits held back by a stack call are part of the pool's logical state
   MOE_POOL_APPLY(const_cast<slotpool*>(pool));
   *out = pool->stats;
   return MOE_OK;
+}
+
+int32_t slotpool_get_stats(const slotpool* pool, slotpool_counters* out) {
+  return slotpool_stats(pool, out);
 }
 
 int32_t slotpool_slot_of(const slotpool* pool, int32_t layer, int32_t expert, int32_t* slot) {

@@ -184,9 +184,9 @@ struct Shape {
   static_assert(H <= 2048 && H % 256 == 0, "router row in one wave");
 };
 
-// POOL: routed blobs come from the pool's device table (a.res_tab) and the
-// call may start at a.l0 > 0; the resident instance reads routed_base and
-// always starts at layer 0.
+// POOL: routed blobs come from each layer's row of the pool's device table
+// (StackLayerDesc::res_row) and the call may start at a.l0 > 0; the resident
+// instance reads routed_base and always starts at layer 0.
 template <class S, int VPL, bool POOL>
 __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   using F = typename S::F;
@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     if (rrow < E && D0.rb) rbv = ldf(D0.rb + rrow);
   }
 
+  int l_fail = a.L;  // the layer a wait ran out of time in
   for (int l = l0; l < a.L && !failed; ++l) {
     const StackLayerDesc D = s_layers[l];
 
@@ -269,6 +270,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
       } else if (!poll_y<H>(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, tag, yv, deadline)) {
         failed = true;
+        l_fail = l;
         break;
       }
       // sum of squares in the per-layer router's order (256 threads)
@@ -433,8 +435,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
         if (lane == 0) s_w[K] = a.has_wsg ? 1.0f / (1.0f + expf(-vs)) : 0.f;
         if (POOL) {  // pool mode: the chosen blobs, if all resident
-          const uint8_t* addr =
-              lane < K ? a.res_tab[(size_t)l * E + s_sel[lane]] : nullptr;
+          const uint8_t* addr = lane < K ? D.res_row[s_sel[lane]] : nullptr;
           if (lane < K) s_addr[lane] = addr;
           const bool miss = __ballot(lane < K && addr == nullptr) != 0ull;
           if (lane == 0) s_stop = miss ? 1 : 0;
@@ -459,6 +460,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     __syncthreads();
     if (s_abort) {
       failed = true;
+        l_fail = l;
       break;
     }
     if (POOL && s_stop) {  // the same decision in every workgroup
@@ -576,6 +578,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     };
     if (!poll_h<K * I / 2, IS / 2>(hrep, tag16, hl, deadline, hsh)) {
       failed = true;
+        l_fail = l;
       break;
     }
     __syncthreads();
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     h_request<0, K * I / 2>(hrep, 0u, hrt);
     if (!poll_h<0, K * I / 2>(hrep, tag16, hl, deadline, hrt)) {
       failed = true;
+        l_fail = l;
       break;
     }
     __syncthreads();
@@ -610,10 +614,28 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     // workgroup barrier.
   }
 
+  if (failed) {
+    // the rows this workgroup owns become NaN in the call's outputs (the
+    // final bf16 output and the f32 output of every layer from the one that
+    // failed on), so a call that ran out of time never leaves valid-looking
+    // data; the host reports the error
+    for (int r = tid; r < R; r += kNT) {
+      a.y_last[row0 + r] = (uint16_t)0x7FC0u;
+      if (a.y_layers)
+        for (int lf = l_fail; lf < a.L; ++lf)
+          a.y_layers[(size_t)lf * H + row0 + r] = __uint_as_float(0x7FC00000u);
+    }
+  }
   if (tid == 0) {
     if (failed) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     st_dev(a.epochs + blk, epoch + 1u);
   }
+}
+
+// Zero-fill of n 32-bit words (hand-off buffers whose tags could alias).
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0u;
 }
 
 template <class S, int VPL, bool POOL>
@@ -627,7 +649,7 @@ hipError_t launch_mode(const StackArgs& a, hipStream_t s) {
 
 template <class S, int VPL>
 hipError_t launch_shape(const StackArgs& a, hipStream_t s) {
-  return a.res_tab ? launch_mode<S, VPL, true>(a, s) : launch_mode<S, VPL, false>(a, s);
+  return a.pool ? launch_mode<S, VPL, true>(a, s) : launch_mode<S, VPL, false>(a, s);
 }
 
 // The instances: (bits, H, I, Is, k) x top-k width (64 * VPL >= E).
@@ -653,6 +675,14 @@ bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cu
   MOE_STACK_SHAPES(MOE_STACK_MATCH)
 #undef MOE_STACK_MATCH
   return false;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,

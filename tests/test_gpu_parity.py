@@ -211,12 +211,15 @@ def test_expert_forward(torch, name, H, I, T):
 
 # -------------------------------------------------------------------- layer
 
-def _layer_case(torch, cfg, calls, layer=0):
-    """Run the layer on calls = [token-id lists] and compare every token."""
+def _layer_case(torch, cfg, calls, layer=0, max_undecided=1):
+    """Run the layer on calls = [token-id lists] and compare every token whose
+    routing equals the oracle's; at most `max_undecided` tokens may differ
+    in routing (each only where the f32 error bound leaves the choice open)."""
     import int4_group_quantized_router_amd as m
     dm = DeviceModel(cfg, layers=layer + 1)
     L = dm.make_layers()[layer]
     worst = 0.0
+    total = compared = 0
     try:
         for toks in calls:
             T = len(toks)
@@ -232,14 +235,17 @@ def _layer_case(torch, cfg, calls, layer=0):
                 ref = oracle_layer(cfg, layer, xb[i])
                 x = O.bf16_to_f64(xb[i])
                 check_routing(idx.cpu().numpy()[i], None, x, Wr, rb, cfg.top_k)
+                total += 1
                 if np.array_equal(idx.cpu().numpy()[i], ref["idx"]):
+                    compared += 1
                     err = rel_err(y32.cpu().numpy()[i], ref["y"])
                     worst = max(worst, err)
                     assert err <= REL_TOL, (toks, i, err)
             check_bf16_of_f32(y16.cpu().numpy(), y32.cpu().numpy())
     finally:
         dm.destroy()
-    _print("worst rel err", worst)
+    _print("worst rel err", worst, "tokens compared", compared, "/", total)
+    assert compared >= total - max_undecided, (compared, total)
     return worst
 
 
@@ -596,6 +602,190 @@ def test_pool_stack_persistent_equals_per_layer(torch, cap):
         for p in pools:
             m.slotpool_destroy(p)
         m.expert_store_destroy(store)
+
+
+def _stack_outputs(torch, m, st, cfg, tok):
+    """One token through a stack: (y_last, x_layers, y_layers, idx, w) on the host."""
+    H, k, L = cfg.hidden, cfg.top_k, len(st.keep)
+    x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+    xl = torch.empty((L, 1, H), dtype=torch.int16, device="cuda")
+    yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, 1, k), dtype=torch.float32, device="cuda")
+    y = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx, w=w)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in (y, xl, yl, idx, w)]
+
+
+def test_pool_stack_layer_indices_offset_and_permuted(torch):
+    """Pooled stacks whose layers draw on store layers other than 0..n-1 (a
+    permutation of the store's layers, and an offset run of two of them):
+    the persistent kernel looks each layer's choices up in that layer's own
+    row of the pool's table, so it equals the per-layer pooled path bit for
+    bit and leaves the pool in the same state."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=4)
+    _print("pooled stack, layer indices permuted / offset")
+    dm = DeviceModel(cfg, resident=False)
+    store, _ = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    try:
+        for order in ([2, 0, 3, 1], [1, 2]):
+            pools = [m.slotpool_create(store, 30, 0), m.slotpool_create(store, 30, 0)]
+            stacks = []
+            for p in pools:
+                layers = []
+                for l in order:
+                    d = dims_of(cfg)
+                    d["layer_index"] = l
+                    layers.append(m.moe_layer_create(d, dm.Wr[l], dm.rb[l], dm.shared[l], dm.wsg[l],
+                                                     pool=p))
+                stacks.append(m.moe_stack_create(layers))
+            m.moe_stack_set_persistent(stacks[1], False)
+            assert m.moe_stack_persistent_active(stacks[0])
+            try:
+                for tok in [0, 0, 1, 2, 1, 0]:
+                    a = _stack_outputs(torch, m, stacks[0], cfg, tok)
+                    b = _stack_outputs(torch, m, stacks[1], cfg, tok)
+                    for u, v in zip(a, b):
+                        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), (order, tok)
+                    st0, st1 = ({k: v for k, v in m.slotpool_stats(p).items() if k != "read_ns"}
+                                for p in pools)
+                    assert st0 == st1, (order, tok, st0, st1)
+                for l in range(cfg.layers):
+                    for e in range(cfg.experts):
+                        assert m.slotpool_slot_of(pools[0], l, e) == m.slotpool_slot_of(pools[1], l, e)
+                # a store layer the stack does not use is never touched
+                unused = [l for l in range(cfg.layers) if l not in order]
+                for l in unused:
+                    assert all(m.slotpool_slot_of(pools[0], l, e) == -1 for e in range(cfg.experts))
+            finally:
+                for st in stacks:
+                    for L in st.keep:
+                        m.moe_layer_destroy(L)
+                    m.moe_stack_destroy(st)
+                for p in pools:
+                    m.slotpool_destroy(p)
+    finally:
+        m.expert_store_destroy(store)
+
+
+def test_pool_layer_must_match_store(torch):
+    """A pooled layer is checked against its pool's store before any launch:
+    its layer index must exist there, its expert count and blob stride must
+    equal the store's."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import _lib
+    cfg = CONFIGS["tiny"].replace(layers=2)
+    stride = m.moe_blob_layout_get(cfg.hidden, cfg.inter, cfg.bits)["stride"]
+    store = m.expert_store_create(cfg.layers, cfg.experts, stride)
+    pool = m.slotpool_create(store, 4, 0)
+    dm = DeviceModel(cfg, resident=False)
+    try:
+        from harness import dims_of
+        for bad in ({"layer_index": 2}, {"experts": 32}, {"inter": 128}):
+            d = dict(dims_of(cfg), layer_index=0)
+            d.update(bad)
+            with pytest.raises(m.MoEError) as ei:
+                m.moe_layer_create(d, dm.Wr[0], dm.rb[0], dm.shared[0], dm.wsg[0], pool=pool)
+            assert ei.value.status == _lib.MOE_E_INVAL, bad
+        ok = m.moe_layer_create(dict(dims_of(cfg), layer_index=1), dm.Wr[1], dm.rb[1],
+                                dm.shared[1], dm.wsg[1], pool=pool)
+        m.moe_layer_destroy(ok)
+    finally:
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
+def test_stack_stale_handoff_words_never_match(torch):
+    """The persistent kernel's h hand-off words carry a 15-bit launch tag.  A
+    pooled call that stops at a layer leaves that layer's routed h words from
+    an earlier launch; here the launch count is advanced so that a later
+    launch's tag equals theirs, and that launch must still equal the
+    resident stack bit for bit (the host clears words that old)."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from harness import dims_of
+    cfg = CONFIGS["tiny"].replace(layers=2)
+    _print("stale hand-off words", cfg.name)
+    dm = DeviceModel(cfg)
+    store, _ = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    pool = m.slotpool_create(store, cfg.layers * cfg.experts, 0)
+    s_res = m.moe_stack_create(dm.make_layers())
+    s_pool = m.moe_stack_create(dm.make_layers(pool=pool))
+    assert m.moe_stack_persistent_active(s_pool) and m.moe_stack_persistent_active(s_res)
+    try:
+        tok_a = 0
+        _stack_outputs(torch, m, s_pool, cfg, tok_a)           # fills A's experts
+        e_a = m.moe_stack_epoch(s_pool)
+        _stack_outputs(torch, m, s_pool, cfg, tok_a)           # one launch through both layers
+        assert m.moe_stack_epoch(s_pool) == e_a + 1
+        # a token whose experts are not all resident: the kernel stops at a layer
+        tok_b = next(t for t in range(1, 64)
+                     if any(set(r) - set(q) for r, q in zip(
+                         _stack_outputs(torch, m, s_res, cfg, t)[3][:, 0].tolist(),
+                         _stack_outputs(torch, m, s_res, cfg, tok_a)[3][:, 0].tolist())))
+        want = _stack_outputs(torch, m, s_res, cfg, tok_b)
+        miss0 = m.slotpool_stats(pool)["misses"]
+        got = _stack_outputs(torch, m, s_pool, cfg, tok_b)
+        assert m.slotpool_stats(pool)["misses"] > miss0
+        for u, v in zip(got, want):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+        # next launch gets the tag of the launch that last wrote the stopped
+        # layer's routed h words
+        m.moe_stack_advance_epoch(s_pool, e_a + 32768 - m.moe_stack_epoch(s_pool))
+        for rep in range(3):
+            e0 = m.moe_stack_epoch(s_pool)
+            got = _stack_outputs(torch, m, s_pool, cfg, tok_b)
+            assert m.moe_stack_epoch(s_pool) == e0 + 1  # all resident: one launch
+            for u, v in zip(got, want):
+                assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), rep
+            m.moe_stack_advance_epoch(s_pool, 32767)
+        # the resident stack, advanced a whole tag period, is unaffected too
+        m.moe_stack_advance_epoch(s_res, 32767)
+        got = _stack_outputs(torch, m, s_res, cfg, tok_b)
+        for u, v in zip(got, want):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    finally:
+        m.moe_stack_destroy(s_res)
+        m.moe_stack_destroy(s_pool)
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
+def test_stack_timeout_poisons_outputs(torch):
+    """Failure handling of the persistent kernel, forced from the host with
+    a zero bound on every wait (each wait returns at its first unmet poll,
+    so every workgroup still leaves): the call's outputs hold NaN, the error
+    comes back on the next call, and after the bound is restored the stack
+    gives the per-layer result again."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import _lib
+    cfg = CONFIGS["tiny"].replace(layers=3)
+    _print("stack timeout", cfg.name)
+    dm = DeviceModel(cfg)
+    st = m.moe_stack_create(dm.make_layers())
+    try:
+        m.moe_stack_set_persistent(st, False)
+        want = _stack_outputs(torch, m, st, cfg, 5)
+        m.moe_stack_set_persistent(st, True)
+        m.moe_stack_set_timeout(st, 0)
+        got = _stack_outputs(torch, m, st, cfg, 5)
+        y16 = got[0].view(np.uint16)
+        assert np.any(y16 == 0x7FC0) or np.any(np.isnan(got[2])), "no output marked"
+        with pytest.raises(m.MoEError) as ei:
+            _stack_outputs(torch, m, st, cfg, 5)
+        assert ei.value.status == _lib.MOE_E_HIP and "timed out" in str(ei.value)
+        m.moe_stack_set_timeout(st, 2_000_000)
+        for _ in range(2):
+            got = _stack_outputs(torch, m, st, cfg, 5)
+            for u, v in zip(got, want):
+                assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    finally:
+        m.moe_stack_destroy(st)
+        dm.destroy()
 
 
 def test_pool_shared_by_two_streams_bitwise(torch):
