@@ -170,6 +170,20 @@ int32_t moe_expert_forward(const uint16_t* x, int32_t T, const moe_qshape* shape
                            const void* blob, const float* coef, float* y_accum,
                            hipStream_t stream);
 
+/* moe_expert_forward without any allocation, for callers that cannot
+ * allocate device memory: code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results
+ * (bit for bit) as moe_expert_forward; h goes to a fixed array of the
+ * library of MOE_NOALLOC_MAX_H bf16 values per device (32 KiB, held until
+ * the process ends) instead of stream-ordered scratch.  MOE_E_INVAL if
+ * T * shape->inter > MOE_NOALLOC_MAX_H (and as moe_expert_forward
+ * otherwise).  Every call on a device uses the same array: calls that
+ * overlap on one device (other streams, other threads) race. */
+#define MOE_NOALLOC_MAX_H (MOE_MAX_DECODE_T * 2048)
+int32_t moe_expert_forward_noalloc(const uint16_t* x, int32_t T, const moe_qshape* shape,
+                                   const void* blob, const float* coef, float* y_accum,
+                                   hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Fixed-stride expert store in pinned host memory: L*E blobs of `stride`
  * bytes ([xix] how-it-works paragraph: fixed-stride blobs in a .qpack

@@ -172,6 +172,19 @@ def moe_expert_forward(x, hidden: int, inter: int, bits: int, blob, coef, y_accu
     return y_accum
 
 
+def moe_expert_forward_noalloc(x, hidden: int, inter: int, bits: int, blob, coef, y_accum,
+                               stream=None, group: int = 64):
+    """moe_expert_forward with h in the library's fixed per-device array (no
+    allocation); returns y_accum."""
+    import torch
+    _check(_lib_().moe_expert_forward_noalloc(
+        _dptr(x, _bf16_types(), "x"), x.shape[0], C.byref(_shape(hidden, inter, bits, group)),
+        _dptr(blob), _dptr(coef, (torch.float32,), "coef"),
+        _dptr(y_accum, (torch.float32,), "y_accum"), _stream(stream)),
+        "moe_expert_forward_noalloc")
+    return y_accum
+
+
 # ------------------------------------------------------------ store / pool
 
 def expert_store_create(layers: int, experts: int, stride: int) -> Handle:

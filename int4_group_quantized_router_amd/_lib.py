@@ -22,6 +22,7 @@ MOE_E_IO = -7
 MOE_MAX_TOPK = 16
 MOE_KERNEL_ROUTE, MOE_KERNEL_GATE_UP, MOE_KERNEL_DOWN, MOE_KERNEL_STACK = 0, 1, 2, 3
 MOE_MAX_DECODE_T = 8
+MOE_NOALLOC_MAX_H = MOE_MAX_DECODE_T * 2048
 
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_E_INVAL", -2: "MOE_E_NOMEM", -3: "MOE_E_HIP",
                 -4: "MOE_E_RANGE", -5: "MOE_E_POOL_EXHAUSTED", -6: "MOE_E_BUSY",
@@ -67,6 +68,7 @@ SIGNATURES = {
     "moe_route_topk": [_P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P],
     "moe_dequant": [_P, C.POINTER(QShape), _I32, _P, _P, _P],
     "moe_expert_forward": [_P, _I32, C.POINTER(QShape), _P, _P, _P, _P],
+    "moe_expert_forward_noalloc": [_P, _I32, C.POINTER(QShape), _P, _P, _P, _P],
     "expert_store_create": [_I32, _I32, _I64, C.POINTER(_P)],
     "expert_store_write": [_P, _I32, _I32, _P, _I64],
     "expert_store_host_ptr": [_P, _I32, _I32, C.POINTER(_P)],
