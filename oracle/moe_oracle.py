@@ -248,6 +248,42 @@ def moe_layer_tokens(X_bits, Wr, rb, wsg, shared: dict, expert_fn, k: int,
     return {"y": y, "idx": idx, "w": w, "logits": logits, "sigma": sigma}
 
 
+# ------------------------------------------------- grouping rows by expert
+
+def sort_by_expert(idx, E: int):
+    """Group the (token, choice) pairs of a routed batch by expert.
+
+    Routing sends each token to k experts ([xix] how-it-works paragraph;
+    [lens] "エキスパートストリーミングの仕組み"); to run each expert once on
+    all its tokens, the pairs are grouped by expert.  Pair p = t*k + j is the
+    j-th choice of token t.  Counting sort: count the pairs per expert, turn
+    the counts into first rows (exclusive prefix sums), then walk the pairs
+    in order p = 0, 1, ... and put each at its expert's next free row, so
+    an expert's rows keep (token, choice) order (reading: the pages give no
+    order; this one makes the grouping unique).
+
+    Returns (perm, offsets): perm[r] = the pair in row r, int64 [T*k];
+    offsets[e] = first row of expert e, offsets[E] = T*k, int64 [E+1].
+    Pairs whose expert lies outside [0, E) are left out (and offsets[E]
+    counts only the others).
+    """
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    counts = [0] * E
+    for e in flat.tolist():
+        if 0 <= e < E:
+            counts[e] += 1
+    offsets = [0] * (E + 1)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    cursor = offsets[:E]
+    perm = [0] * offsets[E]
+    for p, e in enumerate(flat.tolist()):
+        if 0 <= e < E:
+            perm[cursor[e]] = p
+            cursor[e] += 1
+    return np.asarray(perm, dtype=np.int64), np.asarray(offsets, dtype=np.int64)
+
+
 # ------------------------------------------------------ stacked-layer rescale
 
 def rms_rescale(y_f32) -> np.ndarray:

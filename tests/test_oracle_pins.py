@@ -375,3 +375,48 @@ def test_rms_rescale_unit_rms_and_rounding():
     ref = y.astype(np.float64) / np.sqrt(np.mean(y.astype(np.float64) ** 2) + 1e-6)
     ulp = np.ldexp(1.0, np.frexp(ref)[1] - 8)
     assert np.all(np.abs(x - ref) <= ulp * 0.5 + np.abs(ref) * 1e-6)
+
+
+# ------------------------------------------------------- grouping by expert
+
+def test_sort_by_expert_hand_worked():
+    """3 tokens, k = 2, E = 3: pairs p = t*k + j choose experts 2,0 | 0,1 |
+    2,1; grouped by expert with (token, choice) order kept inside each
+    expert: expert 0 <- pairs 1, 2; expert 1 <- 3, 5; expert 2 <- 0, 4."""
+    perm, off = O.sort_by_expert(np.array([[2, 0], [0, 1], [2, 1]]), 3)
+    assert perm.tolist() == [1, 2, 3, 5, 0, 4]
+    assert off.tolist() == [0, 2, 4, 6]
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (7, 2, 16, 1), (50, 4, 8, 2),
+                                        (33, 10, 512, 3), (200, 3, 5, 4)])
+def test_sort_by_expert_against_comparison_sort(T, k, E, seed):
+    """Brute force: Python's comparison sort of the pairs by (expert, pair
+    index); offsets from counting each expert's rows in that order; every
+    row's pair chose the expert of its segment; perm is a permutation."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, size=(T, k))
+    if T > 3:
+        idx[: T // 2, 0] = idx[0, 0]  # a crowded expert
+    perm, off = O.sort_by_expert(idx, E)
+    flat = idx.reshape(-1).tolist()
+    want = sorted(range(T * k), key=lambda p: (flat[p], p))
+    assert perm.tolist() == want
+    assert sorted(perm.tolist()) == list(range(T * k))
+    assert off[0] == 0 and off[E] == T * k and np.all(np.diff(off) >= 0)
+    for e in range(E):
+        rows = perm[off[e]:off[e + 1]]
+        assert all(flat[p] == e for p in rows)
+        assert np.all(np.diff(rows) > 0)
+        assert off[e + 1] - off[e] == flat.count(e)
+
+
+def test_sort_by_expert_edge_cases():
+    """No pairs; a single expert taking every pair; experts outside [0, E)
+    are left out and offsets count only the rest."""
+    perm, off = O.sort_by_expert(np.zeros((0, 4), np.int64), 6)
+    assert perm.size == 0 and off.tolist() == [0] * 7
+    perm, off = O.sort_by_expert(np.full((5, 2), 3), 4)
+    assert perm.tolist() == list(range(10)) and off.tolist() == [0, 0, 0, 0, 10]
+    perm, off = O.sort_by_expert(np.array([[1, -1], [4, 0], [1, 2]]), 3)
+    assert perm.tolist() == [3, 0, 4, 5] and off.tolist() == [0, 1, 3, 4]
