@@ -1,11 +1,17 @@
 #!/usr/bin/env python3
 """Batch-1 decode benchmark of the group-quantised MoE layer stack on one GPU.
 
-Workload (default ``decode35b``): 40 stacked MoE layers shaped like the 35B-A3B
-model (hidden 2048, 256 experts, top-8, expert and shared intermediate 512,
-int4 group 64, Zipf(1.1) routing bias), all experts resident in HBM, tokens
-processed one at a time.  One step = one token through all 40 layers
-(router + gate/up + down/combine per layer, RMS rescale between layers).
+Workload (default ``decode80b_int8``): 48 stacked MoE layers shaped like the
+80B-A3B model (hidden 2048, 512 experts, top-10, expert and shared
+intermediate 512, affine int8 group 64, Zipf(1.1) routing bias), all experts
+resident in HBM, tokens processed one at a time -- the largest batch-1 decode
+configuration of the workload set.  One step = one token through all 48
+layers (router + gate/up + down/combine per layer, RMS rescale between
+layers).  After the timed batch-1 steps the same stack also runs 64 steps of
+8 tokens (reported under ``config.batch8``, not part of ``value``).
+``--workload decode35b`` runs the 35B-shaped int4 stack (40 layers, 256
+experts, top-8) instead; ``stream80b`` and ``prefill80b`` have their own
+modes.
 
 One-token calls run as ONE persistent kernel per token (all layers in one
 launch; ``--per-layer`` runs the three kernels per layer instead).
@@ -15,8 +21,9 @@ Prints one JSON line: tokens/s, plus
   ``--per-layer``, the gate/up dequant-GEMV kernel, the largest share of the
   bytes): algorithmic bytes per launch / its mean launch time, measured with
   HIP events around every launch of it in the timed steps, against 8 TB/s;
+  the same for the quantised expert bytes alone (``expert_quantized_*``);
 * ``cpu_baseline``: the float64 CPU oracle on a bounded sample (one token
-  through all layers), converted to tokens/s.
+  through as many layers as fit the budget), converted to tokens/s.
 """
 
 from __future__ import annotations
@@ -36,19 +43,40 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_COPY_GBS = 5105.0
 MEASURED_BF16_MM_TFLOPS = 1213.0
 
-# HBM counters of the persistent stack kernel on the 40-layer 35B-shaped
-# stack (profiles/decode35b_stack_decode_kernel.md), per launch, with the
-# factors that map a plain copy's counter readings onto its byte count.
-STACK_TRAFFIC = {
-    "decode35b": {"fetch_kib": 362065, "write_kib": 53786,
-                  "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
+# HBM counters (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of the dominant
+# kernel of a workload, from two rocprofv3 --pmc runs of this benchmark, with
+# the factors that map a plain copy's counter readings onto its byte count
+# (bench.py --calibrate-copy).  Each entry names the digest of the kernel
+# sources it was taken on; once those sources change the reading no longer
+# describes the kernel and ``traffic`` is reported as null.
+COPY_FETCH_SCALE = 262144 / 131084
+COPY_WRITE_SCALE = 262144 / 262144
+KERNEL_SOURCES = {
+    "stack": ("stack.hip", "gemv.h", "device.h", "kernels.h"),
+    "prefill_gu": ("prefill.hip", "device.h", "kernels.h"),
 }
-# The same for the gate/up grouped GEMM of the 4096-token prefill layer
-# (profiles/prefill80b_grouped_gemm.md).
-PREFILL_TRAFFIC = {
-    "prefill80b": {"fetch_kib": 617559, "write_kib": 45056,
-                   "fetch_scale": 262144 / 131084, "write_scale": 262144 / 262144},
+TRAFFIC = {
+    # workload: (kernel, fetch KiB, write KiB, source digest)
 }
+
+
+def kernel_digest(kind):
+    """sha256 (16 hex digits) over the sources of a kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "int4_group_quantized_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kind):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, or None when no
+    reading was taken on the current sources."""
+    t = TRAFFIC.get(workload)
+    if not t or t[0] != kind or t[3] != kernel_digest(kind):
+        return None
+    return (t[1] * COPY_FETCH_SCALE + t[2] * COPY_WRITE_SCALE) * 1024
 
 
 def log(*a):
@@ -62,9 +90,10 @@ def algorithmic_bytes(cfg):
     gate_up = k * 2 * mat(I, H) + 2 * mat(Is, H) + H * 2 + (k * I + Is) * 2
     down = k * mat(H, I) + mat(H, Is) + (k * I + Is) * 2 + H * 4 + H * 2
     route = E * H * 4 + E * 4 + H * 4 + H * 4
-    quant = (k + 1) * 3 * mat(I, H) if I == Is else k * 3 * mat(I, H) + 3 * mat(Is, H)
+    quant = k * 3 * mat(I, H) + 3 * mat(Is, H)
     return {"route": route, "gate_up": gate_up, "down": down,
-            "layer": route + gate_up + down, "expert_quantized": quant}
+            "layer": route + gate_up + down, "expert_quantized": quant,
+            "gate_up_quantized": k * 2 * mat(I, H) + 2 * mat(Is, H)}
 
 
 def prefill_flops(cfg, T):
@@ -200,7 +229,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode35b")
+    ap.add_argument("--workload", default="decode80b_int8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true",
                     help="decode: three kernels per layer instead of one persistent kernel")
@@ -222,15 +251,11 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy)
     if args.calibrate_peaks:
         return calibrate_peaks()
-    import int4_group_quantized_router_amd as m
-    from int4_group_quantized_router_amd import weights as W
-    from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
+    from moe_inputs import CONFIGS
 
     cfg = CONFIGS[args.workload]
     if args.layers:
@@ -239,25 +264,23 @@ def main():
         return bench_prefill(args, cfg)
     if not cfg.resident:
         return bench_stream(args, cfg)
-    if cfg.name != "decode35b":
-        return bench_decode_other(args, cfg)
+    return bench_decode(args, cfg)
+
+
+def bench_decode(args, cfg):
+    """Resident batch-1 decode of a stack (one persistent launch per token),
+    then, for the 80B-shaped int8 stack, 64 steps of 8 tokens."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from moe_inputs import tokens_x
     args.steps = 256 if args.steps is None else args.steps
     args.warmup = 16 if args.warmup is None else args.warmup
     assert cfg.batch == 1 and cfg.resident, "decode bench workload must be resident batch-1"
     torch.cuda.set_device(0)
-    dims = {"hidden": cfg.hidden, "experts": cfg.experts, "top_k": cfg.top_k,
-            "inter": cfg.inter, "shared_inter": cfg.shared_inter, "bits": cfg.bits}
-    log(f"[bench] building {cfg.name}: {cfg.layers} layers x {cfg.experts} experts")
+    log(f"[bench] building {cfg.name}: {cfg.layers} layers x {cfg.experts} experts, int{cfg.bits}")
     t_build = time.perf_counter()
-    routed, stride = W.upload_resident(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
-    layers, keep = [], []
-    for l in range(cfg.layers):
-        Wr, rb, wsg = (torch.from_numpy(a).cuda() for a in router_arrays(cfg, l))
-        sh = W.upload_blob(cfg.hidden, cfg.shared_inter, cfg.bits, shared_arrays(cfg, l))
-        keep += [Wr, rb, wsg, sh]
-        layers.append(m.moe_layer_create(dict(dims, layer_index=l), Wr, rb, sh, wsg,
-                                         resident_base=routed))
-    stack = m.moe_stack_create(layers)
+    layers, stack, keep = _build_stack(cfg)
     if args.per_layer:
         m.moe_stack_set_persistent(stack, False)
     persistent = m.moe_stack_persistent_active(stack)
@@ -308,16 +331,30 @@ def main():
         k_name = (f"stack_decode_kernel (one token through all {cfg.layers} layers: router, "
                   f"top-k, dequant-GEMV gate/up + down, combine)")
         k_bytes = per_token_bytes
+        k_quant = ab["expert_quantized"] * cfg.layers
+        traffic = counter_traffic(cfg.name, "stack")
     else:
         k_name = "gate_up_kernel (dequant-GEMV gate+up, fused SiLU*up)"
         k_bytes = ab["gate_up"]
+        k_quant = ab["gate_up_quantized"]
+        traffic = None
     achieved = k_bytes / k_mean_s / 1e9
-    traffic = None
-    if persistent and cfg.name in STACK_TRAFFIC:
-        t = STACK_TRAFFIC[cfg.name]
-        traffic = (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
     log(f"[bench] {tok_s:.1f} tok/s, {elapsed / args.steps * 1e3:.3f} ms/token, "
-        f"kernel mean {k_mean_s * 1e6:.2f} us over {len(gu_ms)} launches")
+        f"kernel mean {k_mean_s * 1e6:.2f} us over {len(gu_ms)} launches, "
+        f"{achieved:.0f} GB/s all bytes, {k_quant / k_mean_s / 1e9:.0f} GB/s quantised expert bytes")
+
+    batch8 = None
+    if cfg.name == "decode80b_int8" and not args.per_layer:
+        # the configuration's second decode shape: 8 tokens per step (the
+        # per-layer kernels; each distinct expert of a layer read once)
+        steps8, warm8 = 64, 4
+        n8 = (warm8 + steps8) * 8
+        X8 = torch.from_numpy(tokens_x(cfg, 0, n8).view(np.int16)).cuda()
+        Y8 = torch.empty((n8, cfg.hidden), dtype=torch.int16, device="cuda")
+        dt8 = _run_tokens(m, stack, X8, Y8, 8, warm8, steps8)
+        batch8 = {"tokens_per_s": steps8 * 8 / dt8, "ms_per_step": dt8 / steps8 * 1e3,
+                  "steps": steps8, "warmup": warm8, "path": "per-layer kernels (T = 8)"}
+        log(f"[bench] batch 8: {batch8['tokens_per_s']:.1f} tok/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -335,7 +372,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 weights (bf16 dequant pairs), f32 accumulate, bf16 I/O",
+        "dtype": f"int{cfg.bits} weights (affine group 64), f32 accumulate, bf16 I/O",
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {
             "workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden {cfg.hidden}, "
@@ -345,6 +382,7 @@ def main():
             "launch": "one persistent kernel per token" if persistent else "3 kernels per layer",
             "batch": 1, "layers": cfg.layers, "tokens_timed": args.steps,
             "bytes_per_token": per_token_bytes,
+            "quantized_expert_bytes_per_token": ab["expert_quantized"] * cfg.layers,
             "stack_GBps": per_token_bytes * tok_s / 1e9,
             "stack_frac_of_hbm_peak": per_token_bytes * tok_s / 1e9 / HBM_PEAK_GBS,
             "stack_frac_of_measured_copy": per_token_bytes * tok_s / 1e9 / MEASURED_COPY_GBS,
@@ -359,11 +397,17 @@ def main():
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "bytes_per_launch": k_bytes,
+            "expert_quantized_bytes_per_launch": k_quant,
+            "expert_quantized_GBps": k_quant / k_mean_s / 1e9,
+            "expert_quantized_frac": k_quant / k_mean_s / 1e9 / HBM_PEAK_GBS,
+            "frac_of_measured_copy": achieved / MEASURED_COPY_GBS,
             "mean_launch_us": k_mean_s * 1e6,
             "launches": int(len(gu_ms)),
         },
         "cpu_baseline": cpu,
     }
+    if batch8 is not None:
+        out["config"]["batch8"] = batch8
     if dn_ms is not None:
         # quantised expert bytes over the two expert kernels' mean durations
         t_exp = (float(np.mean(gu_ms)) + float(np.mean(dn_ms))) / 1e3
@@ -412,50 +456,6 @@ def _run_tokens(m, stack, X, Y, T, warmup, steps, after_warmup=None):
         m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
-
-
-def bench_decode_other(args, cfg):
-    """Resident decode of another stack shape (e.g. int8 experts), batch 1
-    (persistent kernel) and batch 8 (per-layer kernels)."""
-    import numpy as np
-    import torch
-    import int4_group_quantized_router_amd as m
-    from moe_inputs import tokens_x
-    warmup = 8 if args.warmup is None else args.warmup
-    # default: the workload's tokens one at a time, then 64 steps of 8 tokens
-    steps_of = {1: max(1, cfg.tokens - warmup) if args.steps is None else args.steps,
-                8: 64 if args.steps is None else args.steps}
-    torch.cuda.set_device(0)
-    log(f"[bench] building {cfg.name}: {cfg.layers} layers x {cfg.experts} experts, int{cfg.bits}")
-    layers, stack, keep = _build_stack(cfg)
-    ab = algorithmic_bytes(cfg)
-    res = {}
-    for T in (1, 8):
-        steps = steps_of[T]
-        n = (warmup + steps) * T
-        X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
-        Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
-        dt = _run_tokens(m, stack, X, Y, T, warmup, steps)
-        res[T] = {"tokens_per_s": steps * T / dt, "ms_per_step": dt / steps * 1e3, "steps": steps,
-                  "path": ("persistent stack kernel" if T == 1 and m.moe_stack_persistent_active(stack)
-                           else "per-layer kernels")}
-        log(f"[bench] T={T}: {res[T]['tokens_per_s']:.1f} tok/s ({res[T]['path']})")
-    per_token = ab["layer"] * cfg.layers
-    out = {"metric": f"MoE stack tokens/sec at batch 1 and 8, int{cfg.bits} experts, 1 GPU",
-           "value": res[1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps_of[1],
-           "warmup": warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": f"int{cfg.bits} weights, f32 accumulate, bf16 I/O",
-           "data": "synthetic (seeded; random-init weights of the stated shape)",
-           "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden {cfg.hidden}, "
-                                  f"{cfg.experts} experts top-{cfg.top_k}, intermediate {cfg.inter}, "
-                                  f"int{cfg.bits}, all resident",
-                      "batch1": res[1], "batch8": res[8],
-                      "bytes_per_token_batch1": per_token,
-                      "batch1_GBps": per_token * res[1]["tokens_per_s"] / 1e9}}
-    print(json.dumps(out), flush=True)
-    m.moe_stack_destroy(stack)
-    for L in layers:
-        m.moe_layer_destroy(L)
 
 
 def bench_stream(args, cfg):
@@ -597,10 +597,7 @@ def bench_prefill(args, cfg):
     for t in timers.values():
         m.moe_timer_destroy(t)
     gu_flops, dn_flops = prefill_flops(cfg, T)
-    traffic = None
-    if cfg.name in PREFILL_TRAFFIC and T == cfg.tokens:
-        t = PREFILL_TRAFFIC[cfg.name]
-        traffic = (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"]) * 1024
+    traffic = counter_traffic(cfg.name, "prefill_gu") if T == cfg.tokens else None
     achieved = gu_flops / (ms["gate_up"] / 1e3) / 1e12
     both = (gu_flops + dn_flops) / ((ms["gate_up"] + ms["down"]) / 1e3) / 1e12
     tok_s = T * steps / t_all

@@ -141,6 +141,26 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Group the (token, choice) pairs of a routed batch by expert: each token
+ * goes to k of E experts ([xix] how-it-works paragraph; [lens]
+ * "エキスパートストリーミングの仕組み"), and the many-token path runs each
+ * expert once on all of its rows, so rows are sorted by expert, keeping
+ * (token, choice) order inside an expert.  This is the sort the layer's
+ * many-token path runs before its grouped GEMMs.
+ *
+ * idx: device int32 [T, k] (a router's output); pair p = t*k + j.
+ * perm: device int32 [T*k] (out): perm[r] = the pair in sorted row r.
+ * offsets: device int32 [E + 1] (out): first row of expert e; offsets[E] =
+ * number of pairs sorted.  Pairs whose expert lies outside [0, E) are left
+ * out (perm rows from offsets[E] on are not written).  T = 0 zeroes
+ * offsets.  Scratch is stream-ordered (hipMallocAsync / hipFreeAsync on
+ * `stream`).  MOE_E_INVAL if k is not in [1, MOE_MAX_TOPK], E not in
+ * [1, 1024], T < 0, T * (k + 1) >= 2^30, or a needed pointer is NULL.
+ * ---------------------------------------------------------------------- */
+int32_t moe_expert_sort(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* perm,
+                        int32_t* offsets, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Dequantise one matrix of a device blob (test hook for the bit-exact
  * dequant check): the MLX-style affine group dequantisation the pages name
  * for the expert weights ([xix] lineage paragraph: MLX-style int4/int8

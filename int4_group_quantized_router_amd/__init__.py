@@ -147,6 +147,21 @@ def moe_route_topk(x, Wr, rb, k: int, wsg=None, with_sigma: bool = True, idx=Non
     return {"idx": idx, "w": w, "sigma": sigma, "logits": logits}
 
 
+def moe_expert_sort(idx, E: int, perm=None, offsets=None, stream=None):
+    """Group the (token, choice) pairs of idx (device int32 [T, k]) by expert;
+    returns (perm [T*k], offsets [E+1]) device int32 tensors."""
+    import torch
+    T, k = idx.shape
+    perm = perm if perm is not None else torch.empty(T * k, dtype=torch.int32, device=idx.device)
+    offsets = offsets if offsets is not None else torch.empty(E + 1, dtype=torch.int32,
+                                                               device=idx.device)
+    _check(_lib_().moe_expert_sort(_dptr(idx, (torch.int32,), "idx"), T, k, int(E),
+                                   _dptr(perm, (torch.int32,), "perm"),
+                                   _dptr(offsets, (torch.int32,), "offsets"), _stream(stream)),
+           "moe_expert_sort")
+    return perm, offsets
+
+
 def moe_dequant(blob, hidden: int, inter: int, bits: int, which: int, want_bf16: bool = True,
                 stream=None, group: int = 64):
     """Dequantise matrix `which` (0 gate, 1 up, 2 down) of a device blob."""

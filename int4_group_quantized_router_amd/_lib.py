@@ -66,6 +66,7 @@ SIGNATURES = {
     "moe_blob_pack": [C.POINTER(QShape), C.POINTER(QMatrixHost), C.POINTER(QMatrixHost),
                       C.POINTER(QMatrixHost), _P],
     "moe_route_topk": [_P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P, _P, _P],
+    "moe_expert_sort": [_P, _I32, _I32, _I32, _P, _P, _P],
     "moe_dequant": [_P, C.POINTER(QShape), _I32, _P, _P, _P],
     "moe_expert_forward": [_P, _I32, C.POINTER(QShape), _P, _P, _P, _P],
     "moe_expert_forward_noalloc": [_P, _I32, C.POINTER(QShape), _P, _P, _P, _P],

@@ -138,6 +138,9 @@ hipError_t launch_split_router(const float* Wr, int E, int H, uint16_t* wr3, hip
 hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* wr3, int E,
                               float* part, hipStream_t s);
 hipError_t launch_prefill_sort(const PrefillArgs& a, hipStream_t s);
+// perm[row] = pair index t * k + j, for every pair whose expert is in [0, E)
+// (after launch_prefill_sort, from its inverse map).
+hipError_t launch_prefill_perm(const PrefillArgs& a, int32_t* perm, hipStream_t s);
 hipError_t launch_prefill_gu(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_down(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t s);

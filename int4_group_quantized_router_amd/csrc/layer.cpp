@@ -692,6 +692,63 @@ int32_t moe_route_topk(const uint16_t* x, int32_t T, int32_t H, const float* Wr,
   }
 }
 
+int32_t moe_expert_sort(const int32_t* idx, int32_t T, int32_t k, int32_t E, int32_t* perm,
+                        int32_t* offsets, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0, "T must be >= 0");
+  MOE_REQUIRE(k >= 1 && k <= MOE_MAX_TOPK, "k must be in [1, %d]", MOE_MAX_TOPK);
+  MOE_REQUIRE(E >= 1 && E <= 1024, "E must be in [1, 1024]");
+  MOE_REQUIRE((int64_t)T * (k + 1) < (1ll << 30), "T * (k + 1) must be below 2^30");
+  MOE_REQUIRE(offsets, "null argument");
+  if (T == 0) {
+    MOE_HIP_TRY(launch_fill_zero(offsets, (size_t)(E + 1) * 4, stream));
+    return MOE_OK;
+  }
+  MOE_REQUIRE(idx && perm, "null argument");
+  const int64_t P = (int64_t)T * k;
+  const int mt = max_tiles_for(T, k, E);
+  const size_t sizes[] = {
+      (size_t)kSortChunks * E * 4,  // per-chunk histograms
+      (size_t)(E + 2) * 4,          // row offsets (group E: the shared rows)
+      4,                            // tile count
+      (size_t)mt * 4,               // tile groups
+      (size_t)mt * 4,               // tile first rows
+      (size_t)(P + T) * 4,          // sorted row -> token
+      (size_t)P * 4,                // pair -> sorted row
+  };
+  size_t total = 0;
+  for (size_t sz : sizes) total += align256(sz);
+  void* ws = nullptr;
+  MOE_HIP_TRY(hipMallocAsync(&ws, total, stream));
+  uint8_t* q = static_cast<uint8_t*>(ws);
+  void* parts[7];
+  for (int i = 0; i < 7; ++i) {
+    parts[i] = q;
+    q += align256(sizes[i]);
+  }
+  PrefillArgs a{};
+  a.T = T;
+  a.k = k;
+  a.E = E;
+  a.idx = idx;
+  a.hist = static_cast<int32_t*>(parts[0]);
+  a.row_off = static_cast<int32_t*>(parts[1]);
+  a.n_tiles = static_cast<int32_t*>(parts[2]);
+  a.tile_group = static_cast<int32_t*>(parts[3]);
+  a.tile_m0 = static_cast<int32_t*>(parts[4]);
+  a.max_tiles = mt;
+  a.perm_tok = static_cast<int32_t*>(parts[5]);
+  a.inv = static_cast<int32_t*>(parts[6]);
+  hipError_t e = launch_prefill_sort(a, stream);
+  if (e == hipSuccess) e = launch_prefill_perm(a, perm, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(offsets, a.row_off, (size_t)(E + 1) * 4, hipMemcpyDeviceToDevice, stream);
+  const hipError_t e2 = hipFreeAsync(ws, stream);
+  MOE_HIP_TRY(e);
+  MOE_HIP_TRY(e2);
+  return MOE_OK;
+}
+
 int32_t moe_dequant(const void* blob, const moe_qshape* shape, int32_t which, float* out_f32,
                     uint16_t* out_bf16, hipStream_t stream) {
   clear_error();

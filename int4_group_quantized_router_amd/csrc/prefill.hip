@@ -251,7 +251,10 @@ __global__ __launch_bounds__(kThreads) void prefill_hist_kernel(PrefillArgs a) {
   __syncthreads();
   int p0, p1;
   sort_chunk(a, blockIdx.x, &p0, &p1);
-  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) atomicAdd(&h[a.idx[p]], 1);
+  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) {
+    const int e = a.idx[p];
+    if ((unsigned)e < (unsigned)a.E) atomicAdd(&h[e], 1);  // other values: left out
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < a.E; e += kThreads) a.hist[blockIdx.x * a.E + e] = h[e];
 }
@@ -347,7 +350,17 @@ __global__ __launch_bounds__(kThreads) void prefill_scatter_kernel(PrefillArgs a
   __syncthreads();
   int p0, p1;
   sort_chunk(a, blockIdx.x, &p0, &p1);
-  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) a.perm_tok[atomicAdd(&cur[a.idx[p]], 1)] = p;
+  for (int p = p0 + threadIdx.x; p < p1; p += kThreads) {
+    const int e = a.idx[p];
+    if ((unsigned)e < (unsigned)a.E) a.perm_tok[atomicAdd(&cur[e], 1)] = p;
+  }
+}
+
+// Sorted row -> pair index (t * k + j), from the inverse map the sort wrote.
+__global__ __launch_bounds__(kThreads) void prefill_perm_kernel(PrefillArgs a, int32_t* perm) {
+  const int P = a.T * a.k;
+  for (int p = blockIdx.x * kThreads + threadIdx.x; p < P; p += gridDim.x * kThreads)
+    if ((unsigned)a.idx[p] < (unsigned)a.E) perm[a.inv[p]] = p;
 }
 
 constexpr int kSortMax = 8192;  // longest segment sorted in LDS
@@ -892,6 +905,14 @@ hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* w
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(router_gemm_kernel, dim3(pad8((T + RT - 1) / RT) * n_et * ks), dim3(kThreads),
                      lds, s, x, T, H, wr3, E, n_et, ks, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_perm(const PrefillArgs& a, int32_t* perm, hipStream_t s) {
+  const int P = a.T * a.k;
+  if (P == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min((P + kThreads - 1) / kThreads, 1024);
+  hipLaunchKernelGGL(prefill_perm_kernel, dim3(blocks), dim3(kThreads), 0, s, a, perm);
   return hipGetLastError();
 }
 

@@ -217,12 +217,15 @@ def moe_layer(x_bits, Wr, rb, wsg, shared: dict, expert_fn, k: int, bits: int,
 
 
 def moe_layer_tokens(X_bits, Wr, rb, wsg, shared: dict, expert_fn, k: int,
-                     bits: int, group: int = 64, bf16_weights: bool = False) -> dict:
+                     bits: int, group: int = 64, bf16_weights: bool = False,
+                     workers: int = 1) -> dict:
     """The same layer for many tokens at once.
 
     Identical per token to ``moe_layer``; each expert is dequantised once and
     applied (one matrix product) to the rows of the tokens that chose it.
     The combine is still summed per token in j order, then the shared term.
+    ``workers`` > 1 runs different experts on a thread pool; each expert's
+    arithmetic, and so the result, is unchanged.
     """
     X = bf16_to_f64(X_bits)
     T, H = X.shape
@@ -234,10 +237,22 @@ def moe_layer_tokens(X_bits, Wr, rb, wsg, shared: dict, expert_fn, k: int,
         idx[t] = select_topk(logits[t], k)
         w[t] = p[idx[t]] / p[idx[t]].sum()
     Yj = np.zeros((T, k, H))
-    for e in np.unique(idx):
+
+    def one_expert(e):
         rows, slots = np.nonzero(idx == e)
         Wg, Wu, Wd = dequant_expert(expert_fn(int(e)), bits, group, bf16_weights)
         Yj[rows, slots] = swiglu(X[rows], Wg, Wu, Wd)[0]
+
+    if workers > 1:
+        # one BLAS thread per worker: concurrent multi-threaded BLAS calls
+        # would queue on each other
+        from concurrent.futures import ThreadPoolExecutor
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one_expert, np.unique(idx)))
+    else:
+        for e in np.unique(idx):
+            one_expert(e)
     sigma = sigmoid(X @ np.asarray(wsg, np.float64))
     Wg, Wu, Wd = dequant_expert(shared, bits, group, bf16_weights)
     ysh = swiglu(X, Wg, Wu, Wd)[0]

@@ -76,10 +76,11 @@ def oracle_layer(cfg, layer: int, x_bits, bf16_weights=False):
 
 
 def oracle_tokens(cfg, layer: int, X_bits, bf16_weights=False):
+    import os
     Wr, rb, wsg = router_arrays(cfg, layer)
     return O.moe_layer_tokens(X_bits, Wr, rb, wsg, shared_arrays(cfg, layer),
                               lambda e: expert_arrays(cfg, layer, e), cfg.top_k, cfg.bits,
-                              cfg.group, bf16_weights)
+                              cfg.group, bf16_weights, workers=min(16, os.cpu_count() or 1))
 
 
 # ------------------------------------------------------------- comparisons

@@ -371,22 +371,46 @@ def test_stack_teacher_forced(torch):
             w = torch.empty((L, T, k), dtype=torch.float32, device="cuda")
             ylast = m.moe_stack_forward(st, x0, x_layers=xl, y_layers=yl, idx=idx, w=w)
             torch.cuda.synchronize()
-            xl_, yl_ = xl.cpu().numpy().view(np.uint16), yl.cpu().numpy()
-            assert np.array_equal(xl_[0, 0], token_x(cfg, tok))
-            for l in range(L):
-                ref = oracle_layer(cfg, l, xl_[l, 0])
-                Wr, rb, _ = router_arrays(cfg, l)
-                check_routing(idx.cpu().numpy()[l, 0], None, O.bf16_to_f64(xl_[l, 0]), Wr, rb, k)
-                if np.array_equal(idx.cpu().numpy()[l, 0], ref["idx"]):
-                    assert rel_err(yl_[l, 0], ref["y"]) <= REL_TOL
-                if l + 1 < L:
-                    nxt = O.rms_rescale(yl_[l, 0])
-                    diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
-                    assert diff.max() <= 1
-            check_bf16_of_f32(ylast.cpu().numpy(), yl_[L - 1])
+            _check_stack_layers(cfg, tok, ylast.cpu().numpy(), xl.cpu().numpy(),
+                                yl.cpu().numpy(), idx.cpu().numpy())
     finally:
         m.moe_stack_destroy(st)
         dm.destroy()
+
+
+def _check_stack_layers(cfg, tok, ylast, xl_, yl_, ix, max_undecided=1):
+    """Every layer of one token's stack exports against the oracle on the
+    GPU's own input to that layer (teacher forcing), the RMS rescale chain
+    to one bf16 ulp, the final bf16 output the rounding of the last f32
+    output.  Layers whose routing differs from the oracle's (allowed only
+    inside the f32 error bound) are counted; at most `max_undecided`."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    H, k, L = cfg.hidden, cfg.top_k, xl_.shape[0]
+    xl_ = xl_.view(np.uint16)
+    assert np.array_equal(xl_[0, 0], token_x(cfg, tok))
+    # each layer's oracle run is independent (teacher forcing): one per worker
+    with threadpool_limits(limits=1, user_api="blas"), \
+            ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        refs = list(ex.map(lambda l: oracle_layer(cfg, l, xl_[l, 0]), range(L)))
+    compared, worst = 0, 0.0
+    for l in range(L):
+        ref = refs[l]
+        Wr, rb, _ = router_arrays(cfg, l)
+        check_routing(ix[l, 0], None, O.bf16_to_f64(xl_[l, 0]), Wr, rb, k)
+        if np.array_equal(ix[l, 0], ref["idx"]):
+            compared += 1
+            err = rel_err(yl_[l, 0], ref["y"])
+            worst = max(worst, err)
+            assert err <= REL_TOL, (tok, l, err)
+        if l + 1 < L:
+            nxt = O.rms_rescale(yl_[l, 0])
+            diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
+            assert diff.max() <= 1, (tok, l)
+    check_bf16_of_f32(ylast, yl_[L - 1])
+    _print("token", tok, "layers compared", compared, "/", L, "worst rel err", worst)
+    assert compared >= L - max_undecided, (tok, compared, L)
 
 
 @pytest.mark.parametrize("name,tokens", [("decode35b", (0, 131)), ("decode80b_int8", (7,))])
@@ -419,24 +443,65 @@ def test_stack_full_depth_sampled(torch, name, tokens):
                              idx.cpu().numpy()))
             for a, b in zip(outs[0], outs[1]):
                 assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), tok
-            ylast, xl_, yl_, ix = outs[0]
-            xl_ = xl_.view(np.uint16)
-            assert np.array_equal(xl_[0, 0], token_x(cfg, tok))
-            for l in range(L):
-                ref = oracle_layer(cfg, l, xl_[l, 0])
-                Wr, rb, _ = router_arrays(cfg, l)
-                check_routing(ix[l, 0], None, O.bf16_to_f64(xl_[l, 0]), Wr, rb, k)
-                if np.array_equal(ix[l, 0], ref["idx"]):
-                    assert rel_err(yl_[l, 0], ref["y"]) <= REL_TOL, (tok, l)
-                if l + 1 < L:
-                    nxt = O.rms_rescale(yl_[l, 0])
-                    diff = np.abs(nxt.astype(np.int64) - xl_[l + 1, 0].astype(np.int64))
-                    assert diff.max() <= 1, (tok, l)
-            check_bf16_of_f32(ylast, yl_[L - 1])
+            _check_stack_layers(cfg, tok, *outs[0])
     finally:
         m.moe_stack_set_persistent(st, True)
         m.moe_stack_destroy(st)
         dm.destroy()
+
+
+def test_stack_80b_int4_full_depth_resident_and_pooled(torch):
+    """The 80B-shaped int4 stack at full depth (48 layers, 512 experts,
+    top-10): resident, and through a slot pool of 30% of the experts over the
+    pinned store (cold: every choice misses; warm: all hit, one launch; after
+    a flush: misses again), in the persistent kernel.  All runs give the same
+    bits, and every layer of the resident run matches the oracle on its own
+    input.  The pool's counters and slots equal the oracle's replay."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from oracle.pool_replay import PoolReplay
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"]
+    L, k = cfg.layers, cfg.top_k
+    _print("80B int4 stack, full depth", L)
+    dm = DeviceModel(cfg)
+    store, stride = Wt.fill_store(dims_of(cfg), L, lambda l, e: expert_arrays(cfg, l, e))
+    cap = int(cfg.pool_frac * L * cfg.experts)
+    pool = m.slotpool_create(store, cap, 0)
+    s_res = m.moe_stack_create(dm.make_layers())
+    s_pool = m.moe_stack_create(dm.make_layers(pool=pool))
+    assert m.moe_stack_persistent_active(s_res) and m.moe_stack_persistent_active(s_pool)
+    replay = PoolReplay(cap, stride)
+    try:
+        for rnd, toks in enumerate(((0, 1), (0,))):
+            for tok in toks:
+                want = _stack_outputs(torch, m, s_res, cfg, tok)
+                for run in ("first", "again"):
+                    e0 = m.moe_stack_epoch(s_pool)
+                    got = _stack_outputs(torch, m, s_pool, cfg, tok)
+                    for u, v in zip(got, want):
+                        assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), (rnd, tok, run)
+                    for l in range(L):
+                        replay.acquire(l, got[3][l, 0].tolist())
+                        replay.release(l, got[3][l, 0].tolist())
+                    if run == "again":  # every choice resident: one launch, no stop
+                        assert m.moe_stack_epoch(s_pool) == e0 + 1
+                if rnd == 0:
+                    _check_stack_layers(cfg, tok, *want[:4])
+            st = m.slotpool_stats(pool)
+            assert {x: st[x] for x in replay.stats()} == replay.stats(), (st, replay.stats())
+            for l in (0, L // 2, L - 1):
+                for e in range(cfg.experts):
+                    want_slot = replay.slot_of[(l, e)] if replay.resident(l, e) else -1
+                    assert m.slotpool_slot_of(pool, l, e) == want_slot
+            m.slotpool_flush(pool)
+            replay.flush()
+    finally:
+        m.moe_stack_destroy(s_res)
+        m.moe_stack_destroy(s_pool)
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
 
 
 @pytest.mark.parametrize("name,L", [("tiny", 3), ("decode35b", 6), ("stream80b", 2),
@@ -1002,6 +1067,67 @@ def test_prefill_token_permutation_is_bitwise(torch):
         assert np.array_equal(y_a[perm].view(np.uint32), y_b.view(np.uint32))
     finally:
         dm.destroy()
+
+
+def _sort_case(torch, idx_host, E):
+    import int4_group_quantized_router_amd as m
+    idx = torch.from_numpy(np.ascontiguousarray(idx_host, dtype=np.int32)).cuda()
+    perm, off = m.moe_expert_sort(idx, E)
+    torch.cuda.synchronize()
+    want_perm, want_off = O.sort_by_expert(idx_host, E)
+    got_off = off.cpu().numpy()
+    assert np.array_equal(got_off, want_off), (got_off[:8], want_off[:8])
+    n = int(want_off[E])
+    assert np.array_equal(perm.cpu().numpy()[:n], want_perm)
+
+
+def test_expert_sort_matches_oracle(torch):
+    """The many-token path's grouping of (token, choice) pairs by expert,
+    exported through moe_expert_sort, equals the oracle's stable counting
+    sort exactly: on the router's own choices for the 4096-token 80B-shaped
+    batch, on random choices, on one expert taking more rows than the
+    in-LDS sort holds (9000), with a single expert, with choices outside
+    [0, E) (left out), and with no tokens."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["prefill80b"]
+    Wr, rb, _ = router_arrays(cfg, 0)
+    xb = tokens_x(cfg, 0, cfg.tokens)
+    out = m.moe_route_topk(torch.from_numpy(xb.view(np.int16)).cuda(), torch.from_numpy(Wr).cuda(),
+                           torch.from_numpy(rb).cuda(), cfg.top_k, with_logits=False)
+    torch.cuda.synchronize()
+    assert out["logits"] is None
+    _print("sort: router choices", cfg.tokens, cfg.top_k)
+    _sort_case(torch, out["idx"].cpu().numpy(), cfg.experts)
+    rng = np.random.default_rng(9)
+    _print("sort: random")
+    _sort_case(torch, rng.integers(0, 50, size=(777, 3)), 50)
+    _print("sort: long segment")
+    crowd = np.full((9000, 1), 7)
+    crowd[::97, 0] = rng.integers(0, 16, size=crowd[::97, 0].shape)
+    _sort_case(torch, crowd, 16)
+    _print("sort: one expert")
+    _sort_case(torch, np.zeros((10, 2), np.int64), 1)
+    _print("sort: out-of-range choices")
+    bad = rng.integers(0, 64, size=(300, 4))
+    bad[::7, 1] = -1
+    bad[::5, 2] = 64
+    _sort_case(torch, bad, 64)
+    _print("sort: max experts, top-16")
+    _sort_case(torch, rng.integers(0, 1024, size=(2000, 16)), 1024)
+    off = torch.full((9,), 5, dtype=torch.int32, device="cuda")
+    m.moe_expert_sort(torch.zeros((0, 2), dtype=torch.int32, device="cuda"), 8, offsets=off)
+    torch.cuda.synchronize()
+    assert off.cpu().numpy().tolist() == [0] * 9
+
+
+def test_prefill_full_size_every_token(torch):
+    """4096 tokens, 512 experts, top-10 -- the only shape whose experts span
+    several 96-row tiles and whose shared group has 43 tiles -- against the
+    oracle's bf16-weight mode on every token: at least 95% of the tokens
+    route exactly as the oracle does (the rest only within the f32 error
+    bound), and every one of those is within 2e-3."""
+    dm, *_ = _prefill_case(torch, CONFIGS["prefill80b"], CONFIGS["prefill80b"].tokens)
+    dm.destroy()
 
 
 def test_prefill_full_size_sampled(torch):
