@@ -245,7 +245,15 @@ def main():
                     help="only run 10 device-to-device copies of BYTES (reference for HBM counters)")
     ap.add_argument("--calibrate-peaks", action="store_true",
                     help="only measure a 1 GiB device copy and an 8192^3 bf16 matmul")
+    ap.add_argument("--phases", type=int, default=0, metavar="TOKENS",
+                    help="decode: run TOKENS tokens through the profiling build "
+                         "(libmoe_phases.so, built by `python -m "
+                         "int4_group_quantized_router_amd._build --phases`) and print the "
+                         "persistent kernel's per-phase times")
     args = ap.parse_args()
+    if args.phases:  # before the package is imported: it loads the library named there
+        os.environ["MOE_LIBRARY"] = os.path.join(ROOT, "int4_group_quantized_router_amd",
+                                                 "libmoe_phases.so")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -264,7 +272,78 @@ def main():
         return bench_prefill(args, cfg)
     if not cfg.resident:
         return bench_stream(args, cfg)
+    if args.phases:
+        return bench_phases(args, cfg)
     return bench_decode(args, cfg)
+
+
+PHASE_NAMES = ["previous output received", "input staged (RMS rescale)", "router row published",
+               "logits received + top-k (shared gate/up alongside)", "routed gate/up",
+               "shared h received", "routed h received", "down rows", "output published"]
+
+
+def bench_phases(args, cfg):
+    """Per-phase times of the persistent stack kernel (profiling build): for
+    every layer but the first, workgroup and token, the wall-clock time from
+    one phase boundary to the next; medians and 90th percentiles."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import _lib
+    from moe_inputs import tokens_x
+    assert _lib.LIB_PATH.endswith("libmoe_phases.so"), _lib.LIB_PATH
+    torch.cuda.set_device(0)
+    log(f"[phases] building {cfg.name}: {cfg.layers} layers")
+    layers, stack, keep = _build_stack(cfg)
+    assert m.moe_stack_persistent_active(stack)
+    L, G, P = cfg.layers, 256, 12
+    n = args.phases
+    warm = 8
+    X = torch.from_numpy(tokens_x(cfg, 0, warm + n).view(np.int16)).cuda()
+    Y = torch.empty((warm + n, cfg.hidden), dtype=torch.int16, device="cuda")
+    buf = torch.zeros((L, G, P), dtype=torch.int64, device="cuda")
+    for i in range(warm):
+        m.moe_stack_forward(stack, X[i:i + 1], y_last=Y[i:i + 1])
+    m.moe_stack_set_phase_log(stack, buf)
+    runs = []
+    for i in range(warm, warm + n):
+        buf.zero_()
+        m.moe_stack_forward(stack, X[i:i + 1], y_last=Y[i:i + 1])
+        torch.cuda.synchronize()
+        runs.append(buf.cpu().numpy().astype(np.int64))
+    m.moe_stack_set_phase_log(stack, None)
+    t = np.stack(runs)[:, 1:]              # tokens, layers 1.., workgroups, phases
+    assert np.all(t > 0), "missing timestamps"
+    us = 0.01                              # 100 MHz wall clock
+    d = np.diff(t[..., :10], axis=-1) * us  # phase p-1 -> p, p = 1..9
+    # inside "top-k done": wave 0's logits wait, its selection, then the wait
+    # for waves 1..7 (shared gate/up) at the barrier
+    sub = {"logits wait (wave 0)": (t[..., 10] - t[..., 3]) * us,
+           "top-k selection (wave 0)": (t[..., 11] - t[..., 10]) * us,
+           "barrier after top-k": (t[..., 4] - t[..., 11]) * us}
+    period = (t[:, 1:, :, 0] - t[:, :-1, :, 0]) * us
+    spread = (t[:, :, :, 9].max(axis=2) - t[:, :, :, 9].min(axis=2)) * us
+    rows = []
+    for p in range(9):
+        v = d[..., p].ravel()
+        rows.append({"phase": PHASE_NAMES[p], "median_us": float(np.median(v)),
+                     "p90_us": float(np.percentile(v, 90))})
+        if p == 3:
+            for name, sv in sub.items():
+                rows.append({"phase": "  " + name, "median_us": float(np.median(sv)),
+                             "p90_us": float(np.percentile(sv, 90))})
+    out = {"phases": rows, "workload": cfg.name, "tokens": n,
+           "layer_period_median_us": float(np.median(period)),
+           "layer_period_p90_us": float(np.percentile(period, 90)),
+           "output_publish_spread_median_us": float(np.median(spread))}
+    for r in rows:
+        log(f"[phases] {r['phase']:52s} {r['median_us']:7.2f} us (p90 {r['p90_us']:.2f})")
+    log(f"[phases] layer period {out['layer_period_median_us']:.2f} us; output spread "
+        f"{out['output_publish_spread_median_us']:.2f} us")
+    print(json.dumps(out), flush=True)
+    m.moe_stack_destroy(stack)
+    for Lh in layers:
+        m.moe_layer_destroy(Lh)
 
 
 def bench_decode(args, cfg):

@@ -434,6 +434,15 @@ int32_t moe_stack_persistent_active(const moe_stack* stack, int32_t* active);
 int32_t moe_stack_epoch(const moe_stack* stack, uint32_t* epoch);
 int32_t moe_stack_advance_epoch(moe_stack* stack, uint32_t n);
 int32_t moe_stack_set_timeout(moe_stack* stack, int64_t microseconds);
+/* Profiling hook of a library built with -DMOE_STACK_PHASES (the
+ * libmoe_phases.so variant; MOE_E_INVAL otherwise): phases, device uint64
+ * [L][256][12] or NULL, receives per layer and workgroup the wall-clock
+ * ticks (100 MHz) at twelve points of every persistent launch: layer start,
+ * previous output received, input staged, router row published, top-k done
+ * (all waves), routed gate/up done, shared h received, routed h received,
+ * down rows done, output published, then (wave 0 alone) every logit
+ * received and the top-k selected.  Each launch overwrites it. */
+int32_t moe_stack_set_phase_log(moe_stack* stack, uint64_t* phases);
 int32_t moe_stack_destroy(moe_stack* stack);
 
 /* ------------------------------------------------------------------------

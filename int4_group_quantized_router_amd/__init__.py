@@ -390,6 +390,11 @@ def moe_stack_set_timeout(stack, microseconds: int) -> None:
     _check(_lib_().moe_stack_set_timeout(_h(stack), int(microseconds)), "moe_stack_set_timeout")
 
 
+def moe_stack_set_phase_log(stack, phases) -> None:
+    """Profiling builds only: phases = device int64 tensor [L, 256, 10] or None."""
+    _check(_lib_().moe_stack_set_phase_log(_h(stack), _dptr(phases)), "moe_stack_set_phase_log")
+
+
 def moe_stack_destroy(stack) -> None:
     _check(_lib_().moe_stack_destroy(_h(stack)), "moe_stack_destroy")
 

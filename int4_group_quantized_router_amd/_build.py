@@ -41,9 +41,9 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-x", "hip", *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
@@ -54,20 +54,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, phases: bool = False) -> str:
+    """Compile and link libmoe.so; phases=True builds the profiling variant
+    libmoe_phases.so instead (the persistent stack kernel records phase
+    timestamps, see moe_stack_set_phase_log)."""
+    build_dir = BUILD + "_phases" if phases else BUILD
+    lib = os.path.join(PKG, "libmoe_phases.so") if phases else LIB
+    extra = ("-DMOE_STACK_PHASES",) if phases else ()
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(phases="--phases" in sys.argv[1:]))

@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+# MOE_LIBRARY may name a profiling build of the same library (libmoe_phases.so)
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+PHASES_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_phases.so")
 
 MOE_OK = 0
 MOE_E_INVAL = -1
@@ -97,6 +100,7 @@ SIGNATURES = {
     "moe_stack_epoch": [_P, C.POINTER(C.c_uint32)],
     "moe_stack_advance_epoch": [_P, C.c_uint32],
     "moe_stack_set_timeout": [_P, _I64],
+    "moe_stack_set_phase_log": [_P, _P],
     "moe_stack_destroy": [_P],
     "moe_timer_create": [_I32, _I32, C.POINTER(_P)],
     "moe_timer_attach": [_P],

@@ -145,6 +145,28 @@ __device__ __forceinline__ float ldf(const void* p) {
   return *(__attribute__((address_space(1))) const float*)p;
 }
 
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS loads (global_load_lds): lane i's 16 (4) bytes at src go to
+// LDS address m0 + 16 i (4 i); m0 must be wave-uniform.  Issued as plain
+// instructions, they are invisible to the compiler's wait-count bookkeeping:
+// the caller waits for them with wait_vm_n before reading the LDS they
+// write.  Vector loads complete in issue order, so waiting until at most N
+// loads are outstanding completes every load older than the last N issued.
+__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t m0) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace dev
 }  // namespace moe
 
@@ -197,18 +219,17 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// Top-k of up to 64*VPL logits held by one wave (value i of lane l is
-// expert l + 64 i, invalid entries key 0), ordered by (logit desc, index
-// asc).  A bitwise search from the top bit finds a threshold key t with at
-// least k keys >= t, stopping early as soon as exactly k are (then those k
-// are the answer); otherwise it ends at the k-th largest key and ties at t
-// go to the lowest indices.  The k winners are compacted to LDS and ranked
-// by broadcasting each one's key (readlane).  Results: sel_e[j], sel_v[j]
-// for j < k (LDS; tmp_e / tmp_v: the wave's own scratch of >= k entries).
-// All lanes must call it.
-template <int VPL>
-__device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e, float* tmp_v,
-                          int* sel_e, float* sel_v) {
+// Selection inside one wave: among the keys held one per lane-slot (slot i
+// of lane l holds key[i] with index idx_of(l, i), invalid entries key 0),
+// the k best by (key desc, index asc), given that the index order equals
+// the (i, lane) order.  A bitwise search from the top bit finds a threshold
+// key t with at least k keys >= t, stopping early as soon as exactly k are
+// (then those k are the answer); otherwise it ends at the k-th largest key
+// and ties at t go to the lowest indices.  The winners are compacted to
+// tmp (k entries) and ranked by broadcasting each one's key (readlane).
+template <int VPL, class IdxOf>
+__device__ void select_k(const float* v, const uint32_t* key, int k, IdxOf idx_of, int* tmp_e,
+                         float* tmp_v, int* sel_e, float* sel_v) {
   const int lane = threadIdx.x & 63;
   uint32_t thr = 0;
   for (int b = 31; b >= 0; --b) {
@@ -236,7 +257,7 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
     const uint64_t sm = __ballot(sel);
     if (sel) {
       const int pos = base + __popcll(sm & below);
-      tmp_e[pos] = lane + 64 * i;
+      tmp_e[pos] = idx_of(lane, i);
       tmp_v[pos] = v[i];
     }
     base += __popcll(sm);
@@ -262,6 +283,68 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Top-k of up to 64*VPL logits held by one wave (value i of lane l is
+// expert l + 64 i, invalid entries key 0), ordered by (logit desc, index
+// asc).  Results: sel_e[j], sel_v[j] for j < k (LDS).  tmp_e / tmp_v / tmp_k:
+// the wave's own LDS scratch of >= 64 entries each.  All lanes must call it.
+//
+// With several keys per lane the search runs on a pruned set: the k-th
+// largest of the 64 per-lane maxima, t1, is found first (one key per lane);
+// at least k lanes hold a key >= t1, so every one of the k best keys is
+// >= t1.  The keys >= t1 -- usually few more than k -- are compacted one
+// per lane in (i, lane) order, which is increasing expert index, and the
+// selection runs on them.  If more than 64 keys are >= t1 (many ties), the
+// selection runs on all keys instead.  Either way the result is the unique
+// top-k by (key desc, index asc).
+template <int VPL>
+__device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e, float* tmp_v,
+                          uint32_t* tmp_k, int* sel_e, float* sel_v) {
+  auto natural = [](int l, int i) { return l + 64 * i; };
+  if (VPL == 1) {
+    select_k<VPL>(v, key, k, natural, tmp_e, tmp_v, sel_e, sel_v);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  uint32_t mx = key[0];
+#pragma unroll
+  for (int i = 1; i < VPL; ++i) mx = mx > key[i] ? mx : key[i];
+  uint32_t t1 = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = t1 | (1u << b);
+    const int cnt = __popcll(__ballot(mx >= cand));
+    if (cnt >= k) {
+      t1 = cand;
+      if (cnt == k) break;
+    }
+  }
+  const uint64_t below = lanes_below();
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const bool c = key[i] >= t1 && key[i] != 0u;
+    const uint64_t bm = __ballot(c);
+    const int pos = n + __popcll(bm & below);
+    if (c && pos < 64) {
+      tmp_k[pos] = key[i];
+      tmp_v[pos] = v[i];
+      tmp_e[pos] = lane + 64 * i;
+    }
+    n += __popcll(bm);
+  }
+  if (n > 64 || n < k) {  // wave-uniform
+    select_k<VPL>(v, key, k, natural, tmp_e, tmp_v, sel_e, sel_v);
+    return;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const float cv = lane < n ? tmp_v[lane] : 0.f;
+  const uint32_t ck = lane < n ? tmp_k[lane] : 0u;
+  const int ce = lane < n ? tmp_e[lane] : 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  select_k<1>(&cv, &ck, k, [&](int, int) { return ce; }, tmp_e, tmp_v, sel_e, sel_v);
 }
 
 }  // namespace dev

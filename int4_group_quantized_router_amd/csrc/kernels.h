@@ -154,6 +154,7 @@ constexpr int kStackThreads = 512;
 constexpr int kStackGrid = 256;       // workgroups: one per compute unit of MI355X
 constexpr int kStackReplicas = 8;     // copies of every hand-off word (one per XCD)
 constexpr int kStackMaxLayers = 64;   // layer descriptors kept in LDS
+constexpr int kStackPhases = 12;      // phase timestamps per layer and workgroup (profiling)
 
 struct StackLayerDesc {
   const float* Wr;              // f32 [E, H]
@@ -196,12 +197,14 @@ struct StackArgs {
   // f32 output, from which layer l0's input is formed as usual
   int l0;
   const float* y_start;
+  // profiling builds (MOE_STACK_PHASES): [L][grid][kStackPhases] wall-clock
+  // timestamps, or NULL
+  uint64_t* phases;
 };
 
 // True if the persistent kernel has an instance for this shape on a device
 // with `cus` compute units (else the per-layer kernels run).
 bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cus);
-size_t stack_lds_bytes(int H, int E, int k, int I, int Is, int bits);
 hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,
                                hipStream_t s);
 // Zero `bytes` (a multiple of 4) of device memory with a kernel (usable

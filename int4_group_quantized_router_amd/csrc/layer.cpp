@@ -1112,6 +1112,19 @@ int32_t moe_stack_advance_epoch(moe_stack* stack, uint32_t n) {
   return MOE_OK;
 }
 
+int32_t moe_stack_set_phase_log(moe_stack* stack, uint64_t* phases) {
+  clear_error();
+  MOE_REQUIRE(stack, "null argument");
+  MOE_REQUIRE(stack->ps_mem, "the stack has no persistent path");
+#ifdef MOE_STACK_PHASES
+  stack->ps.phases = phases;
+  return MOE_OK;
+#else
+  (void)phases;
+  return fail(MOE_E_INVAL, "this library was built without phase timestamps (MOE_STACK_PHASES)");
+#endif
+}
+
 int32_t moe_stack_set_timeout(moe_stack* stack, int64_t microseconds) {
   clear_error();
   MOE_REQUIRE(stack && microseconds >= 0, "bad argument");

@@ -480,23 +480,8 @@ struct BRaw {  // one K group of packed weights for the lane's two weight rows
   float s24[2], s20[2], bi[2];  // per column block: s * 2^24, s * 2^20, b
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct-to-LDS loads: lane i's 16 (4) bytes at src go to LDS address
-// m0 + 16 i (4 i).  Issued as plain instructions, they are invisible to the
-// compiler's wait-count bookkeeping; the loop below waits for them itself.
-__device__ __forceinline__ void dma16(const void* src, uint32_t m0) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t m0) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_n() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// (lds_addr, dma16, dma4 and wait_vm_n: device.h.)  The loop below waits
+// for its direct-to-LDS loads itself.
 // wait until at most n of this wave's loads are outstanding (n <= 15)
 __device__ __forceinline__ void wait_vm(int n) {
   switch (n) {

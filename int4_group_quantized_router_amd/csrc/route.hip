@@ -114,8 +114,9 @@ __device__ void stage_input(const RouteArgs& a, float* xs, float (*red)[4], int 
 template <int VPL, int NW>
 __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, float* s_val,
                             float* s_sraw) {
-  __shared__ int tmp_e[NW][MOE_MAX_TOPK];
-  __shared__ float tmp_v[NW][MOE_MAX_TOPK];
+  __shared__ int tmp_e[NW][kWave];
+  __shared__ float tmp_v[NW][kWave];
+  __shared__ uint32_t tmp_k[NW][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int E = a.E, k = a.k;
   for (int t = t0 + wave; t < t1; t += NW) {
@@ -163,7 +164,7 @@ __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, floa
         key[i] = e < E ? order_key(v[i]) : 0u;
       }
     }
-    wave_topk<VPL>(v, key, k, tmp_e[wave], tmp_v[wave], s_sel + (t - t0) * k,
+    wave_topk<VPL>(v, key, k, tmp_e[wave], tmp_v[wave], tmp_k[wave], s_sel + (t - t0) * k,
                    s_val + (t - t0) * k);
   }
 }

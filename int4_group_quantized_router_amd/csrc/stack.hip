@@ -53,6 +53,21 @@ namespace {
 
 using namespace dev;
 
+// Phase timestamps (profiling builds only, -DMOE_STACK_PHASES): thread 0 of
+// every workgroup records the wall clock (100 MHz) at the phase boundaries
+// of each layer into a.phases[(l * grid + block) * kStackPhases + p].
+#ifdef MOE_STACK_PHASES
+#define STACK_PHASE(P)                                                          \
+  do {                                                                          \
+    if (threadIdx.x == 0 && a.phases)                                           \
+      a.phases[((size_t)l * kG + blk) * kStackPhases + (P)] = wall_clock64();   \
+  } while (0)
+#else
+#define STACK_PHASE(P) \
+  do {                 \
+  } while (0)
+#endif
+
 constexpr int kNT = kStackThreads;
 constexpr int kNW = kNT / kWave;
 constexpr int kG = kStackGrid;
@@ -74,20 +89,23 @@ __device__ __forceinline__ bool poll_round(bool ok, int64_t deadline, bool* time
   return false;
 }
 
-// Wait for the previous layer's output y: thread t < 256 takes y[t + 256 m]
-// (the per-layer router's order for the sum of squares) into registers.
+// Wait for the previous layer's output y: the threads of waves 4..7 (t =
+// threadIdx - 256 in 0..255) take y[t + 256 m] (the per-layer router's
+// order for the sum of squares) into registers.  Waves 0..3, which own the
+// router rows and so have those rows' loads in flight, do not poll.
+constexpr int kYT0 = 256;  // first thread of the y pollers
 template <int H>
 __device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t deadline) {
   constexpr int M = H / 256;
-  const int t = threadIdx.x;
+  const int t = (int)threadIdx.x - kYT0;
   uint32_t done = 0;
   for (;;) {
     uint64_t e[M];
 #pragma unroll
     for (int m = 0; m < M; ++m)
-      e[m] = (t < 256 && !((done >> m) & 1u)) ? ld_dev(buf + t + m * 256) : 0ull;
+      e[m] = (t >= 0 && !((done >> m) & 1u)) ? ld_dev(buf + t + m * 256) : 0ull;
     bool ok = true;
-    if (t < 256) {
+    if (t >= 0) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         if (!((done >> m) & 1u)) {
@@ -184,6 +202,24 @@ struct Shape {
   static_assert(H <= 2048 && H % 256 == 0, "router row in one wave");
 };
 
+// LDS of one workgroup (bytes; every region 16-byte aligned): the layer
+// input (f32 and bf16), the h pairs, the router row of each wave that may
+// own one, and per wave DN slots of down weights (16 bytes per lane) and of
+// their (scale, bias) words (4 bytes per lane), both filled by
+// direct-to-LDS loads.
+template <class S, int VPL>
+struct StackLds {
+  static constexpr int kRwRaw = (64 * VPL + 1 + kG - 1) / kG;
+  static constexpr int RW = kRwRaw < kNW ? kRwRaw : kNW;
+  static constexpr size_t XB = (size_t)S::H * 4;
+  static constexpr size_t HL = (size_t)S::H * 6;
+  static constexpr size_t WR = HL + (size_t)S::HW * 2;
+  static constexpr size_t DW = WR + (size_t)RW * S::H * 4;
+  static constexpr size_t kDwWave = (size_t)S::DN * (1024 + 256);
+  static constexpr size_t BYTES = DW + kNW * kDwWave;
+  static_assert(XB % 16 == 0 && HL % 16 == 0 && WR % 16 == 0 && DW % 16 == 0, "LDS alignment");
+};
+
 // POOL: routed blobs come from each layer's row of the pool's device table
 // (StackLayerDesc::res_row) and the call may start at a.l0 > 0; the resident
 // instance reads routed_base and always starts at layer 0.
@@ -198,8 +234,9 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   __shared__ int s_sel[MOE_MAX_TOPK];
   __shared__ float s_val[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK + 1];
-  __shared__ int tmp_e[MOE_MAX_TOPK];
-  __shared__ float tmp_v[MOE_MAX_TOPK];
+  __shared__ int tmp_e[kWave];
+  __shared__ float tmp_v[kWave];
+  __shared__ uint32_t tmp_k[kWave];
   __shared__ const uint8_t* s_addr[POOL ? MOE_MAX_TOPK : 1];  // pool mode: blob of choice j
   __shared__ int s_stop;
   __shared__ StackLayerDesc s_layers[kStackMaxLayers];
@@ -213,10 +250,17 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   const int tid = threadIdx.x;
   const int e_rows = E + (a.has_wsg ? 1 : 0);
 
-  // LDS carve-up (sizes as in stack_lds_bytes)
+  // LDS carve-up (StackLds)
+  using LD = StackLds<S, VPL>;
   float* xf = reinterpret_cast<float*>(smem);                       // [H] f32 input
-  uint16_t* xb = reinterpret_cast<uint16_t*>(smem + (size_t)H * 4);  // [H] bf16 input
-  uint32_t* hl = reinterpret_cast<uint32_t*>(smem + (size_t)H * 6);  // [HW / 2] h pairs
+  uint16_t* xb = reinterpret_cast<uint16_t*>(smem + LD::XB);        // [H] bf16 input
+  uint32_t* hl = reinterpret_cast<uint32_t*>(smem + LD::HL);        // [HW / 2] h pairs
+  // router row of each wave that has one (waves 0 .. (E + 1) / G), f32 [H]
+  float* wrl = reinterpret_cast<float*>(smem + LD::WR) + (size_t)wave * H;
+  // this wave's down-weight slots: 16 bytes per lane per item, then the
+  // items' (scale, bias) words, 4 bytes per lane
+  const uint8_t* dwl = smem + LD::DW + (size_t)wave * LD::kDwWave;
+  const uint32_t dq_m0 = lds_addr(dwl), dsb_m0 = dq_m0 + S::DN * 1024;
 
   const int rep = blk % kRep;  // the XCD of this workgroup
   const uint32_t epoch = ld_dev(a.epochs + blk);
@@ -235,22 +279,27 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   const int gw = wave * kG + blk;  // global wave index: gate/up row group gw + n * 8G
   const int row0 = blk * R;        // down rows [row0, row0 + R)
 
-  // router row of each wave (E = the shared gate), requested one layer ahead
+  // router row of each wave (E = the shared gate), requested one layer
+  // ahead straight into LDS (lane i's float4 m at wrl + 256 m + 4 i)
   const int rrow = blk + kG * wave;
   const int l0 = POOL ? a.l0 : 0;
-  float4 wv[kWrN];
+  const uint32_t wrl_m0 = lds_addr(wrl);
+  auto router_request = [&](const StackLayerDesc& Dx) {
+    const float* wr = rrow < E ? Dx.Wr + (size_t)rrow * H : Dx.wsg;
+#pragma unroll
+    for (int m = 0; m < kWrN; ++m) dma16(wr + m * 256 + lane * 4, wrl_m0 + m * 1024);
+  };
   float rbv = 0.f;
   if (rrow < e_rows) {
     const StackLayerDesc& D0 = s_layers[l0];
-    const float* wr = rrow < E ? D0.Wr + (size_t)rrow * H : D0.wsg;
-#pragma unroll
-    for (int m = 0; m < kWrN; ++m) wv[m] = ldf4(wr + m * 256 + lane * 4);
+    router_request(D0);
     if (rrow < E && D0.rb) rbv = ldf(D0.rb + rrow);
   }
 
   int l_fail = a.L;  // the layer a wait ran out of time in
   for (int l = l0; l < a.L && !failed; ++l) {
     const StackLayerDesc D = s_layers[l];
+    STACK_PHASE(0);  // layer start
 
     // ---- layer input: x0, or bf16(y / rms(y)) of the previous layer
     if (l == 0) {  // (a call starting later than layer 0 begins from y_start)
@@ -264,30 +313,31 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     } else {
       float yv[H / 256];
       if (POOL && l == l0) {
-        if (tid < 256) {
+        if (tid >= kYT0) {
 #pragma unroll
-          for (int m = 0; m < H / 256; ++m) yv[m] = a.y_start[tid + m * 256];
+          for (int m = 0; m < H / 256; ++m) yv[m] = a.y_start[tid - kYT0 + m * 256];
         }
       } else if (!poll_y<H>(a.ybuf + ((size_t)(l - 1) * kRep + rep) * H, tag, yv, deadline)) {
         failed = true;
         l_fail = l;
         break;
       }
+      STACK_PHASE(1);  // previous layer's y received
       // sum of squares in the per-layer router's order (256 threads)
-      if (tid < 256) {
+      if (tid >= kYT0) {
         float s = 0.f;
 #pragma unroll
         for (int m = 0; m < H / 256; ++m) s = fmaf(yv[m], yv[m], s);
         s = group_sum(s, kWave);
-        if (lane == 0) red[tid >> 6] = s;
+        if (lane == 0) red[(tid - kYT0) >> 6] = s;
       }
       __syncthreads();
       const float tot = ((red[0] + red[1]) + red[2]) + red[3];
       const float r = 1.0f / sqrtf(tot / (float)H + 1e-6f);
-      if (tid < 256) {
+      if (tid >= kYT0) {
 #pragma unroll
         for (int m = 0; m < H / 256; ++m) {
-          const int i = tid + m * 256;
+          const int i = tid - kYT0 + m * 256;
           const uint32_t bb = f32_to_bf16(yv[m] * r);
           xb[i] = (uint16_t)bb;
           xf[i] = bf16_to_f32(bb);
@@ -297,18 +347,21 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       __syncthreads();
     }
 
+    STACK_PHASE(2);  // input x staged
     // ---- router row: halves summed separately, as the per-layer router
     if (rrow < e_rows) {
       constexpr int half = (H % 512 == 0) ? kWrN / 2 : kWrN;
       float acc0 = 0.f, acc1 = 0.f;
+      wait_vm_n<0>();  // this wave's router row has landed in LDS
 #pragma unroll
       for (int m = 0; m < kWrN; ++m) {
         const float4 xv = *reinterpret_cast<const float4*>(xf + m * 256 + lane * 4);
+        const float4 wm = *reinterpret_cast<const float4*>(wrl + m * 256 + lane * 4);
         float s = m < half ? acc0 : acc1;
-        s = fmaf(wv[m].x, xv.x, s);
-        s = fmaf(wv[m].y, xv.y, s);
-        s = fmaf(wv[m].z, xv.z, s);
-        s = fmaf(wv[m].w, xv.w, s);
+        s = fmaf(wm.x, xv.x, s);
+        s = fmaf(wm.y, xv.y, s);
+        s = fmaf(wm.z, xv.z, s);
+        s = fmaf(wm.w, xv.w, s);
         if (m < half) acc0 = s; else acc1 = s;
       }
       acc0 = group_sum(acc0, kWave);
@@ -320,24 +373,49 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       }
     }
 
+    STACK_PHASE(3);  // router row published
     // ---- shared expert, independent of routing: its down rows are
     // requested and its gate/up rows computed (h published) while the
     // logits round trip is in flight
     uint32_t* hb = a.hbuf + (size_t)l * kRep * S::HW;
-    uint32_t xp[CPL][F::kPairs];
+    // this lane's x chunks as bf16 pairs, and their sums.  8-bit weights
+    // pair with x in natural order, so those pairs are read from LDS where
+    // they are used rather than held in registers across the layer
+    constexpr bool kXpLds = BITS == 8;
+    uint32_t xp[kXpLds ? 1 : CPL][F::kPairs];
     float xs[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int ci = sub + c * LPR;
-      pair_natural<BITS>(reinterpret_cast<const uint4*>(xb + ci * F::kEpc), xp[c], xs[c]);
+      uint32_t tmp[F::kPairs];
+      pair_natural<BITS>(reinterpret_cast<const uint4*>(xb + ci * F::kEpc),
+                         kXpLds ? tmp : xp[kXpLds ? 0 : c], xs[c]);
     }
+    auto x_pairs = [&](int c, uint32_t (&out)[F::kPairs]) {
+      if constexpr (kXpLds) {
+        const uint4* src = reinterpret_cast<const uint4*>(xb + (sub + c * LPR) * F::kEpc);
+#pragma unroll
+        for (int v = 0; v < F::kPairs / 4; ++v) {
+          const uint4 d = src[v];
+          out[4 * v] = d.x;
+          out[4 * v + 1] = d.y;
+          out[4 * v + 2] = d.z;
+          out[4 * v + 3] = d.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < F::kPairs; ++i) out[i] = xp[kXpLds ? 0 : c][i];
+      }
+    };
     // one row group of gate/up: h = bf16(silu(g) * u), kRep copies
     auto gu_rows = [&](const uint4 (&q)[2][CPL], const uint32_t (&sbw)[2][CPL], int base, int row) {
       float g = 0.f, u = 0.f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        g = chunk_term<BITS>(g, sbw[0][c], chunk_dot<BITS>(q[0][c], xp[c]), xs[c]);
-        u = chunk_term<BITS>(u, sbw[1][c], chunk_dot<BITS>(q[1][c], xp[c]), xs[c]);
+        uint32_t xc[F::kPairs];
+        x_pairs(c, xc);
+        g = chunk_term<BITS>(g, sbw[0][c], chunk_dot<BITS>(q[0][c], xc), xs[c]);
+        u = chunk_term<BITS>(u, sbw[1][c], chunk_dot<BITS>(q[1][c], xc), xs[c]);
       }
       g = group_sum(g, LPR);
       u = group_sum(u, LPR);
@@ -361,20 +439,20 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       }
     };
 
-    uint4 dq[S::DN];
-    uint32_t dsb[S::DN];
+    // shared down rows of this workgroup -> LDS (lanes of rows past R load
+    // nothing; their sums are never used)
 #pragma unroll
     for (int n = 0; n < S::DN; ++n) {
       const int it = wave + n * kNW;
       if (it >= K * S::NIR && it < S::NITEMS) {
         const int pp = it - K * S::NIR;
         const int ci = lane % S::CS, rloc = pp * S::RPPS + lane / S::CS;
-        dq[n] = make_uint4(0, 0, 0, 0);
-        dsb[n] = 0;
         if (rloc < R) {
           const int row = row0 + rloc;
-          dq[n] = ld16(D.shared_blob + a.sq[2] + (size_t)row * (IS * BITS / 8) + ci * 16);
-          dsb[n] = ldu32(D.shared_blob + a.ssb[2] + ((size_t)row * (IS / 64) + ci * F::kEpc / 64) * 4);
+          dma16(D.shared_blob + a.sq[2] + (size_t)row * (IS * BITS / 8) + ci * 16,
+                dq_m0 + n * 1024);
+          dma4(D.shared_blob + a.ssb[2] + ((size_t)row * (IS / 64) + ci * F::kEpc / 64) * 4,
+               dsb_m0 + n * 256);
         }
       }
     }
@@ -415,13 +493,15 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
         __builtin_amdgcn_s_sleep(1);
       }
+      STACK_PHASE(10);  // wave 0: every logit received
       if (!timed_out) {
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
           if (lane + kWave * i >= E) v[i] = 0.f;
           key[i] = lane + kWave * i < E ? order_key(v[i]) : 0u;
         }
-        wave_topk<VPL>(v, key, K, tmp_e, tmp_v, s_sel, s_val);
+        wave_topk<VPL>(v, key, K, tmp_e, tmp_v, tmp_k, s_sel, s_val);
+        STACK_PHASE(11);  // wave 0: top-k selected
         // renormalised weights = softmax over the chosen logits, summed in j order
         const float ex = lane < K ? expf(s_val[lane] - s_val[0]) : 0.f;
         float sum = 0.f;
@@ -458,6 +538,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       }
     }
     __syncthreads();
+    STACK_PHASE(4);  // top-k done (and the shared gate/up)
     if (s_abort) {
       failed = true;
         l_fail = l;
@@ -502,6 +583,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       }
     }
 
+    STACK_PHASE(5);  // routed gate/up done
     // ---- routed down requests for this workgroup's rows (needed after the h wait)
 #pragma unroll
     for (int n = 0; n < S::DN; ++n) {
@@ -512,24 +594,15 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         const uint8_t* blob =
             POOL ? s_addr[j]
                       : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
-        dq[n] = make_uint4(0, 0, 0, 0);
-        dsb[n] = 0;
         if (rloc < R) {
           const int row = row0 + rloc;
-          dq[n] = ld16(blob + a.lq[2] + (size_t)row * (I * BITS / 8) + ci * 16);
-          dsb[n] = ldu32(blob + a.lsb[2] + ((size_t)row * (I / 64) + ci * F::kEpc / 64) * 4);
+          dma16(blob + a.lq[2] + (size_t)row * (I * BITS / 8) + ci * 16, dq_m0 + n * 1024);
+          dma4(blob + a.lsb[2] + ((size_t)row * (I / 64) + ci * F::kEpc / 64) * 4,
+               dsb_m0 + n * 256);
         }
       }
     }
 
-    // ---- next layer's router row
-    if (l + 1 < a.L && rrow < e_rows) {
-      const StackLayerDesc& Dn = s_layers[l + 1];
-      const float* wr = rrow < E ? Dn.Wr + (size_t)rrow * H : Dn.wsg;
-#pragma unroll
-      for (int m = 0; m < kWrN; ++m) wv[m] = ldf4(wr + m * 256 + lane * 4);
-      if (rrow < E && Dn.rb) rbv = ldf(Dn.rb + rrow);
-    }
 
     // ---- down + combine for rows [row0, row0 + R): shared rows first (its h
     // was published during the logits round trip), then the routed rows
@@ -570,7 +643,9 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
             hp[4 * v + 2] = d.z;
             hp[4 * v + 3] = d.w;
           }
-          float acc = chunk_term<BITS>(0.f, dsb[n], chunk_dot<BITS>(dq[n], hp), hsum[chunk]);
+          const uint4 dq = *reinterpret_cast<const uint4*>(dwl + n * 1024 + lane * 16);
+          const uint32_t dsb = *reinterpret_cast<const uint32_t*>(dwl + S::DN * 1024 + n * 256 + lane * 4);
+          float acc = chunk_term<BITS>(0.f, dsb, chunk_dot<BITS>(dq, hp), hsum[chunk]);
           acc = group_sum(acc, C);
           if (ci == 0 && rloc < R) part[s * R + rloc] = acc;
         }
@@ -582,6 +657,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       break;
     }
     __syncthreads();
+    STACK_PHASE(6);  // shared h received
+    wait_vm_n<0>();  // every down weight of this wave has landed in LDS
     chunk_sums(K * I / F::kEpc, S::HW / F::kEpc);
     __syncthreads();
     down_items(true);
@@ -593,10 +670,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       break;
     }
     __syncthreads();
+    STACK_PHASE(7);  // routed h received
     chunk_sums(0, K * I / F::kEpc);
     __syncthreads();
     down_items(false);
     __syncthreads();
+    STACK_PHASE(8);  // down rows done
     if (tid < R * kRep) {  // kRep threads per row, one per copy
       const int r = tid % R, cp = tid / R, row = row0 + r;
       float y = 0.f;
@@ -608,6 +687,16 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         if (a.y_layers) a.y_layers[(size_t)l * H + row] = y;
         if (l == a.L - 1) a.y_last[row] = (uint16_t)f32_to_bf16(y);
       }
+    }
+    STACK_PHASE(9);  // y rows published
+    // the next layer's router row goes out once this layer's loads are all
+    // done (a wave's loads complete in order, so any later wait in this
+    // layer would wait for it too); waves 0..3, which own the router rows,
+    // do not poll the next y
+    if (l + 1 < a.L && rrow < e_rows) {
+      const StackLayerDesc& Dn = s_layers[l + 1];
+      router_request(Dn);
+      if (rrow < E && Dn.rb) rbv = ldf(Dn.rb + rrow);
     }
     // No barrier here: the next LDS writes that could meet this layer's
     // reads (s_w, part, hl) come after the next layer's y wait, itself a
@@ -640,7 +729,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n) {
 
 template <class S, int VPL, bool POOL>
 hipError_t launch_mode(const StackArgs& a, hipStream_t s) {
-  const size_t lds = stack_lds_bytes(S::H, a.E, S::K, S::I, S::IS, S::BITS);
+  const size_t lds = StackLds<S, VPL>::BYTES;
   hipError_t e = allow_lds(stack_decode_kernel<S, VPL, POOL>, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stack_decode_kernel<S, VPL, POOL>), dim3(kG), dim3(kNT), lds, s, a);
@@ -660,12 +749,6 @@ hipError_t launch_shape(const StackArgs& a, hipStream_t s) {
   X(4, 256, 64, 64, 2, 1)     /* small test shape */
 
 }  // namespace
-
-size_t stack_lds_bytes(int H, int E, int k, int I, int Is, int bits) {
-  (void)bits;
-  (void)E;
-  return (size_t)H * 6 + (size_t)(k * I + Is) * 2;
-}
 
 bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cus) {
   if (cus < kG || E + 1 > kNW * kG || E < k) return false;

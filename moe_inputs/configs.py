@@ -75,6 +75,11 @@ CONFIGS = {
                            top_k=10, inter=512, shared_inter=512, tokens=512,
                            batch=1, zipf=1.1, pool_frac=0.3, resident=False,
                            **_INT4),
+    # The same 80B-A3B-shaped int4 stack with every expert resident in HBM
+    # (same seeded weights as stream80b).
+    "decode80b": MoEConfig(name="decode80b", layers=48, hidden=2048, experts=512,
+                           top_k=10, inter=512, shared_inter=512, tokens=512,
+                           batch=1, zipf=1.1, **_INT4),
     # 80B-A3B-shaped decode, int8 experts, all resident; batch 1 and batch 8.
     "decode80b_int8": MoEConfig(name="decode80b_int8", layers=48, hidden=2048,
                                 experts=512, top_k=10, inter=512,
