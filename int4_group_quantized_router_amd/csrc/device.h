@@ -214,6 +214,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Lanes set in a wave mask, as a 32-bit count (two 32-bit popcounts keep
+// later comparisons of the count on the scalar unit).
+__device__ __forceinline__ uint32_t count_lanes(uint64_t m) {
+  return (uint32_t)__builtin_popcount((uint32_t)m) + (uint32_t)__builtin_popcount((uint32_t)(m >> 32));
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = threadIdx.x & 63;
   return lane ? (~0ull >> (64 - lane)) : 0ull;
@@ -231,15 +237,18 @@ template <int VPL, class IdxOf>
 __device__ void select_k(const float* v, const uint32_t* key, int k, IdxOf idx_of, int* tmp_e,
                          float* tmp_v, int* sel_e, float* sel_v) {
   const int lane = threadIdx.x & 63;
+  // (thr, cand and cnt are wave-uniform; readfirstlane keeps them scalar)
   uint32_t thr = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = thr | (1u << b);
-    int cnt = 0;
+  const uint32_t ku = (uint32_t)__builtin_amdgcn_readfirstlane(k);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) {
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = (uint32_t)__builtin_amdgcn_readfirstlane(thr | (1u << b));
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) cnt += count_lanes(__ballot(key[i] >= cand));
+    if (cnt >= ku) {
       thr = cand;
-      if (cnt == k) break;
+      if (cnt == ku) break;
     }
   }
   int n_gt = 0;
@@ -311,12 +320,14 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
 #pragma unroll
   for (int i = 1; i < VPL; ++i) mx = mx > key[i] ? mx : key[i];
   uint32_t t1 = 0;
+  const uint32_t ku = (uint32_t)__builtin_amdgcn_readfirstlane(k);
+#pragma unroll
   for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = t1 | (1u << b);
-    const int cnt = __popcll(__ballot(mx >= cand));
-    if (cnt >= k) {
+    const uint32_t cand = (uint32_t)__builtin_amdgcn_readfirstlane(t1 | (1u << b));
+    const uint32_t cnt = count_lanes(__ballot(mx >= cand));
+    if (cnt >= ku) {
       t1 = cand;
-      if (cnt == k) break;
+      if (cnt == ku) break;
     }
   }
   const uint64_t below = lanes_below();

@@ -125,37 +125,40 @@ __device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t dea
 }
 
 // Pairs [FIRST, FIRST + COUNT) of this layer's h words (dense: slot j < k
-// at j * I, shared at k * I), PER per thread.
-template <int COUNT>
+// at j * I, shared at k * I), PER per polling thread.  Pollers are the
+// threads [T0, T0 + N): every thread, or (see Roles) waves 0..3 alone.
+template <int N, int COUNT>
 constexpr int h_per() {
-  return (COUNT + kNT - 1) / kNT;
+  return (COUNT + N - 1) / N;
 }
 
 // Request this thread's pairs; `done` marks pairs already staged.
-template <int FIRST, int COUNT>
+template <int T0, int N, int FIRST, int COUNT>
 __device__ __forceinline__ void h_request(const uint64_t* src, uint32_t done,
-                                          uint64_t (&e)[h_per<COUNT>()]) {
+                                          uint64_t (&e)[h_per<N, COUNT>()]) {
+  const int t = (int)threadIdx.x - T0;
 #pragma unroll
-  for (int m = 0; m < h_per<COUNT>(); ++m) {
-    const int i = threadIdx.x + m * kNT;
-    e[m] = (i < COUNT && !((done >> m) & 1u)) ? ld_dev(src + FIRST + i) : 0ull;
+  for (int m = 0; m < h_per<N, COUNT>(); ++m) {
+    const int i = t + m * N;
+    e[m] = (t >= 0 && t < N && i < COUNT && !((done >> m) & 1u)) ? ld_dev(src + FIRST + i) : 0ull;
   }
 }
 
 // Wait for the pairs, starting from the already requested round `e`, and
 // stage them in LDS as bf16 pairs: hl[i] = (h[2i], h[2i+1]).
-template <int FIRST, int COUNT>
+template <int T0, int N, int FIRST, int COUNT>
 __device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_t deadline,
-                       uint64_t (&e)[h_per<COUNT>()]) {
-  constexpr int PER = h_per<COUNT>();
+                       uint64_t (&e)[h_per<N, COUNT>()]) {
+  constexpr int PER = h_per<N, COUNT>();
   static_assert(PER <= 32, "h pairs per thread");
+  const int t = (int)threadIdx.x - T0;
   uint32_t done = 0;
   for (;;) {
     bool ok = true;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int i = threadIdx.x + m * kNT;
-      if (i < COUNT && !((done >> m) & 1u)) {
+      const int i = t + m * N;
+      if (t >= 0 && t < N && i < COUNT && !((done >> m) & 1u)) {
         const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
         if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
           hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
@@ -168,9 +171,22 @@ __device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_
     bool to = false;
     if (poll_round(ok, deadline, &to)) return true;
     if (to) return false;
-    h_request<FIRST, COUNT>(src, done, e);
+    h_request<T0, N, FIRST, COUNT>(src, done, e);
   }
 }
+
+// Division of the down-phase work between the waves of a workgroup.  A
+// wave's loads complete in order, so a poll issued behind a wave's own
+// down-weight loads waits for them.  SPLIT: waves 4..7 (which have the
+// fewest routed gate/up rows) load every down item's weights and waves
+// 0..3 poll h -- fewer address registers per wave, which the 8-bit shapes
+// need to stay within 256 VGPRs; otherwise every wave loads the items it
+// computes and every thread polls.
+template <int BITS>
+struct Roles {
+  static constexpr bool SPLIT = BITS == 8;
+  static constexpr int HT0 = 0, HN = SPLIT ? 256 : kNT;
+};
 
 // Compile-time geometry of one model shape.
 template <int BITS_, int H_, int I_, int IS_, int K_>
@@ -204,9 +220,9 @@ struct Shape {
 
 // LDS of one workgroup (bytes; every region 16-byte aligned): the layer
 // input (f32 and bf16), the h pairs, the router row of each wave that may
-// own one, and per wave DN slots of down weights (16 bytes per lane) and of
-// their (scale, bias) words (4 bytes per lane), both filled by
-// direct-to-LDS loads.
+// own one, and one slot per down item of the workgroup (NITEMS): its
+// weights (16 bytes per lane) and (scale, bias) words (4 bytes per lane),
+// filled by direct-to-LDS loads.
 template <class S, int VPL>
 struct StackLds {
   static constexpr int kRwRaw = (64 * VPL + 1 + kG - 1) / kG;
@@ -215,8 +231,8 @@ struct StackLds {
   static constexpr size_t HL = (size_t)S::H * 6;
   static constexpr size_t WR = HL + (size_t)S::HW * 2;
   static constexpr size_t DW = WR + (size_t)RW * S::H * 4;
-  static constexpr size_t kDwWave = (size_t)S::DN * (1024 + 256);
-  static constexpr size_t BYTES = DW + kNW * kDwWave;
+  static constexpr size_t DSB = DW + (size_t)S::NITEMS * 1024;
+  static constexpr size_t BYTES = DSB + (size_t)S::NITEMS * 256;
   static_assert(XB % 16 == 0 && HL % 16 == 0 && WR % 16 == 0 && DW % 16 == 0, "LDS alignment");
 };
 
@@ -226,6 +242,7 @@ struct StackLds {
 template <class S, int VPL, bool POOL>
 __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   using F = typename S::F;
+  using RO = Roles<S::BITS>;
   constexpr int BITS = S::BITS, H = S::H, I = S::I, IS = S::IS, K = S::K, R = S::R;
   constexpr int CPL = S::CPL, LPR = S::LPR, RPP = S::RPP;
   constexpr int kWrN = H / 256;  // float4 router loads per lane (a whole row per wave)
@@ -257,10 +274,11 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   uint32_t* hl = reinterpret_cast<uint32_t*>(smem + LD::HL);        // [HW / 2] h pairs
   // router row of each wave that has one (waves 0 .. (E + 1) / G), f32 [H]
   float* wrl = reinterpret_cast<float*>(smem + LD::WR) + (size_t)wave * H;
-  // this wave's down-weight slots: 16 bytes per lane per item, then the
-  // items' (scale, bias) words, 4 bytes per lane
-  const uint8_t* dwl = smem + LD::DW + (size_t)wave * LD::kDwWave;
-  const uint32_t dq_m0 = lds_addr(dwl), dsb_m0 = dq_m0 + S::DN * 1024;
+  // down items' slots: weights (item it at dwl + 1024 it, lane i's 16 bytes
+  // at + 16 i) and (scale, bias) words (at dsbl + 256 it + 4 i)
+  const uint8_t* dwl = smem + LD::DW;
+  const uint8_t* dsbl = smem + LD::DSB;
+  const uint32_t dq_m0 = lds_addr(dwl), dsb_m0 = lds_addr(dsbl);
 
   const int rep = blk % kRep;  // the XCD of this workgroup
   const uint32_t epoch = ld_dev(a.epochs + blk);
@@ -278,6 +296,23 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   const int sub = lane % LPR, rsub = lane / LPR;
   const int gw = wave * kG + blk;  // global wave index: gate/up row group gw + n * 8G
   const int row0 = blk * R;        // down rows [row0, row0 + R)
+  // one down item's weights into its slot: lane i loads what lane i of the
+  // wave that computes the item will read (lanes of rows past R load
+  // nothing; their sums are never used).  Each wave loads the items it
+  // computes.
+  auto down_request = [&](int it, const uint8_t* blob, bool shared) {
+    const int C = shared ? S::CS : S::CR, RP = shared ? S::RPPS : S::RPPR;
+    const int II = shared ? IS : I;
+    const int pp = shared ? it - K * S::NIR : it % S::NIR;
+    const int ci = lane % C, rloc = pp * RP + lane / C;
+    const uint32_t* qo = shared ? a.sq : a.lq;
+    const uint32_t* so = shared ? a.ssb : a.lsb;
+    if (rloc < R) {
+      const int row = row0 + rloc;
+      dma16(blob + qo[2] + (size_t)row * (II * BITS / 8) + ci * 16, dq_m0 + it * 1024);
+      dma4(blob + so[2] + ((size_t)row * (II / 64) + ci * F::kEpc / 64) * 4, dsb_m0 + it * 256);
+    }
+  };
 
   // router row of each wave (E = the shared gate), requested one layer
   // ahead straight into LDS (lane i's float4 m at wrl + 256 m + 4 i)
@@ -439,23 +474,6 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       }
     };
 
-    // shared down rows of this workgroup -> LDS (lanes of rows past R load
-    // nothing; their sums are never used)
-#pragma unroll
-    for (int n = 0; n < S::DN; ++n) {
-      const int it = wave + n * kNW;
-      if (it >= K * S::NIR && it < S::NITEMS) {
-        const int pp = it - K * S::NIR;
-        const int ci = lane % S::CS, rloc = pp * S::RPPS + lane / S::CS;
-        if (rloc < R) {
-          const int row = row0 + rloc;
-          dma16(D.shared_blob + a.sq[2] + (size_t)row * (IS * BITS / 8) + ci * 16,
-                dq_m0 + n * 1024);
-          dma4(D.shared_blob + a.ssb[2] + ((size_t)row * (IS / 64) + ci * F::kEpc / 64) * 4,
-               dsb_m0 + n * 256);
-        }
-      }
-    }
     // Wave 0 waits for the logits (in the registers the top-k reads) and
     // selects; waves 1..7 compute the shared expert's gate/up meanwhile.
     __shared__ int s_abort;
@@ -536,6 +554,25 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         const int p = q0 + n * (kNW - 1) * kG;
         if (p < S::PS) gu_rows(gq[n], gsb[n], K * I, p * RPP + rsub);
       }
+      // shared down items -> LDS, after the loads above have been used
+      if constexpr (RO::SPLIT) {
+        if (wave >= 4) {
+#pragma unroll
+          for (int n = 0; n < (S::NIS + 3) / 4; ++n) {
+            const int it = K * S::NIR + (wave - 4) + 4 * n;
+            if (it < S::NITEMS) down_request(it, D.shared_blob, true);
+          }
+        }
+      } else {
+        // waves 1..7 in turn (wave 0 is selecting); whoever computes an item
+        // reads it after the workgroup barrier that follows every wave's
+        // wait for its own loads
+#pragma unroll
+        for (int n = 0; n < (S::NIS + kNW - 2) / (kNW - 1); ++n) {
+          const int it = K * S::NIR + (wave - 1) + (kNW - 1) * n;
+          if (it < S::NITEMS) down_request(it, D.shared_blob, true);
+        }
+      }
     }
     __syncthreads();
     STACK_PHASE(4);  // top-k done (and the shared gate/up)
@@ -551,7 +588,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     // the shared h (published while the logits were in flight) is requested
     // after the first routed gate/up pass and looked at after the last
     const uint64_t* hrep = reinterpret_cast<const uint64_t*>(hb + (size_t)rep * S::HW);
-    uint64_t hsh[h_per<IS / 2>()];
+    uint64_t hsh[h_per<RO::HN, IS / 2>()];
 
     // ---- routed gate/up: row group gw + n * 8G of K * PR; at most DEPTH
     // passes of weights are in flight per lane
@@ -579,27 +616,33 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           gu_rows(gq[n % DEPTH], gsb[n % DEPTH], j * I, (pr % S::PR) * RPP + rsub);
         }
         if (n + DEPTH < S::NPR) routed_load(n + DEPTH);
-        if (n == 0) h_request<K * I / 2, IS / 2>(hrep, 0u, hsh);
+        if (n == 0) h_request<RO::HT0, RO::HN, K * I / 2, IS / 2>(hrep, 0u, hsh);
       }
     }
 
     STACK_PHASE(5);  // routed gate/up done
-    // ---- routed down requests for this workgroup's rows (needed after the h wait)
+    // ---- routed down items -> LDS (needed after the h wait)
+    auto routed_item = [&](int it) {
+      const int j = it / S::NIR;
+      const uint8_t* blob =
+          POOL ? s_addr[j]
+               : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
+      down_request(it, blob, false);
+    };
+    if constexpr (RO::SPLIT) {
+      if (wave >= 4) {
 #pragma unroll
-    for (int n = 0; n < S::DN; ++n) {
-      const int it = wave + n * kNW;
-      if (it < K * S::NIR) {
-        const int j = it / S::NIR, pp = it % S::NIR;
-        const int ci = lane % S::CR, rloc = pp * S::RPPR + lane / S::CR;
-        const uint8_t* blob =
-            POOL ? s_addr[j]
-                      : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
-        if (rloc < R) {
-          const int row = row0 + rloc;
-          dma16(blob + a.lq[2] + (size_t)row * (I * BITS / 8) + ci * 16, dq_m0 + n * 1024);
-          dma4(blob + a.lsb[2] + ((size_t)row * (I / 64) + ci * F::kEpc / 64) * 4,
-               dsb_m0 + n * 256);
+        for (int n = 0; n < (K * S::NIR + 3) / 4; ++n) {
+          const int it = (wave - 4) + 4 * n;
+          if (it < K * S::NIR) routed_item(it);
         }
+        wait_vm_n<0>();
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < S::DN; ++n) {
+        const int it = wave + n * kNW;
+        if (it < K * S::NIR) routed_item(it);
       }
     }
 
@@ -643,28 +686,28 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
             hp[4 * v + 2] = d.z;
             hp[4 * v + 3] = d.w;
           }
-          const uint4 dq = *reinterpret_cast<const uint4*>(dwl + n * 1024 + lane * 16);
-          const uint32_t dsb = *reinterpret_cast<const uint32_t*>(dwl + S::DN * 1024 + n * 256 + lane * 4);
+          const uint4 dq = *reinterpret_cast<const uint4*>(dwl + (size_t)it * 1024 + lane * 16);
+          const uint32_t dsb = *reinterpret_cast<const uint32_t*>(dsbl + (size_t)it * 256 + lane * 4);
           float acc = chunk_term<BITS>(0.f, dsb, chunk_dot<BITS>(dq, hp), hsum[chunk]);
           acc = group_sum(acc, C);
           if (ci == 0 && rloc < R) part[s * R + rloc] = acc;
         }
       }
     };
-    if (!poll_h<K * I / 2, IS / 2>(hrep, tag16, hl, deadline, hsh)) {
+    if (!poll_h<RO::HT0, RO::HN, K * I / 2, IS / 2>(hrep, tag16, hl, deadline, hsh)) {
       failed = true;
         l_fail = l;
       break;
     }
     __syncthreads();
     STACK_PHASE(6);  // shared h received
-    wait_vm_n<0>();  // every down weight of this wave has landed in LDS
+    wait_vm_n<0>();  // this wave's down-item loads have landed
     chunk_sums(K * I / F::kEpc, S::HW / F::kEpc);
     __syncthreads();
     down_items(true);
-    uint64_t hrt[h_per<K * I / 2>()];
-    h_request<0, K * I / 2>(hrep, 0u, hrt);
-    if (!poll_h<0, K * I / 2>(hrep, tag16, hl, deadline, hrt)) {
+    uint64_t hrt[h_per<RO::HN, K * I / 2>()];
+    h_request<RO::HT0, RO::HN, 0, K * I / 2>(hrep, 0u, hrt);
+    if (!poll_h<RO::HT0, RO::HN, 0, K * I / 2>(hrep, tag16, hl, deadline, hrt)) {
       failed = true;
         l_fail = l;
       break;
