@@ -57,7 +57,15 @@ KERNEL_SOURCES = {
 }
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
+    # profiles/decode80b_int8_stack_decode_kernel.md
+    "decode80b_int8": ("stack", 975091, 79900, "8519f761ae6f337d"),
 }
+# bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
+# algorithmic bytes are streamed once per phase with 3 dependent all-to-all
+# hand-offs per phase (the stack kernel's count per layer) -- the ceiling a
+# batch-1 decode layer of that size reaches on this device
+# (profiles/decode_layer_ceiling.md).
+CEILING_3HANDOFFS_GBPS = {"decode80b_int8": 3048.0, "decode80b": 2197.0, "decode35b": 1962.0}
 
 
 def kernel_digest(kind):
@@ -224,6 +232,33 @@ def calibrate_peaks():
           flush=True)
 
 
+def calibrate_stream():
+    """The ceiling of a batch-1 decode layer: the calibration kernel streams
+    each workload's per-layer algorithmic bytes once per phase, on the stack
+    kernel's grid, with 0, 1 or 3 dependent all-to-all hand-offs per phase
+    (the stack kernel has 3 per layer), over as many phases as the stack has
+    layers; microseconds per phase and the GB/s they give."""
+    import torch
+    import int4_group_quantized_router_amd as m
+    from moe_inputs import CONFIGS
+    torch.cuda.set_device(0)
+    rows = []
+    for name in ("decode80b_int8", "decode80b", "decode35b"):
+        cfg = CONFIGS[name]
+        nbytes = (algorithmic_bytes(cfg)["layer"] + 15) // 16 * 16
+        buf = torch.empty(cfg.layers * nbytes, dtype=torch.uint8, device="cuda")
+        for handoffs in (0, 1, 3):
+            ms = m.moe_calibrate_stream(buf, nbytes, cfg.layers, handoffs, reps=10)
+            us = ms * 1e3 / cfg.layers
+            rows.append({"workload": name, "bytes_per_phase": nbytes, "phases": cfg.layers,
+                         "handoffs_per_phase": handoffs, "us_per_phase": us,
+                         "GBps": nbytes / us / 1e3, "frac_of_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBS})
+            log(f"[calibrate] {name}: {nbytes / 1e6:.2f} MB + {handoffs} hand-offs per phase: "
+                f"{us:.2f} us ({nbytes / us / 1e3:.0f} GB/s)")
+        del buf
+    print(json.dumps({"calibrate_stream": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -245,6 +280,9 @@ def main():
                     help="only run 10 device-to-device copies of BYTES (reference for HBM counters)")
     ap.add_argument("--calibrate-peaks", action="store_true",
                     help="only measure a 1 GiB device copy and an 8192^3 bf16 matmul")
+    ap.add_argument("--calibrate-stream", action="store_true",
+                    help="only measure the decode-layer ceiling: each workload's per-layer "
+                         "bytes streamed per phase with 0, 1 or 3 all-to-all hand-offs")
     ap.add_argument("--phases", type=int, default=0, metavar="TOKENS",
                     help="decode: run TOKENS tokens through the profiling build "
                          "(libmoe_phases.so, built by `python -m "
@@ -263,6 +301,8 @@ def main():
         return calibrate_copy(args.calibrate_copy)
     if args.calibrate_peaks:
         return calibrate_peaks()
+    if args.calibrate_stream:
+        return calibrate_stream()
     from moe_inputs import CONFIGS
 
     cfg = CONFIGS[args.workload]
@@ -480,6 +520,9 @@ def bench_decode(args, cfg):
             "expert_quantized_GBps": k_quant / k_mean_s / 1e9,
             "expert_quantized_frac": k_quant / k_mean_s / 1e9 / HBM_PEAK_GBS,
             "frac_of_measured_copy": achieved / MEASURED_COPY_GBS,
+            "frac_of_layer_ceiling": (achieved / CEILING_3HANDOFFS_GBPS[cfg.name]
+                                      if persistent and cfg.name in CEILING_3HANDOFFS_GBPS
+                                      else None),
             "mean_launch_us": k_mean_s * 1e6,
             "launches": int(len(gu_ms)),
         },

@@ -469,6 +469,20 @@ int32_t moe_timer_attach(moe_timer* timer);
 int32_t moe_timer_read(moe_timer* timer, float* ms, int32_t* n);
 int32_t moe_timer_destroy(moe_timer* timer);
 
+/* ------------------------------------------------------------------------
+ * Calibration hook: the ceiling of a batch-1 decode layer on this device.
+ * On the persistent stack kernel's grid (256 workgroups, all resident),
+ * `phases` times: read `bytes` of fresh memory (phase p reads buf + p*bytes,
+ * 16-byte loads), then `handoffs` all-to-all exchanges of tagged words (the
+ * stack kernel's hand-off).  buf: device memory of at least phases * bytes
+ * (read only); bytes a positive multiple of 16; 0 <= handoffs <= 8.  One
+ * warm-up launch, then `reps` timed ones; ms (out): mean milliseconds per
+ * launch.  Synchronises `stream`.  MOE_E_INVAL on a device with fewer than
+ * 256 compute units; MOE_E_HIP if a wait runs out of time (2 s).
+ * ---------------------------------------------------------------------- */
+int32_t moe_calibrate_stream(const void* buf, int64_t bytes, int32_t phases, int32_t handoffs,
+                             int32_t reps, float* ms, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

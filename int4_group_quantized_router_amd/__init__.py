@@ -399,6 +399,18 @@ def moe_stack_destroy(stack) -> None:
     _check(_lib_().moe_stack_destroy(_h(stack)), "moe_stack_destroy")
 
 
+# ------------------------------------------------------------- calibration
+
+def moe_calibrate_stream(buf, bytes_per_phase: int, phases: int, handoffs: int, reps: int = 5,
+                         stream=None) -> float:
+    """Mean ms per launch of the streaming calibration kernel (see moe.h)."""
+    ms = C.c_float()
+    _check(_lib_().moe_calibrate_stream(_dptr(buf), int(bytes_per_phase), int(phases),
+                                        int(handoffs), int(reps), C.byref(ms), _stream(stream)),
+           "moe_calibrate_stream")
+    return ms.value
+
+
 # ------------------------------------------------------------------ timing
 
 def moe_timer_create(kernel: int, capacity: int) -> Handle:

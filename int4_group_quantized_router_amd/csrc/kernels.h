@@ -207,6 +207,13 @@ struct StackArgs {
 bool stack_decode_supported(int H, int E, int k, int I, int Is, int bits, int cus);
 hipError_t launch_stack_decode(const StackArgs& a, int H, int k, int I, int Is, int bits,
                                hipStream_t s);
+// Calibration: phases x (stream `bytes` of buf, then `handoffs` all-to-all
+// tagged exchanges) on the stack kernel's grid.  words: [phases][handoffs]
+// [replicas][grid] u64; epochs: [grid] call counters; sink: [grid][threads].
+hipError_t launch_stream_phases(const void* buf, int64_t bytes, int phases, int handoffs,
+                                uint64_t* words, uint32_t* epochs, float* sink, int32_t* err,
+                                int64_t timeout_ticks, hipStream_t s);
+
 // Zero `bytes` (a multiple of 4) of device memory with a kernel (usable
 // where a memset node would not be, e.g. under stream capture).
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -1150,6 +1150,58 @@ int32_t moe_stack_destroy(moe_stack* stack) {
   return MOE_OK;
 }
 
+int32_t moe_calibrate_stream(const void* buf, int64_t bytes, int32_t phases, int32_t handoffs,
+                             int32_t reps, float* ms, hipStream_t stream) {
+  clear_error();
+  MOE_REQUIRE(buf && ms, "null argument");
+  MOE_REQUIRE(bytes > 0 && bytes % 16 == 0, "bytes must be a positive multiple of 16");
+  MOE_REQUIRE(phases >= 1 && handoffs >= 0 && handoffs <= 8 && reps >= 1, "bad argument");
+  int dev = 0, cus = 0, clk_khz = 0;
+  MOE_HIP_TRY(hipGetDevice(&dev));
+  MOE_HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  MOE_HIP_TRY(hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, dev));
+  MOE_REQUIRE(cus >= kStackGrid, "needs %d compute units (the device has %d)", kStackGrid, cus);
+  const size_t wbytes = (size_t)phases * (handoffs > 0 ? handoffs : 1) * kStackReplicas *
+                        kStackGrid * 8;
+  const size_t sizes[] = {wbytes, (size_t)kStackGrid * 4, (size_t)kStackGrid * kStackThreads * 4};
+  size_t total = 0;
+  for (size_t sz : sizes) total += align256(sz);
+  void* mem = nullptr;
+  int32_t* err = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  MOE_HIP_TRY(hipMalloc(&mem, total));
+  hipError_t e = hipMemset(mem, 0, total);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&err), 4, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  uint8_t* p = static_cast<uint8_t*>(mem);
+  uint64_t* words = reinterpret_cast<uint64_t*>(p);
+  uint32_t* epochs = reinterpret_cast<uint32_t*>(p + align256(sizes[0]));
+  float* sink = reinterpret_cast<float*>(p + align256(sizes[0]) + align256(sizes[1]));
+  const int64_t ticks = (int64_t)clk_khz * 1000 * 2;
+  if (e == hipSuccess) {
+    *err = 0;
+    // one launch to warm up, then `reps` timed ones (fresh tags each time)
+    e = launch_stream_phases(buf, bytes, phases, handoffs, words, epochs, sink, err, ticks, stream);
+    if (e == hipSuccess) e = hipEventRecord(e0, stream);
+    for (int r = 0; r < reps && e == hipSuccess; ++r)
+      e = launch_stream_phases(buf, bytes, phases, handoffs, words, epochs, sink, err, ticks,
+                               stream);
+    if (e == hipSuccess) e = hipEventRecord(e1, stream);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(ms, e0, e1);
+    if (e == hipSuccess) *ms /= (float)reps;
+  }
+  const bool timed_out = err && *err;
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (err) (void)hipHostFree(err);
+  (void)hipFree(mem);
+  MOE_HIP_TRY(e);
+  if (timed_out) return fail(MOE_E_HIP, "calibration kernel ran out of time");
+  return MOE_OK;
+}
+
 int32_t moe_timer_create(int32_t kernel, int32_t capacity, moe_timer** out) {
   clear_error();
   MOE_REQUIRE(out && capacity >= 1 && kernel >= MOE_KERNEL_ROUTE && kernel <= MOE_KERNEL_STACK,
