@@ -389,17 +389,18 @@ int32_t moe_layer_destroy(moe_layer* layer);
  *
  * On a pool the kernel reads each chosen expert's address from the pool's
  * device table and stops at the first layer with a non-resident choice
- * (all workgroups see the same top-k, so all stop there).  The calling
- * thread waits for the kernel, records the hits of the layers that ran
- * (they enter the pool policy in access order before any later use of the
- * pool: every slotpool_* call, and the next pooled stack call right after
- * its launch, applies them first), runs the stopped layer as a pooled
- * moe_layer_forward (which fills its misses) and relaunches from the next
- * layer.  The calling thread thus waits for every persistent launch of the
- * call (work after the last one may still be queued on `stream` when it
- * returns); the pool sees the same accesses, in the same order, as
- * per-layer calls would give, and the outputs equal the resident stack's
- * bit for bit.
+ * (all workgroups see the same top-k, so all stop there), after exporting
+ * that layer's choices.  The calling thread waits for the kernel, records
+ * the hits of the layers that ran (they enter the pool policy in access
+ * order before any later use of the pool: every slotpool_* call, and the
+ * next pooled stack call right after its launch, applies them first),
+ * acquires the stopped layer's choices (filling its misses: one copy each),
+ * launches the kernel again at that layer from the previous layer's output,
+ * and releases the layer behind that launch.  The calling thread thus waits
+ * for every persistent launch of the call (work after the last one may
+ * still be queued on `stream` when it returns); the pool sees the same
+ * accesses, in the same order, as per-layer calls would give, and the
+ * outputs equal the resident stack's bit for bit.
  * ---------------------------------------------------------------------- */
 typedef struct moe_stack moe_stack;
 

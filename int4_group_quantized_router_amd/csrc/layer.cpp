@@ -82,7 +82,8 @@ struct moe_stack {
   slotpool* pool = nullptr;
   int32_t* stop_host = nullptr;  // pinned: the layer the kernel stopped at
   int32_t* idx_host = nullptr;   // pinned [L][k]: every layer's choices
-  uint16_t* xl_dev = nullptr;    // device [L][H]: layer inputs, to resume from
+  uint16_t* xl_dev = nullptr;    // device [L][H]: layer inputs (export)
+  float* yl_dev = nullptr;       // device [L][H]: layer outputs, to resume from
   std::vector<int32_t> layer_ids;
   // launches so far (the device's per-workgroup call counters hold the
   // same value), and per layer a lower bound on the launch that wrote any
@@ -375,6 +376,8 @@ int32_t setup_persistent(moe_stack* st) {
                         hipHostMallocDefault);
     if (e == hipSuccess)
       e = hipMalloc(reinterpret_cast<void**>(&st->xl_dev), (size_t)n * H * sizeof(uint16_t));
+    if (e == hipSuccess)
+      e = hipMalloc(reinterpret_cast<void**>(&st->yl_dev), (size_t)n * H * sizeof(float));
     for (const moe_layer* L : st->layers) st->layer_ids.push_back(L->cfg.layer_index);
   }
   if (e != hipSuccess) {
@@ -383,8 +386,10 @@ int32_t setup_persistent(moe_stack* st) {
     if (st->stop_host) (void)hipHostFree(st->stop_host);
     if (st->idx_host) (void)hipHostFree(st->idx_host);
     if (st->xl_dev) (void)hipFree(st->xl_dev);
+    if (st->yl_dev) (void)hipFree(st->yl_dev);
     st->stop_host = st->idx_host = nullptr;
     st->xl_dev = nullptr;
+    st->yl_dev = nullptr;
     return fail(MOE_E_HIP, "stack setup: %s", hipGetErrorString(e));
   }
   *st->err_host = 0;
@@ -978,9 +983,10 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     const moe_layer_cfg& c = stack->layers[0]->cfg;
     const int nl = (int)stack->layers.size(), H = c.hidden, k = c.top_k;
     if (stack->pool) {
-      // the kernel reads the pool's table; it exports every layer's input
+      // the kernel reads the pool's table; it exports every layer's output
       // (to resume from) and choices (for the pool policy)
       a.x_layers = x_layers ? x_layers : stack->xl_dev;
+      a.y_layers = y_layers ? y_layers : stack->yl_dev;
       a.idx = stack->idx_host;
       *stack->stop_host = nl;
       const int32_t st = pool_before_lookup(stack->pool, stream);
@@ -1004,10 +1010,13 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
     // with a non-resident choice, or nl) before it can go on.  The policy
     // then sees the layers the kernel ran as the per-layer path would have
     // (each a call whose experts all hit, in order; held in the pool and
-    // applied before its next use); the stopped layer runs on the per-layer
-    // path (its misses are filled there), and the kernel resumes from the
-    // next layer with that layer's output.
-    int l0 = 0;
+    // applied before its next use).  The stopped layer's choices, which the
+    // kernel exported before it stopped, are acquired (its misses filled),
+    // and the kernel is launched again at that layer, from the previous
+    // layer's output; the layer is released right behind that launch, as
+    // the per-layer path releases it behind its kernels.
+    int l0 = 0;       // first layer of the launch in flight
+    int replay0 = 0;  // first layer of it whose accesses the pool has not seen
     for (;;) {
       const hipError_t se = hipStreamSynchronize(stream);
       if (se != hipSuccess) {
@@ -1022,40 +1031,46 @@ int32_t moe_stack_forward(moe_stack* stack, const uint16_t* x0, int32_t T, uint1
         return fail(MOE_E_HIP, "a persistent decode call on this stack timed out");
       }
       const int stop = *stack->stop_host;
-      if (stop < l0 || stop > nl) {
+      if (stop < replay0 || stop > nl) {
         stack->epoch += 1;
         stack_forget(stack);
-        return fail(MOE_E_HIP, "persistent decode stopped at layer %d", stop);
+        return fail(MOE_E_HIP, "persistent decode stopped at layer %d (launched at %d)", stop, l0);
       }
       stack_launched(stack, l0, stop);
-      int32_t st = pool_defer_hits(stack->pool, stack->layer_ids.data() + l0,
-                                   stack->idx_host + (size_t)l0 * k, stop - l0, k, stream);
+      int32_t st = pool_defer_hits(stack->pool, stack->layer_ids.data() + replay0,
+                                   stack->idx_host + (size_t)replay0 * k, stop - replay0, k,
+                                   stream);
       if (st != MOE_OK) return st;
       if (idx && stop > l0)
         MOE_HIP_TRY(hipMemcpyAsync(idx + (size_t)l0 * k, stack->idx_host + (size_t)l0 * k,
                                    (size_t)(stop - l0) * k * sizeof(int32_t),
                                    hipMemcpyHostToDevice, stream));
       if (stop == nl) return MOE_OK;
-      moe_layer* L = stack->layers[stop];
-      float* yout = y_layers ? y_layers + (size_t)stop * H : L->y;
-      st = forward_decode(L, a.x_layers + (size_t)stop * H, nullptr, nullptr, 1,
-                          stop == nl - 1 ? y_last : nullptr, yout,
-                          idx ? idx + (size_t)stop * k : nullptr, w ? w + (size_t)stop * k : nullptr,
-                          stream);
+      // the stopped layer's choices (distinct, in selection order, as the
+      // per-layer router lists them) -> resident and pinned
+      int32_t experts[MOE_MAX_TOPK];
+      const void* ptrs[MOE_MAX_TOPK];
+      for (int j = 0; j < k; ++j) experts[j] = stack->idx_host[(size_t)stop * k + j];
+      const int32_t lid = stack->layer_ids[stop];
+      st = slotpool_acquire(stack->pool, lid, experts, k, stream, ptrs, nullptr);
       if (st != MOE_OK) return st;
-      if (stop == nl - 1) return MOE_OK;
       // the kernel that wrote the pinned words has finished (the sync
       // above); the relaunch writes them again only after what was enqueued
-      // since, the copy of its choices included
-      l0 = stop + 1;
+      // since, the copy of the choices included
+      l0 = stop;
+      replay0 = stop + 1;
       a.l0 = l0;
-      a.y_start = yout;
+      a.y_start = stop > 0 ? a.y_layers + (size_t)(stop - 1) * H : nullptr;
       *stack->stop_host = nl;
       st = pool_before_lookup(stack->pool, stream);
+      if (st == MOE_OK) st = stack_clear_stale(stack, l0, stream);
+      const hipError_t le =
+          st == MOE_OK ? launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream)
+                       : hipSuccess;
+      const int32_t rst = slotpool_release(stack->pool, lid, experts, k, stream);
       if (st != MOE_OK) return st;
-      st = stack_clear_stale(stack, l0, stream);
-      if (st != MOE_OK) return st;
-      MOE_HIP_TRY(launch_stack_decode(a, H, k, c.inter, c.shared_inter, c.bits, stream));
+      MOE_HIP_TRY(le);
+      if (rst != MOE_OK) return rst;
     }
   }
   const int n = (int)stack->layers.size();
@@ -1145,6 +1160,7 @@ int32_t moe_stack_destroy(moe_stack* stack) {
   if (stack->stop_host) (void)hipHostFree(stack->stop_host);
   if (stack->idx_host) (void)hipHostFree(stack->idx_host);
   if (stack->xl_dev) (void)hipFree(stack->xl_dev);
+  if (stack->yl_dev) (void)hipFree(stack->yl_dev);
   delete stack;
   if (e != hipSuccess) return fail(MOE_E_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
   return MOE_OK;
