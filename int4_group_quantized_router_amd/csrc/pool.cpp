@@ -185,6 +185,15 @@ void drop(slotpool* p, int32_t s) {
   x.layer = x.expert = -1;
   x.count = x.last = 0;
   p->free_slots.insert(s);
+#ifdef MOE_POOL_POISON
+  // Debug builds: a dropped slot is overwritten with 0xFF bytes (f32 and
+  // bf16 NaN, all-ones scales and fields) once its last reader is done, so
+  // a kernel that reads a slot it no longer owns produces NaN instead of a
+  // plausible stale expert.  The next fill of the slot replaces them.
+  if (x.last_use) (void)hipStreamWaitEvent(p->copy, x.last_use, 0);
+  (void)hipMemsetAsync(p->dev + (int64_t)s * p->store->stride, 0xFF, (size_t)p->store->stride,
+                       p->copy);
+#endif
 }
 
 // Copy the table entries changed since the last push (after everything
