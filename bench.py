@@ -58,7 +58,7 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
-    "decode80b_int8": ("stack", 975091, 79900, "8519f761ae6f337d"),
+    "decode80b_int8": ("stack", 976098, 79900, "b37f8cb72b9a6097"),
 }
 # bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
 # algorithmic bytes are streamed once per phase with 3 dependent all-to-all
@@ -336,7 +336,7 @@ def bench_phases(args, cfg):
     log(f"[phases] building {cfg.name}: {cfg.layers} layers")
     layers, stack, keep = _build_stack(cfg)
     assert m.moe_stack_persistent_active(stack)
-    L, G, P = cfg.layers, 256, 12
+    L, G, P = cfg.layers, 256, 20
     n = args.phases
     warm = 8
     X = torch.from_numpy(tokens_x(cfg, 0, warm + n).view(np.int16)).cuda()
@@ -353,14 +353,27 @@ def bench_phases(args, cfg):
         runs.append(buf.cpu().numpy().astype(np.int64))
     m.moe_stack_set_phase_log(stack, None)
     t = np.stack(runs)[:, 1:]              # tokens, layers 1.., workgroups, phases
-    assert np.all(t > 0), "missing timestamps"
+    split = cfg.bits == 8                  # 8-bit shapes: waves 4..7 load the down items
+    need = [p for p in range(P) if split or p not in (15, 16)]
+    assert np.all(t[..., need] > 0), "missing timestamps"
     us = 0.01                              # 100 MHz wall clock
     d = np.diff(t[..., :10], axis=-1) * us  # phase p-1 -> p, p = 1..9
-    # inside "top-k done": wave 0's logits wait, its selection, then the wait
-    # for waves 1..7 (shared gate/up) at the barrier
-    sub = {"logits wait (wave 0)": (t[..., 10] - t[..., 3]) * us,
-           "top-k selection (wave 0)": (t[..., 11] - t[..., 10]) * us,
-           "barrier after top-k": (t[..., 4] - t[..., 11]) * us}
+
+    def since(p, q):
+        return (t[..., p] - t[..., q]) * us
+    # inside a phase: when single waves reach points of their own work,
+    # counted from the start of that phase
+    sub = {3: {"logits wait (wave 0)": since(10, 3),
+               "top-k selection (wave 0)": since(11, 10),
+               "wave 0 at the barrier (weights written)": since(14, 3),
+               "wave 1 at the barrier (shared gate/up published)": since(13, 3),
+               "wave 4 at the barrier (shared down requested)": since(12, 3)},
+           5: {"wave 0 has polled the shared h": since(17, 5)},
+           6: {"wave 0 has polled the routed h": since(18, 6)},
+           7: {"routed chunk sums": since(19, 7), "down items": since(8, 19)}}
+    if split:
+        sub[5].update({"wave 4 routed down items requested": since(15, 5),
+                       "wave 4 down items landed": since(16, 5)})
     period = (t[:, 1:, :, 0] - t[:, :-1, :, 0]) * us
     spread = (t[:, :, :, 9].max(axis=2) - t[:, :, :, 9].min(axis=2)) * us
     rows = []
@@ -368,10 +381,9 @@ def bench_phases(args, cfg):
         v = d[..., p].ravel()
         rows.append({"phase": PHASE_NAMES[p], "median_us": float(np.median(v)),
                      "p90_us": float(np.percentile(v, 90))})
-        if p == 3:
-            for name, sv in sub.items():
-                rows.append({"phase": "  " + name, "median_us": float(np.median(sv)),
-                             "p90_us": float(np.percentile(sv, 90))})
+        for name, sv in sub.get(p, {}).items():
+            rows.append({"phase": "  " + name, "median_us": float(np.median(sv)),
+                         "p90_us": float(np.percentile(sv, 90))})
     out = {"phases": rows, "workload": cfg.name, "tokens": n,
            "layer_period_median_us": float(np.median(period)),
            "layer_period_p90_us": float(np.percentile(period, 90)),

@@ -437,12 +437,16 @@ int32_t moe_stack_advance_epoch(moe_stack* stack, uint32_t n);
 int32_t moe_stack_set_timeout(moe_stack* stack, int64_t microseconds);
 /* Profiling hook of a library built with -DMOE_STACK_PHASES (the
  * libmoe_phases.so variant; MOE_E_INVAL otherwise): phases, device uint64
- * [L][256][12] or NULL, receives per layer and workgroup the wall-clock
- * ticks (100 MHz) at twelve points of every persistent launch: layer start,
- * previous output received, input staged, router row published, top-k done
- * (all waves), routed gate/up done, shared h received, routed h received,
- * down rows done, output published, then (wave 0 alone) every logit
- * received and the top-k selected.  Each launch overwrites it. */
+ * [L][256][20] or NULL, receives per layer and workgroup the wall-clock
+ * ticks (100 MHz) at twenty points of every persistent launch: 0-9 layer
+ * start, previous output received, input staged, router row published,
+ * top-k done (all waves), routed gate/up done, shared h received, routed h
+ * received, down rows done, output published; then single waves at points
+ * of their own work: 10-11 wave 0 every logit received, top-k selected;
+ * 12-14 waves 4, 1 and 0 at the barrier that ends the top-k; 15-16 wave 4
+ * routed down items requested, its down items landed (8-bit shapes only);
+ * 17-18 wave 0 shared h polled, routed h polled; 19 routed chunk sums done.
+ * Each launch overwrites it. */
 int32_t moe_stack_set_phase_log(moe_stack* stack, uint64_t* phases);
 int32_t moe_stack_destroy(moe_stack* stack);
 

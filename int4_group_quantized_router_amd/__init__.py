@@ -391,7 +391,7 @@ def moe_stack_set_timeout(stack, microseconds: int) -> None:
 
 
 def moe_stack_set_phase_log(stack, phases) -> None:
-    """Profiling builds only: phases = device int64 tensor [L, 256, 10] or None."""
+    """Profiling builds only: phases = device int64 tensor [L, 256, 20] or None."""
     _check(_lib_().moe_stack_set_phase_log(_h(stack), _dptr(phases)), "moe_stack_set_phase_log")
 
 

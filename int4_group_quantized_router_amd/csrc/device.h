@@ -299,14 +299,17 @@ __device__ void select_k(const float* v, const uint32_t* key, int k, IdxOf idx_o
 // asc).  Results: sel_e[j], sel_v[j] for j < k (LDS).  tmp_e / tmp_v / tmp_k:
 // the wave's own LDS scratch of >= 64 entries each.  All lanes must call it.
 //
-// With several keys per lane the search runs on a pruned set: the k-th
-// largest of the 64 per-lane maxima, t1, is found first (one key per lane);
-// at least k lanes hold a key >= t1, so every one of the k best keys is
-// >= t1.  The keys >= t1 -- usually few more than k -- are compacted one
-// per lane in (i, lane) order, which is increasing expert index, and the
-// selection runs on them.  If more than 64 keys are >= t1 (many ties), the
-// selection runs on all keys instead.  Either way the result is the unique
-// top-k by (key desc, index asc).
+// With several keys per lane the selection runs on a pruned set: the k-th
+// largest of the 64 per-lane maxima, t1, is found first (one key per lane,
+// bitwise search); at least k lanes hold a key >= t1, so every one of the k
+// best keys is >= t1.  The keys >= t1 -- usually few more than k -- are
+// compacted one per lane with their expert index, and each one's place is
+// its rank among them: the number of candidates whose (key, -index) is
+// larger, counted by broadcasting each candidate in turn (one 64-bit
+// comparison per candidate).  Ranks are distinct, so the lanes of rank < k
+// write the result in order.  If more than 64 keys are >= t1 (many ties),
+// the bitwise selection runs on all keys instead.  Either way the result is
+// the unique top-k by (key desc, index asc).
 template <int VPL>
 __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e, float* tmp_v,
                           uint32_t* tmp_k, int* sel_e, float* sel_v) {
@@ -330,32 +333,61 @@ __device__ void wave_topk(const float* v, const uint32_t* key, int k, int* tmp_e
       if (cnt == ku) break;
     }
   }
-  const uint64_t below = lanes_below();
-  int n = 0;
+  // candidates: keys >= t1 (t1 > 0 whenever any lane holds a valid key; the
+  // floor of 1 keeps invalid entries out).  Their masks first (the total
+  // decides the path), then the writes.
+  const uint32_t tlo = t1 > 0u ? t1 : 1u;
+  uint64_t cm[VPL];
+  uint32_t n = 0;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const bool c = key[i] >= t1 && key[i] != 0u;
-    const uint64_t bm = __ballot(c);
-    const int pos = n + __popcll(bm & below);
-    if (c && pos < 64) {
-      tmp_k[pos] = key[i];
-      tmp_v[pos] = v[i];
-      tmp_e[pos] = lane + 64 * i;
-    }
-    n += __popcll(bm);
+    cm[i] = __ballot(key[i] >= tlo);
+    n += count_lanes(cm[i]);
   }
-  if (n > 64 || n < k) {  // wave-uniform
+  n = (uint32_t)__builtin_amdgcn_readfirstlane(n);
+  if (n > 64u || n < ku) {  // wave-uniform
     select_k<VPL>(v, key, k, natural, tmp_e, tmp_v, sel_e, sel_v);
     return;
   }
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    if (key[i] >= tlo) {
+      const uint32_t pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(cm[i] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)cm[i], 0u));
+      tmp_k[pos] = key[i];
+      tmp_e[pos] = lane + 64 * i;
+    }
+    base += count_lanes(cm[i]);
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const float cv = lane < n ? tmp_v[lane] : 0.f;
-  const uint32_t ck = lane < n ? tmp_k[lane] : 0u;
-  const int ce = lane < n ? tmp_e[lane] : 0;
+  const bool have = (uint32_t)lane < n;
+  const uint32_t ck = have ? tmp_k[lane] : 0u;
+  const int ce = have ? tmp_e[lane] : 0;
+  // the value back from its key (the inverse of order_key)
+  const float cv = __uint_as_float((ck & 0x80000000u) ? (ck & 0x7FFFFFFFu) : ~ck);
+  // (key, -index) as one 64-bit order: a larger key, then a lower index, wins
+  const uint32_t nce = ~(uint32_t)ce;
+  const uint64_t mine = ((uint64_t)ck << 32) | nce;
+  uint32_t r = 0;
+  // lanes >= n hold key 0, below every candidate: looping over them in
+  // steps of 4 adds nothing to a candidate's rank
+  const uint32_t n4 = (n + 3u) & ~3u;
+  for (uint32_t m = 0; m < n4; m += 4) {
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)ck, (int)(m + u));
+      const uint32_t em = (uint32_t)__builtin_amdgcn_readlane((int)nce, (int)(m + u));
+      r += (((uint64_t)km << 32) | em) > mine ? 1u : 0u;
+    }
+  }
+  if (have && r < ku) {
+    sel_e[r] = ce;
+    sel_v[r] = cv;
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  select_k<1>(&cv, &ck, k, [&](int, int) { return ce; }, tmp_e, tmp_v, sel_e, sel_v);
 }
 
 }  // namespace dev

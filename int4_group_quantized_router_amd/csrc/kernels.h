@@ -154,7 +154,7 @@ constexpr int kStackThreads = 512;
 constexpr int kStackGrid = 256;       // workgroups: one per compute unit of MI355X
 constexpr int kStackReplicas = 8;     // copies of every hand-off word (one per XCD)
 constexpr int kStackMaxLayers = 64;   // layer descriptors kept in LDS
-constexpr int kStackPhases = 12;      // phase timestamps per layer and workgroup (profiling)
+constexpr int kStackPhases = 20;      // phase timestamps per layer and workgroup (profiling)
 
 struct StackLayerDesc {
   const float* Wr;              // f32 [E, H]

@@ -56,17 +56,20 @@ using namespace dev;
 // Phase timestamps (profiling builds only, -DMOE_STACK_PHASES): thread 0 of
 // every workgroup records the wall clock (100 MHz) at the phase boundaries
 // of each layer into a.phases[(l * grid + block) * kStackPhases + p].
+// STACK_PHASE_AT records the same clock from thread T (lane 0 of another
+// wave) at points of that wave's own work.
 #ifdef MOE_STACK_PHASES
-#define STACK_PHASE(P)                                                          \
+#define STACK_PHASE_AT(P, T)                                                    \
   do {                                                                          \
-    if (threadIdx.x == 0 && a.phases)                                           \
+    if (threadIdx.x == (T) && a.phases)                                         \
       a.phases[((size_t)l * kG + blk) * kStackPhases + (P)] = wall_clock64();   \
   } while (0)
 #else
-#define STACK_PHASE(P) \
-  do {                 \
+#define STACK_PHASE_AT(P, T) \
+  do {                       \
   } while (0)
 #endif
+#define STACK_PHASE(P) STACK_PHASE_AT(P, 0)
 
 constexpr int kNT = kStackThreads;
 constexpr int kNW = kNT / kWave;
@@ -540,6 +543,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
       }
       if (lane == 0) s_abort = timed_out ? 1 : 0;
+      STACK_PHASE(14);  // wave 0: weights written, at the barrier
     } else {
       uint4 gq[S::NPS][2][CPL];
       uint32_t gsb[S::NPS][2][CPL];
@@ -573,6 +577,8 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           if (it < S::NITEMS) down_request(it, D.shared_blob, true);
         }
       }
+      STACK_PHASE_AT(12, 4 * kWave);  // wave 4: shared work issued, at the barrier
+      STACK_PHASE_AT(13, kWave);      // wave 1: the same
     }
     __syncthreads();
     STACK_PHASE(4);  // top-k done (and the shared gate/up)
@@ -636,7 +642,9 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           const int it = (wave - 4) + 4 * n;
           if (it < K * S::NIR) routed_item(it);
         }
+        STACK_PHASE_AT(15, 4 * kWave);  // wave 4: routed down items requested
         wait_vm_n<0>();
+        STACK_PHASE_AT(16, 4 * kWave);  // wave 4: its down items landed
       }
     } else {
 #pragma unroll
@@ -699,6 +707,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         l_fail = l;
       break;
     }
+    STACK_PHASE(17);  // wave 0: shared h polled, at the barrier
     __syncthreads();
     STACK_PHASE(6);  // shared h received
     wait_vm_n<0>();  // this wave's down-item loads have landed
@@ -712,10 +721,12 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         l_fail = l;
       break;
     }
+    STACK_PHASE(18);  // wave 0: routed h polled, at the barrier
     __syncthreads();
     STACK_PHASE(7);  // routed h received
     chunk_sums(0, K * I / F::kEpc);
     __syncthreads();
+    STACK_PHASE(19);  // routed chunk sums done
     down_items(false);
     __syncthreads();
     STACK_PHASE(8);  // down rows done
@@ -762,6 +773,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     if (failed) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     st_dev(a.epochs + blk, epoch + 1u);
   }
+  wait_vm_n<0>();  // no direct-to-LDS load outlives the workgroup's LDS
 }
 
 // Zero-fill of n 32-bit words (hand-off buffers whose tags could alias).

@@ -181,6 +181,33 @@ def test_route_edge_cases(torch):
     m.moe_route_topk(x0[:0], dWr, None, 2)
 
 
+@pytest.mark.parametrize("E,k,group", [(256, 8, 2), (512, 10, 2), (512, 10, 3), (1024, 16, 4)])
+@pytest.mark.parametrize("T", [1, 8, 300])
+def test_route_exact_ties(torch, E, k, group, T):
+    """Router rows repeated in groups of `group` (equal rows, equal bias):
+    every logit occurs `group` times exactly, so the best logits tie with
+    each other and the k-th place falls inside a tie.  The GPU's choice must
+    be the oracle's selection rule on the GPU's own logits -- (logit desc,
+    index asc) -- on every token."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS["stream80b"].replace(experts=E, top_k=k)
+    _print("route ties", E, k, group, T)
+    Wr, rb, _ = router_arrays(cfg, 0)
+    Wr = np.repeat(Wr[: (E + group - 1) // group], group, axis=0)[:E].copy()
+    rb = np.repeat(rb[: (E + group - 1) // group], group)[:E].copy()
+    xb = tokens_x(cfg, 0, T)
+    out = m.moe_route_topk(torch.from_numpy(xb.view(np.int16)).cuda(), torch.from_numpy(Wr).cuda(),
+                           torch.from_numpy(rb).cuda(), k)
+    torch.cuda.synchronize()
+    idx, lg = out["idx"].cpu().numpy(), out["logits"].cpu().numpy()
+    ties = 0
+    for t in range(T):
+        want = O.select_topk(lg[t].astype(np.float64), k)
+        assert np.array_equal(idx[t], want), (t, idx[t], want)
+        ties += int(np.sum(lg[t] == lg[t][want[-1]]) > 1)
+    assert ties == T  # the k-th logit is tied on every token
+
+
 # ------------------------------------------------------------ single expert
 
 @pytest.mark.parametrize("name,H,I,T", [("tiny", 256, 64, 3), ("decode35b", 2048, 512, 1),
