@@ -71,6 +71,14 @@ using namespace dev;
 #endif
 #define STACK_PHASE(P) STACK_PHASE_AT(P, 0)
 
+// A pointer every lane holds the same value of, kept in scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+
 constexpr int kNT = kStackThreads;
 constexpr int kNW = kNT / kWave;
 constexpr int kG = kStackGrid;
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         if (pr < K * S::PR) {
           const int j = pr / S::PR;
           const uint8_t* blob =
-              POOL ? s_addr[j]
+              POOL ? uniform_ptr(s_addr[j])
                         : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
           gu_load(blob, a.lq, a.lsb, (pr % S::PR) * RPP + rsub, gq[n % DEPTH], gsb[n % DEPTH]);
         }
@@ -631,7 +639,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     auto routed_item = [&](int it) {
       const int j = it / S::NIR;
       const uint8_t* blob =
-          POOL ? s_addr[j]
+          POOL ? uniform_ptr(s_addr[j])
                : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
       down_request(it, blob, false);
     };
@@ -682,7 +690,10 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
           const int s = is_shared ? K : it / S::NIR;
           const int pp = is_shared ? it - K * S::NIR : it % S::NIR;
           const int C = is_shared ? S::CS : S::CR, RP = is_shared ? S::RPPS : S::RPPR;
-          const int ci = lane % C, rloc = pp * RP + lane / C;
+          int ci = lane % C, rloc = pp * RP + lane / C;
+          // recomputed per layer, not held across the layer loop: the
+          // registers are scarcer than the two integer operations
+          asm volatile("" : "+v"(ci), "+v"(rloc));
           const int chunk = s * (I / F::kEpc) + ci;  // chunk index in the dense h
           const uint4* hsrc = reinterpret_cast<const uint4*>(hl + (size_t)chunk * F::kPairs);
           uint32_t hp[F::kPairs];
