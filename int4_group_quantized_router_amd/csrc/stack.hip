@@ -644,12 +644,19 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       down_request(it, blob, false);
     };
     if constexpr (RO::SPLIT) {
+      static_assert(S::NIR % 4 == 0, "split down phase: items of an expert in fours");
       if (wave >= 4) {
+        // wave 4 + w takes the items it = j * NIR + w + 4 m of every choice
+        // j; the chosen blobs are read once (LDS, then scalar registers)
+        const uint8_t* blobs[K];
 #pragma unroll
-        for (int n = 0; n < (K * S::NIR + 3) / 4; ++n) {
-          const int it = (wave - 4) + 4 * n;
-          if (it < K * S::NIR) routed_item(it);
-        }
+        for (int j = 0; j < K; ++j)
+          blobs[j] = POOL ? uniform_ptr(s_addr[j])
+                          : D.routed_base + (int64_t)__builtin_amdgcn_readfirstlane(s_sel[j]) * a.stride;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+          for (int m = 0; m < S::NIR / 4; ++m) down_request(j * S::NIR + (wave - 4) + 4 * m, blobs[j], false);
         STACK_PHASE_AT(15, 4 * kWave);  // wave 4: routed down items requested
         wait_vm_n<0>();
         STACK_PHASE_AT(16, 4 * kWave);  // wave 4: its down items landed
