@@ -58,7 +58,7 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
-    "decode80b_int8": ("stack", 976098, 79900, "b37f8cb72b9a6097"),
+    "decode80b_int8": ("stack", 976376, 79900, "1899706188163318"),
 }
 # bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
 # algorithmic bytes are streamed once per phase with 3 dependent all-to-all

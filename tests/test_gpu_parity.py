@@ -571,6 +571,49 @@ def test_stack_persistent_matches_per_layer(torch, name, L):
         dm.destroy()
 
 
+@pytest.mark.parametrize("name", ["decode80b_int8", "decode35b"])
+def test_stack_exact_ties_persistent_matches_per_layer(torch, name):
+    """Routers whose rows come in equal triples (every logit occurs three
+    times, and with k = 8 or 10 the k-th place splits a triple, so the tie
+    rule decides which of equal experts are chosen): the persistent
+    kernel's top-k instance picks exactly what the per-layer router picks
+    (whose ties are checked against the oracle's rule elsewhere), and every
+    export agrees bit for bit."""
+    import int4_group_quantized_router_amd as m
+    cfg = CONFIGS[name].replace(layers=3)
+    _print("stack ties persistent vs per-layer", name)
+    dm = DeviceModel(cfg)
+    E = cfg.experts
+    for l in range(cfg.layers):
+        Wr, rb, _ = router_arrays(cfg, l)
+        dm.Wr[l] = torch.from_numpy(np.repeat(Wr[: (E + 2) // 3], 3, axis=0)[:E].copy()).cuda()
+        dm.rb[l] = torch.from_numpy(np.repeat(rb[: (E + 2) // 3], 3)[:E].copy()).cuda()
+    st = m.moe_stack_create(dm.make_layers())
+    try:
+        assert m.moe_stack_persistent_active(st)
+        for tok in range(4):
+            outs = []
+            for persistent in (True, False):
+                m.moe_stack_set_persistent(st, persistent)
+                outs.append(_stack_outputs(torch, m, st, cfg, tok))
+            for got, want in zip(*outs):
+                assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (name, tok)
+            idx = outs[0][3].reshape(cfg.layers, cfg.top_k)
+            for r in idx:
+                # whole triples, then the lowest indices of the triple the
+                # k-th place splits
+                groups = {}
+                for e in r.tolist():
+                    groups.setdefault(e // 3, []).append(e)
+                partial = [g for g in groups.values() if len(g) < min(3, E - 3 * (g[0] // 3))]
+                assert len(partial) <= 1
+                for g in partial:
+                    assert sorted(g) == list(range(3 * (g[0] // 3), 3 * (g[0] // 3) + len(g)))
+    finally:
+        m.moe_stack_destroy(st)
+        dm.destroy()
+
+
 # --------------------------------------------------------------------- pool
 
 def test_pool_matches_resident_bitwise_and_replay(torch):
