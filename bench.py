@@ -59,6 +59,8 @@ TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
     "decode80b_int8": ("stack", 976376, 79900, "1899706188163318"),
+    # profiles/prefill80b_grouped_gemm.md
+    "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
 }
 # bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
 # algorithmic bytes are streamed once per phase with 3 dependent all-to-all
