@@ -475,6 +475,30 @@ int32_t moe_timer_read(moe_timer* timer, float* ms, int32_t* n);
 int32_t moe_timer_destroy(moe_timer* timer);
 
 /* ------------------------------------------------------------------------
+ * Gated DeltaNet recurrent decode step.  Three of every four layers of the
+ * hybrid stack are Gated DeltaNet linear attention with a fixed-size
+ * recurrent state ([xix] paragraph on Metal and DeltaNet; [lens]
+ * "エキスパートストリーミングの仕組み"); the pages print no recurrence, and
+ * this is the published gated delta rule.  For every sequence b < B and
+ * value head h < Hv, with key / query head g = h / (Hv / Hk):
+ *   k^ = k / sqrt(|k|^2 + eps), q^ = q / sqrt(|q|^2 + eps),
+ *   S  <- alpha (S - beta (S k^) k^T) + beta v k^T,   o = scale S q^,
+ * in f32 (the new state is used for o).
+ *   q, k   bf16 bits [B][Hk][dk]        v      bf16 bits [B][Hv][dv]
+ *   alpha, beta  f32 [B][Hv] (decay in (0, 1], write strength in [0, 1];
+ *                the model's gate activations, computed by the caller)
+ *   state  f32 [B][Hv][dv][dk], read and overwritten in place
+ *   out    f32 [B][Hv][dv]
+ * All device pointers, 16-byte aligned, caller-owned; work is enqueued on
+ * `stream`.  (dk, dv) = (128, 128) or (64, 64).  B = 0 is a no-op.
+ * MOE_E_INVAL: bad sizes, Hv not a multiple of Hk, eps < 0, null pointers.
+ * ---------------------------------------------------------------------- */
+int32_t moe_gdn_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const float* alpha, const float* beta, float* state, float* out,
+                     int32_t B, int32_t Hk, int32_t Hv, int32_t dk, int32_t dv, float scale,
+                     float eps, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Calibration hook: the ceiling of a batch-1 decode layer on this device.
  * On the persistent stack kernel's grid (256 workgroups, all resident),
  * `phases` times: read `bytes` of fresh memory (phase p reads buf + p*bytes,

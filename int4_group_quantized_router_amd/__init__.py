@@ -401,6 +401,26 @@ def moe_stack_destroy(stack) -> None:
 
 # ------------------------------------------------------------- calibration
 
+def moe_gdn_step(q, k, v, alpha, beta, state, out=None, scale=None, eps=1e-6, stream=None):
+    """One Gated DeltaNet decode step (see include/moe.h): q, k bf16 [B, Hk, dk],
+    v bf16 [B, Hv, dv], alpha / beta f32 [B, Hv], state f32 [B, Hv, dv, dk]
+    (updated in place); returns out f32 [B, Hv, dv].  scale defaults to
+    dk ** -0.5."""
+    import torch
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if out is None:
+        out = torch.empty((B, Hv, dv), dtype=torch.float32, device=state.device)
+    scale = dk ** -0.5 if scale is None else scale
+    _check(_lib_().moe_gdn_step(_dptr(q, _bf16_types(), "q"), _dptr(k, _bf16_types(), "k"),
+                                _dptr(v, _bf16_types(), "v"), _dptr(alpha, (torch.float32,), "alpha"),
+                                _dptr(beta, (torch.float32,), "beta"),
+                                _dptr(state, (torch.float32,), "state"),
+                                _dptr(out, (torch.float32,), "out"), B, Hk, Hv, dk, dv,
+                                float(scale), float(eps), _stream(stream)), "moe_gdn_step")
+    return out
+
+
 def moe_calibrate_stream(buf, bytes_per_phase: int, phases: int, handoffs: int, reps: int = 5,
                          stream=None) -> float:
     """Mean ms per launch of the streaming calibration kernel (see moe.h)."""

@@ -103,6 +103,8 @@ SIGNATURES = {
     "moe_stack_set_phase_log": [_P, _P],
     "moe_stack_destroy": [_P],
     "moe_calibrate_stream": [_P, _I64, _I32, _I32, _I32, C.POINTER(C.c_float), _P],
+    "moe_gdn_step": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, C.c_float,
+                     C.c_float, _P],
     "moe_timer_create": [_I32, _I32, C.POINTER(_P)],
     "moe_timer_attach": [_P],
     "moe_timer_read": [_P, _P, C.POINTER(_I32)],

@@ -7,10 +7,11 @@ here.  Random ``uint32`` words stand for packed quantised values directly,
 because i.i.d. uniform words are exactly i.i.d. uniform 4- or 8-bit fields.
 """
 
-from .configs import CONFIGS, MoEConfig, get_config  # noqa: F401
+from .configs import CONFIGS, GDN_CONFIGS, MoEConfig, get_config  # noqa: F401
 from .generate import (  # noqa: F401
     bf16_bits_from_f32,
     expert_arrays,
+    gdn_inputs,
     router_arrays,
     shared_arrays,
     token_x,

@@ -94,3 +94,12 @@ CONFIGS = {
 
 def get_config(name: str) -> MoEConfig:
     return CONFIGS[name]
+
+
+# Gated DeltaNet recurrent decode step shapes (value heads Hv, key heads Hk,
+# head dims dk = dv): the 80B-A3B model's linear-attention layers, and a
+# small one for tests.  B = sequences decoded together.
+GDN_CONFIGS = {
+    "gdn_tiny": {"B": 3, "Hk": 2, "Hv": 4, "dk": 64, "dv": 64},
+    "gdn80b": {"B": 64, "Hk": 16, "Hv": 32, "dk": 128, "dv": 128},
+}

@@ -93,3 +93,21 @@ def token_x(cfg: MoEConfig, t: int) -> np.ndarray:
 def tokens_x(cfg: MoEConfig, t0: int, n: int) -> np.ndarray:
     return np.stack([token_x(cfg, t) for t in range(t0, t0 + n)]) if n else \
         np.zeros((0, cfg.hidden), dtype=np.uint16)
+
+
+def gdn_inputs(seed: int, B: int, Hk: int, Hv: int, dk: int, dv: int, T: int) -> dict:
+    """Seeded inputs of T consecutive Gated DeltaNet decode steps for B
+    sequences: q, k [T][B][Hk][dk] and v [T][B][Hv][dv] as bf16 bits of
+    N(0, 1) draws; decay alpha [T][B][Hv] ~ U(0.9, 1) and write strength
+    beta ~ U(0, 1) as f32; an initial state S0 [B][Hv][dv][dk] ~ N(0, 0.1^2)
+    as f32."""
+    rng = np.random.default_rng((seed, 6, B, Hk, Hv, dk, dv, T))
+    f32 = np.float32
+    return {
+        "q": bf16_bits_from_f32(rng.standard_normal((T, B, Hk, dk)).astype(f32)),
+        "k": bf16_bits_from_f32(rng.standard_normal((T, B, Hk, dk)).astype(f32)),
+        "v": bf16_bits_from_f32(rng.standard_normal((T, B, Hv, dv)).astype(f32)),
+        "alpha": rng.uniform(0.9, 1.0, (T, B, Hv)).astype(f32),
+        "beta": rng.uniform(0.0, 1.0, (T, B, Hv)).astype(f32),
+        "S0": (0.1 * rng.standard_normal((B, Hv, dv, dk))).astype(f32),
+    }

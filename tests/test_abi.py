@@ -112,6 +112,15 @@ def test_argument_errors_without_gpu():
     # a layer call needs a layer, even for an empty batch
     st = lib.moe_layer_forward(None, None, 0, None, None, None, None, None)
     assert st == _lib.MOE_E_INVAL and b"null" in lib.moe_last_error()
+    # Gated DeltaNet step: head dims, head grouping, eps; an empty batch is a no-op
+    gdn = lib.moe_gdn_step
+    assert gdn(1, 1, 1, 1, 1, 1, 1, 2, 2, 4, 96, 96, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
+    assert gdn(1, 1, 1, 1, 1, 1, 1, 2, 3, 4, 128, 128, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
+    assert b"multiple" in lib.moe_last_error()
+    assert gdn(1, 1, 1, 1, 1, 1, 1, 2, 2, 4, 128, 128, 1.0, -1.0, None) == _lib.MOE_E_INVAL
+    assert gdn(None, 1, 1, 1, 1, 1, 1, 2, 2, 4, 64, 64, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
+    assert gdn(None, None, None, None, None, None, None, 0, 2, 4, 64, 64, 1.0, 1e-6,
+               None) == _lib.MOE_OK
 
 
 def test_file_store_round_trip_without_gpu(tmp_path):

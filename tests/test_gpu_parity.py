@@ -8,7 +8,9 @@ import ctypes
 import numpy as np
 import pytest
 
-from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, token_x, tokens_x
+from moe_inputs import (CONFIGS, GDN_CONFIGS, expert_arrays, gdn_inputs, router_arrays,
+                        shared_arrays, token_x, tokens_x)
+from oracle import gdn_oracle as G
 from oracle import moe_oracle as O
 
 from harness import (REL_TOL, DeviceModel, check_bf16_of_f32, check_routing, mfma_depth,
@@ -1243,3 +1245,75 @@ def test_decode_and_prefill_agree(torch):
                     assert rel_err(y_d[i], y_p[t0 + i]) <= 1e-2
     finally:
         dm.destroy()
+
+
+# ---------------------------------------------------------- Gated DeltaNet
+
+# Each step's f32 arithmetic: dot products of dk terms (|k|^2, |q|^2, S k^,
+# S q^) and two roundings per state element.  Relative to the max-norm of
+# the oracle's value, gamma_(dk + 4) ~ 8e-6 for dk = 128 bounds one step;
+# the free-running state adds one such bound per step (alpha <= 1 keeps
+# older errors from growing).
+GDN_STEP_TOL = 2e-5
+
+
+def _gdn_run(torch, m, name, B, T, seed=0):
+    c = dict(GDN_CONFIGS[name], B=B)
+    d = gdn_inputs(seed, c["B"], c["Hk"], c["Hv"], c["dk"], c["dv"], T)
+    return c, d
+
+
+@pytest.mark.parametrize("name,B,T", [("gdn_tiny", 3, 24), ("gdn80b", 2, 16), ("gdn80b", 64, 4)])
+def test_gdn_step_matches_oracle(torch, name, B, T):
+    """T consecutive decode steps on the GPU against the float64 oracle:
+    each step from the GPU's own previous state (teacher-forced, within one
+    step's f32 bound) and the whole run from the initial state (within T
+    bounds)."""
+    import int4_group_quantized_router_amd as m
+    c, d = _gdn_run(torch, m, name, B, T)
+    _print("gdn", name, B, T)
+    scale = c["dk"] ** -0.5
+    S = torch.from_numpy(d["S0"].copy()).cuda()
+    S_free = d["S0"].astype(np.float64)
+    for t in range(T):
+        S_prev = S.cpu().numpy().astype(np.float64)
+        q, k, v = (torch.from_numpy(d[x][t].view(np.int16)).cuda() for x in ("q", "k", "v"))
+        al, be = (torch.from_numpy(d[x][t]).cuda() for x in ("alpha", "beta"))
+        o = m.moe_gdn_step(q, k, v, al, be, S, scale=scale, eps=1e-6)
+        torch.cuda.synchronize()
+        S_ref, o_ref = G.gdn_step_bf16(S_prev, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t],
+                                       d["beta"][t], scale, 1e-6)
+        assert rel_err(S.cpu().numpy(), S_ref) <= GDN_STEP_TOL, t
+        assert rel_err(o.cpu().numpy(), o_ref) <= GDN_STEP_TOL, t
+        S_free, _ = G.gdn_step_bf16(S_free, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t],
+                                    d["beta"][t], scale, 1e-6)
+    assert rel_err(S.cpu().numpy(), S_free) <= T * GDN_STEP_TOL
+
+
+def test_gdn_step_exact_cases(torch):
+    """beta = 0, and a zero key with eps > 0, write nothing: the new state is
+    exactly f32(alpha * S) (one rounding, as the kernel forms it), and the
+    output reads it; rejected shapes leave the state untouched."""
+    import int4_group_quantized_router_amd as m
+    c, d = _gdn_run(torch, m, "gdn80b", 2, 1, seed=3)
+    S0 = d["S0"]
+    q, k, v = (torch.from_numpy(d[x][0].view(np.int16)).cuda() for x in ("q", "k", "v"))
+    al = torch.from_numpy(d["alpha"][0]).cuda()
+    for case in ("beta0", "zero_key"):
+        S = torch.from_numpy(S0.copy()).cuda()
+        be = torch.from_numpy(np.zeros_like(d["beta"][0]) if case == "beta0" else d["beta"][0]).cuda()
+        kk = torch.zeros_like(k) if case == "zero_key" else k
+        o = m.moe_gdn_step(q, kk, v, al, be, S, scale=1.0, eps=1e-6)
+        torch.cuda.synchronize()
+        want = (d["alpha"][0][:, :, None, None] * S0).astype(np.float32)
+        assert np.array_equal(S.cpu().numpy(), want), case
+        _, o_ref = G.gdn_step_bf16(want.astype(np.float64), d["q"][0], np.zeros_like(d["k"][0]),
+                                   d["v"][0], np.ones_like(d["alpha"][0]),
+                                   np.zeros_like(d["beta"][0]), 1.0, 1e-6)
+        assert rel_err(o.cpu().numpy(), o_ref) <= GDN_STEP_TOL
+    S = torch.from_numpy(S0.copy()).cuda()
+    v3, a3 = v[:, :3].contiguous(), al[:, :3].contiguous()
+    with pytest.raises(m.MoEError):
+        m.moe_gdn_step(q, k, v3, a3, a3, S)  # 3 value heads over 16 key heads
+    torch.cuda.synchronize()
+    assert np.array_equal(S.cpu().numpy(), S0)
