@@ -305,8 +305,10 @@ def main():
         return calibrate_peaks()
     if args.calibrate_stream:
         return calibrate_stream()
-    from moe_inputs import CONFIGS
+    from moe_inputs import CONFIGS, GDN_CONFIGS
 
+    if args.workload in GDN_CONFIGS:
+        return bench_gdn(args, args.workload, GDN_CONFIGS[args.workload])
     cfg = CONFIGS[args.workload]
     if args.layers:
         cfg = cfg.replace(layers=args.layers)
@@ -764,6 +766,92 @@ def bench_prefill(args, cfg):
     }
     print(json.dumps(out), flush=True)
     m.moe_layer_destroy(layer)
+
+
+
+
+def gdn_bytes(c):
+    """Algorithmic bytes of one Gated DeltaNet step: the f32 state read and
+    written, the bf16 q, k, v, f32 alpha and beta read, the f32 output."""
+    B, Hk, Hv, dk, dv = c["B"], c["Hk"], c["Hv"], c["dk"], c["dv"]
+    return B * (Hv * dv * dk * 4 * 2 + 2 * Hk * dk * 2 + Hv * dv * 2 + Hv * 8 + Hv * dv * 4)
+
+
+def bench_gdn(args, name, c):
+    """One step = one Gated DeltaNet recurrent decode step of one layer for
+    c["B"] sequences (every value head's state read and written once);
+    value = sequence-tokens per second through the layer."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from moe_inputs import gdn_inputs
+
+    steps = 200 if args.steps is None else args.steps
+    warmup = 10 if args.warmup is None else args.warmup
+    torch.cuda.set_device(0)
+    B, Hk, Hv, dk, dv = c["B"], c["Hk"], c["Hv"], c["dk"], c["dv"]
+    n_in = 8  # distinct token inputs, cycled
+    d = gdn_inputs(0, B, Hk, Hv, dk, dv, n_in)
+    dev = {x: torch.from_numpy(d[x].view(np.int16) if d[x].dtype == np.uint16 else d[x]).cuda()
+           for x in ("q", "k", "v", "alpha", "beta")}
+    S = torch.from_numpy(d["S0"]).cuda()
+    out = torch.empty((B, Hv, dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % n_in
+        m.moe_gdn_step(dev["q"][j], dev["k"][j], dev["v"][j], dev["alpha"][j], dev["beta"][j], S,
+                       out=out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    nbytes = gdn_bytes(c)
+    state_bytes = B * Hv * dv * dk * 8
+    achieved = nbytes / (launch_us * 1e-6) / 1e9
+    log(f"[bench] {name}: {steps} steps of B={B}, {launch_us:.2f} us per step "
+        f"({achieved:.0f} GB/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gdn_oracle as G
+        t1 = time.perf_counter()
+        n = 0
+        Sc = d["S0"].astype(np.float64)
+        while n == 0 or time.perf_counter() - t1 < 10.0:
+            j = n % n_in
+            Sc, _ = G.gdn_step_bf16(Sc, d["q"][j], d["k"][j], d["v"][j], d["alpha"][j],
+                                    d["beta"][j], dk ** -0.5, 1e-6)
+            n += 1
+        sec = (time.perf_counter() - t1) / n
+        cpu = {"value": B / sec, "unit": "sequence-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} steps of B={B} in {sec * n:.1f} s (NumPy float64, per-head loop)"}
+    line = {
+        "metric": "Gated DeltaNet decode step: sequence-tokens/s through one layer + state GB/s "
+                  "(% of HBM peak), 1 GPU",
+        "value": B * steps / dt, "unit": "sequence-tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": dt / steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 state, bf16 q/k/v",
+        "data": "synthetic (seeded)",
+        "config": {"workload": f"{name}: one Gated DeltaNet layer's recurrent step, {B} sequences, "
+                               f"{Hv} value heads over {Hk} key heads, dk = dv = {dk}",
+                   "state_bytes_per_step": state_bytes},
+        "roofline": {"kernel": f"gdn_step_kernel<{dk}, {dv}>", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": nbytes, "mean_launch_us": launch_us},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
