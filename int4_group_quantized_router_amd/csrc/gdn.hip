@@ -12,10 +12,10 @@
 //
 // At decode this is pure state traffic: the state is read and written once
 // (2 x dv x dk x 4 bytes per head) against ~6 dv dk flops, so the kernel is
-// bound by HBM bandwidth.  One workgroup per (sequence, head); TPR adjacent
-// lanes share a state row, each holding CPT consecutive columns in
-// registers, so every row of S is read and written with 16-byte accesses in
-// one pass:
+// bound by HBM bandwidth.  A head's rows are split over SPLIT workgroups
+// (ROWS each); TPR adjacent lanes share a state row, each holding CPT
+// consecutive columns in registers, so every row of S is read and written
+// with 16-byte accesses in one pass:
 //
 //   1. |k|^2, |q|^2 of this thread's columns, summed over the row's lanes
 //      (every row recomputes them; the key and query rows come from cache);
@@ -43,16 +43,18 @@ struct GdnArgs {
   float scale, eps;
 };
 
-template <int DK, int DV, int NT>
+template <int DK, int DV, int NT, int SPLIT>
 __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
-  constexpr int TPR = NT / DV;    // lanes per state row
-  constexpr int CPT = DK / TPR;   // columns per lane
-  static_assert(TPR * DV == NT && CPT * TPR == DK && CPT % 8 == 0, "state tiling");
+  constexpr int ROWS = DV / SPLIT;  // state rows per workgroup
+  constexpr int TPR = NT / ROWS;    // lanes per state row
+  constexpr int CPT = DK / TPR;     // columns per lane
+  static_assert(ROWS * SPLIT == DV && TPR * ROWS == NT && CPT * TPR == DK && CPT % 8 == 0,
+                "state tiling");
   static_assert(TPR == 2 || TPR == 4 || TPR == 8, "row lanes inside a quad or row half");
-  const int bh = blockIdx.x;      // b * Hv + h
+  const int bh = blockIdx.x / SPLIT;  // b * Hv + h
   const int b = bh / a.Hv, h = bh % a.Hv;
   const int g = h / (a.Hv / a.Hk);
-  const int t = threadIdx.x, r = t / TPR, c0 = (t % TPR) * CPT;
+  const int t = threadIdx.x, r = (blockIdx.x % SPLIT) * ROWS + t / TPR, c0 = (t % TPR) * CPT;
 
   // key and query of this lane's columns (16-byte loads of 8 bf16 each)
   const uint16_t* kp = a.k + ((size_t)b * a.Hk + g) * DK + c0;
@@ -119,9 +121,10 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   if (t % TPR == 0) a.out[(size_t)bh * DV + r] = a.scale * o;
 }
 
-template <int DK, int DV, int NT>
+template <int DK, int DV, int NT, int SPLIT>
 hipError_t launch_gdn(const GdnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((gdn_step_kernel<DK, DV, NT>), dim3((unsigned)(B * a.Hv)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((gdn_step_kernel<DK, DV, NT, SPLIT>), dim3((unsigned)(B * a.Hv * SPLIT)),
+                     dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -144,8 +147,8 @@ extern "C" int32_t moe_gdn_step(const uint16_t* q, const uint16_t* k, const uint
   if (B == 0) return MOE_OK;
   MOE_REQUIRE(q && k && v && alpha && beta && state && out, "null argument");
   GdnArgs a{q, k, v, alpha, beta, state, out, Hk, Hv, scale, eps};
-  hipError_t e = dk == 128 ? launch_gdn<128, 128, 512>(a, B, stream)
-                           : launch_gdn<64, 64, 256>(a, B, stream);
+  hipError_t e = dk == 128 ? launch_gdn<128, 128, 512, 2>(a, B, stream)
+                           : launch_gdn<64, 64, 256, 1>(a, B, stream);
   MOE_HIP_TRY(e);
   return MOE_OK;
 }
