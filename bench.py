@@ -54,6 +54,7 @@ COPY_WRITE_SCALE = 262144 / 262144
 KERNEL_SOURCES = {
     "stack": ("stack.hip", "gemv.h", "device.h", "kernels.h"),
     "prefill_gu": ("prefill.hip", "device.h", "kernels.h"),
+    "gdn": ("gdn.hip", "device.h", "kernels.h", "common.h"),
 }
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
@@ -61,6 +62,8 @@ TRAFFIC = {
     "decode80b_int8": ("stack", 976376, 79900, "1899706188163318"),
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
+    # profiles/gdn80b_step.md
+    "gdn80b": ("gdn", 66969, 132112, "093ab1a820bc01f7"),
 }
 # bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
 # algorithmic bytes are streamed once per phase with 3 dependent all-to-all
@@ -847,7 +850,7 @@ def bench_gdn(args, name, c):
                    "state_bytes_per_step": state_bytes},
         "roofline": {"kernel": f"gdn_step_kernel<{dk}, {dv}>", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": counter_traffic(name, "gdn"),
                      "bytes_per_launch": nbytes, "mean_launch_us": launch_us},
         "cpu_baseline": cpu,
     }
