@@ -60,6 +60,8 @@ TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
     "decode80b_int8": ("stack", 976376, 79900, "1899706188163318"),
+    # profiles/decode35b_stack_decode_kernel.md
+    "decode35b": ("stack", 362595, 53786, "1899706188163318"),
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
     # profiles/gdn80b_step.md
@@ -83,11 +85,12 @@ def kernel_digest(kind):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload, kind):
+def counter_traffic(workload, kind, stock=True):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, or None when no
-    reading was taken on the current sources."""
+    reading was taken on the current sources, or when the workload was
+    changed from its stock shape (``stock`` false: e.g. fewer layers)."""
     t = TRAFFIC.get(workload)
-    if not t or t[0] != kind or t[3] != kernel_digest(kind):
+    if not stock or not t or t[0] != kind or t[3] != kernel_digest(kind):
         return None
     return (t[1] * COPY_FETCH_SCALE + t[2] * COPY_WRITE_SCALE) * 1024
 
@@ -411,7 +414,7 @@ def bench_decode(args, cfg):
     import numpy as np
     import torch
     import int4_group_quantized_router_amd as m
-    from moe_inputs import tokens_x
+    from moe_inputs import CONFIGS, tokens_x
     args.steps = 256 if args.steps is None else args.steps
     args.warmup = 16 if args.warmup is None else args.warmup
     assert cfg.batch == 1 and cfg.resident, "decode bench workload must be resident batch-1"
@@ -470,7 +473,7 @@ def bench_decode(args, cfg):
                   f"top-k, dequant-GEMV gate/up + down, combine)")
         k_bytes = per_token_bytes
         k_quant = ab["expert_quantized"] * cfg.layers
-        traffic = counter_traffic(cfg.name, "stack")
+        traffic = counter_traffic(cfg.name, "stack", stock=cfg == CONFIGS[cfg.name])
     else:
         k_name = "gate_up_kernel (dequant-GEMV gate+up, fused SiLU*up)"
         k_bytes = ab["gate_up"]
@@ -701,7 +704,7 @@ def bench_prefill(args, cfg):
     import torch
     import int4_group_quantized_router_amd as m
     from int4_group_quantized_router_amd import weights as W
-    from moe_inputs import expert_arrays, router_arrays, shared_arrays, tokens_x
+    from moe_inputs import CONFIGS, expert_arrays, router_arrays, shared_arrays, tokens_x
 
     steps = 20 if args.steps is None else args.steps
     warmup = 3 if args.warmup is None else args.warmup
@@ -738,7 +741,8 @@ def bench_prefill(args, cfg):
     for t in timers.values():
         m.moe_timer_destroy(t)
     gu_flops, dn_flops = prefill_flops(cfg, T)
-    traffic = counter_traffic(cfg.name, "prefill_gu") if T == cfg.tokens else None
+    traffic = (counter_traffic(cfg.name, "prefill_gu", stock=cfg == CONFIGS[cfg.name])
+               if T == cfg.tokens else None)
     achieved = gu_flops / (ms["gate_up"] / 1e3) / 1e12
     both = (gu_flops + dn_flops) / ((ms["gate_up"] + ms["down"]) / 1e3) / 1e12
     tok_s = T * steps / t_all
