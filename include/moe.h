@@ -489,9 +489,10 @@ int32_t moe_timer_destroy(moe_timer* timer);
  *                the model's gate activations, computed by the caller)
  *   state  f32 [B][Hv][dv][dk], read and overwritten in place
  *   out    f32 [B][Hv][dv]
- * All device pointers, 16-byte aligned, caller-owned; work is enqueued on
- * `stream`.  (dk, dv) = (128, 128) or (64, 64).  B = 0 is a no-op.
- * MOE_E_INVAL: bad sizes, Hv not a multiple of Hk, eps < 0, null pointers.
+ * All device pointers, caller-owned, q, k and state 16-byte aligned; work
+ * is enqueued on `stream`.  (dk, dv) = (128, 128) or (64, 64).  B = 0 is a
+ * no-op.  MOE_E_INVAL: bad sizes, Hv not a multiple of Hk, eps < 0, null
+ * or misaligned pointers.
  * ---------------------------------------------------------------------- */
 int32_t moe_gdn_step(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const float* alpha, const float* beta, float* state, float* out,

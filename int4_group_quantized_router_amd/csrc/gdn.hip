@@ -143,9 +143,11 @@ extern "C" int32_t moe_gdn_step(const uint16_t* q, const uint16_t* k, const uint
   MOE_REQUIRE((dk == 128 && dv == 128) || (dk == 64 && dv == 64),
               "unsupported head dims dk=%d dv=%d (128x128 or 64x64)", dk, dv);
   MOE_REQUIRE(eps >= 0.f && scale == scale, "bad eps / scale");
-  MOE_REQUIRE((int64_t)B * Hv < (1ll << 31), "B * Hv too large");
+  MOE_REQUIRE((int64_t)B * Hv * 2 < (1ll << 31), "B * Hv too large");
   if (B == 0) return MOE_OK;
   MOE_REQUIRE(q && k && v && alpha && beta && state && out, "null argument");
+  MOE_REQUIRE((((uintptr_t)q | (uintptr_t)k | (uintptr_t)state) & 15) == 0,
+              "q, k and state must be 16-byte aligned");
   GdnArgs a{q, k, v, alpha, beta, state, out, Hk, Hv, scale, eps};
   hipError_t e = dk == 128 ? launch_gdn<128, 128, 512, 2>(a, B, stream)
                            : launch_gdn<64, 64, 256, 1>(a, B, stream);

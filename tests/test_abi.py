@@ -121,6 +121,12 @@ def test_argument_errors_without_gpu():
     assert gdn(None, 1, 1, 1, 1, 1, 1, 2, 2, 4, 64, 64, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
     assert gdn(None, None, None, None, None, None, None, 0, 2, 4, 64, 64, 1.0, 1e-6,
                None) == _lib.MOE_OK
+    if not os.path.exists("/dev/kfd"):
+        # misaligned q / state (only where no GPU could run the launch if
+        # the check were missing)
+        assert gdn(8, 16, 16, 16, 16, 32, 16, 2, 2, 4, 64, 64, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
+        assert b"aligned" in lib.moe_last_error()
+        assert gdn(16, 16, 16, 16, 16, 40, 16, 2, 2, 4, 64, 64, 1.0, 1e-6, None) == _lib.MOE_E_INVAL
 
 
 def test_file_store_round_trip_without_gpu(tmp_path):
