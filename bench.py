@@ -65,7 +65,7 @@ TRAFFIC = {
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
     # profiles/gdn80b_step.md
-    "gdn80b": ("gdn", 66969, 132112, "093ab1a820bc01f7"),
+    "gdn80b": ("gdn", 66969, 132116, "51877f82619402ae"),
 }
 # bench.py --calibrate-stream on one MI355X: GB/s when a workload's per-layer
 # algorithmic bytes are streamed once per phase with 3 dependent all-to-all
