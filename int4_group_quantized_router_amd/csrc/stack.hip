@@ -489,9 +489,6 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     // selects; waves 1..7 compute the shared expert's gate/up meanwhile.
     __shared__ int s_abort;
     if (wave == 0) {
-      // wave 0's chain (logits, top-k, weights) ends the phase; the shared
-      // gate/up of the other waves has slack, so wave 0 issues first
-      __builtin_amdgcn_s_setprio(3);
       const uint64_t* lb = a.lbuf + ((size_t)l * kRep + rep) * (E + 1);
       float v[VPL], vs = 0.f;
       uint32_t key[VPL];
@@ -554,7 +551,6 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
       }
       if (lane == 0) s_abort = timed_out ? 1 : 0;
-      __builtin_amdgcn_s_setprio(0);
       STACK_PHASE(14);  // wave 0: weights written, at the barrier
     } else {
       uint4 gq[S::NPS][2][CPL];
