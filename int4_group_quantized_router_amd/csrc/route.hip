@@ -363,9 +363,15 @@ __global__ __launch_bounds__(THR) void route_kernel(RouteArgs a) {
   __shared__ float s_val[NT * MOE_MAX_TOPK];
   __shared__ int s_slot[NT * MOE_MAX_TOPK];
   __shared__ int s_first[1024];
+  __shared__ float s_sraw[NT];
+  // the shared gate's inputs x . wsg are requested together with the
+  // logits (one round trip to the coherence point, not two)
+  const bool gate = a.sigma && a.wsg && (int)threadIdx.x < a.T;
+  const float sraw = gate ? ld_dev(a.sigma + threadIdx.x) : 0.f;
   topk_tokens<VPL, NW>(a, 0, a.T, s_sel, s_val, nullptr);
+  if (gate) s_sraw[threadIdx.x] = sraw;
   __syncthreads();
-  write_weights<THR>(a, 0, a.T, s_sel, s_val, nullptr);
+  write_weights<THR>(a, 0, a.T, s_sel, s_val, a.sigma && a.wsg ? s_sraw : nullptr);
   if (a.n_slots) build_slots<THR>(a, s_sel, s_first, s_slot);
 }
 
