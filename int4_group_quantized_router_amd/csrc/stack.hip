@@ -91,11 +91,18 @@ __device__ __forceinline__ uint64_t pack64(float v, uint32_t tag) {
   return (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
 }
 
-// WG-uniform end of one poll round: true when every thread saw all its
-// words, false to poll again; *timed_out when the deadline has passed.
-__device__ __forceinline__ bool poll_round(bool ok, int64_t deadline, bool* timed_out) {
-  if (__syncthreads_and(ok)) return true;
-  *timed_out = __syncthreads_or(threadIdx.x == 0 && wall_clock64() > deadline) != 0;
+// Polls run per wave: each polling wave loops on its own until all of its
+// lanes' words carry the call's tag (no workgroup barrier per round, so a
+// wave whose words are in stops polling and the round trip of one wave
+// does not wait for the slowest), then one barrier joins the workgroup and
+// makes the result uniform.  One round of a wave: true when all its lanes
+// are done; *timed_out (wave-uniform) once the deadline has passed.
+__device__ __forceinline__ bool wave_round(bool ok, int64_t deadline, bool* timed_out) {
+  if (__ballot(!ok) == 0ull) return true;
+  if (wall_clock64() > deadline) {
+    *timed_out = true;
+    return true;
+  }
   __builtin_amdgcn_s_sleep(1);
   return false;
 }
@@ -109,14 +116,14 @@ template <int H>
 __device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t deadline) {
   constexpr int M = H / 256;
   const int t = (int)threadIdx.x - kYT0;
-  uint32_t done = 0;
-  for (;;) {
-    uint64_t e[M];
+  bool to = false;
+  if (t >= 0) {  // waves 4..7
+    uint32_t done = 0;
+    for (;;) {
+      uint64_t e[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
-      e[m] = (t >= 0 && !((done >> m) & 1u)) ? ld_dev(buf + t + m * 256) : 0ull;
-    bool ok = true;
-    if (t >= 0) {
+      for (int m = 0; m < M; ++m) e[m] = !((done >> m) & 1u) ? ld_dev(buf + t + m * 256) : 0ull;
+      bool ok = true;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         if (!((done >> m) & 1u)) {
@@ -128,11 +135,10 @@ __device__ bool poll_y(const uint64_t* buf, uint32_t tag, float* yv, int64_t dea
           }
         }
       }
+      if (wave_round(ok, deadline, &to)) break;
     }
-    bool to = false;
-    if (poll_round(ok, deadline, &to)) return true;
-    if (to) return false;
   }
+  return !__syncthreads_or(to);
 }
 
 // Pairs [FIRST, FIRST + COUNT) of this layer's h words (dense: slot j < k
@@ -162,28 +168,31 @@ __device__ bool poll_h(const uint64_t* src, uint32_t tag16, uint32_t* hl, int64_
                        uint64_t (&e)[h_per<N, COUNT>()]) {
   constexpr int PER = h_per<N, COUNT>();
   static_assert(PER <= 32, "h pairs per thread");
+  static_assert(T0 % 64 == 0 && N % 64 == 0, "h pollers are whole waves");
   const int t = (int)threadIdx.x - T0;
-  uint32_t done = 0;
-  for (;;) {
-    bool ok = true;
+  bool to = false;
+  if (t >= 0 && t < N) {  // whole waves (T0 and N are multiples of 64)
+    uint32_t done = 0;
+    for (;;) {
+      bool ok = true;
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int i = t + m * N;
-      if (t >= 0 && t < N && i < COUNT && !((done >> m) & 1u)) {
-        const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
-        if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
-          hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
-          done |= 1u << m;
-        } else {
-          ok = false;
+      for (int m = 0; m < PER; ++m) {
+        const int i = t + m * N;
+        if (i < COUNT && !((done >> m) & 1u)) {
+          const uint32_t w0 = (uint32_t)e[m], w1 = (uint32_t)(e[m] >> 32);
+          if ((w0 & 0xFFFFu) == tag16 && (w1 & 0xFFFFu) == tag16) {
+            hl[FIRST + i] = perm(w1, w0, 0x07060302u);  // (bf16 of w0, bf16 of w1)
+            done |= 1u << m;
+          } else {
+            ok = false;
+          }
         }
       }
+      if (wave_round(ok, deadline, &to)) break;
+      h_request<T0, N, FIRST, COUNT>(src, done, e);
     }
-    bool to = false;
-    if (poll_round(ok, deadline, &to)) return true;
-    if (to) return false;
-    h_request<T0, N, FIRST, COUNT>(src, done, e);
   }
+  return !__syncthreads_or(to);
 }
 
 // Division of the down-phase work between the waves of a workgroup.  A
