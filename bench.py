@@ -59,9 +59,9 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
-    "decode80b_int8": ("stack", 976376, 79900, "1899706188163318"),
+    "decode80b_int8": ("stack", 975473, 79900, "a0c0f64a0952765c"),
     # profiles/decode35b_stack_decode_kernel.md
-    "decode35b": ("stack", 362595, 53786, "1899706188163318"),
+    "decode35b": ("stack", 361640, 53786, "a0c0f64a0952765c"),
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
     # profiles/gdn80b_step.md
@@ -72,7 +72,7 @@ TRAFFIC = {
 # hand-offs per phase (the stack kernel's count per layer) -- the ceiling a
 # batch-1 decode layer of that size reaches on this device
 # (profiles/decode_layer_ceiling.md).
-CEILING_3HANDOFFS_GBPS = {"decode80b_int8": 3048.0, "decode80b": 2197.0, "decode35b": 1962.0}
+CEILING_3HANDOFFS_GBPS = {"decode80b_int8": 3141.0, "decode80b": 2306.0, "decode35b": 1993.0}
 
 
 def kernel_digest(kind):

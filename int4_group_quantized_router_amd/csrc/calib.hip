@@ -8,7 +8,8 @@
 // (16-byte loads, every load of a workgroup in flight at once) and then
 // `handoffs` dependent all-to-all exchanges through tagged words, exactly
 // as the stack kernel exchanges y, logits and h (value and call tag in one
-// write-through store, 8 copies, one per XCD; coherent polls).  Its time
+// write-through store, 8 copies, one per XCD; coherent polls, each polling
+// wave on its own, one workgroup barrier after the wait).  Its time
 // per phase is what streaming that many bytes plus that many hand-offs
 // costs on this device.
 #include "device.h"
@@ -62,21 +63,32 @@ __global__ __launch_bounds__(kCT, 1) void stream_phases_kernel(const uint4* buf,
       __syncthreads();
       if (tid < kCRep)
         st_dev(w + (size_t)tid * kCG + blk, (uint64_t)acc | ((uint64_t)tag << 32));
+      // waves 0..3 poll one word per lane, each wave on its own until all
+      // of its words are in; one barrier joins the workgroup
       const uint64_t* mine = w + (size_t)rep * kCG;
       uint32_t got = 0;
-      for (;;) {
-        bool ok = true;
-        if (tid < kCG) {
-          const uint64_t e = ld_dev(mine + tid);
-          if ((uint32_t)(e >> 32) == tag) got = (uint32_t)e;
-          else ok = false;
+      bool to = false;
+      if (tid < kCG) {
+        bool have = false;
+        for (;;) {
+          if (!have) {
+            const uint64_t e = ld_dev(mine + tid);
+            if ((uint32_t)(e >> 32) == tag) {
+              got = (uint32_t)e;
+              have = true;
+            }
+          }
+          if (__ballot(!have) == 0ull) break;
+          if (wall_clock64() > deadline) {
+            to = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        if (__syncthreads_and(ok)) break;
-        if (__syncthreads_or(tid == 0 && wall_clock64() > deadline)) {
-          failed = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
+      }
+      if (__syncthreads_or(to)) {
+        failed = true;
+        break;
       }
       acc += got;
     }
