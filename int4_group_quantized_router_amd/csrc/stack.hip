@@ -738,11 +738,15 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
     __syncthreads();
     STACK_PHASE(6);  // shared h received
     wait_vm_n<0>();  // this wave's down-item loads have landed
+    // 8-bit split: the routed h's first poll round (waves 0..3) is in
+    // flight while the shared rows are computed (measured faster there;
+    // with every wave polling, the 4-bit shapes were slower with it)
+    uint64_t hrt[h_per<RO::HN, K * I / 2>()];
+    if constexpr (RO::SPLIT) h_request<RO::HT0, RO::HN, 0, K * I / 2>(hrep, 0u, hrt);
     chunk_sums(K * I / F::kEpc, S::HW / F::kEpc);
     __syncthreads();
     down_items(true);
-    uint64_t hrt[h_per<RO::HN, K * I / 2>()];
-    h_request<RO::HT0, RO::HN, 0, K * I / 2>(hrep, 0u, hrt);
+    if constexpr (!RO::SPLIT) h_request<RO::HT0, RO::HN, 0, K * I / 2>(hrep, 0u, hrt);
     if (!poll_h<RO::HT0, RO::HN, 0, K * I / 2>(hrep, tag16, hl, deadline, hrt)) {
       failed = true;
         l_fail = l;
