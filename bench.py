@@ -59,9 +59,9 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
-    "decode80b_int8": ("stack", 975473, 79900, "a0c0f64a0952765c"),
+    "decode80b_int8": ("stack", 974362, 79900, "e21841fb98a568a3"),
     # profiles/decode35b_stack_decode_kernel.md
-    "decode35b": ("stack", 361640, 53786, "a0c0f64a0952765c"),
+    "decode35b": ("stack", 361664, 53786, "e21841fb98a568a3"),
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
     # profiles/gdn80b_step.md
