@@ -375,7 +375,7 @@ def bench_phases(args, cfg):
     # counted from the start of that phase
     sub = {3: {"logits wait (wave 0)": since(10, 3),
                "top-k selection (wave 0)": since(11, 10),
-               "wave 0 at the barrier (weights written)": since(14, 3),
+               "wave 0 at the barrier (choices written)": since(14, 3),
                "wave 1 at the barrier (shared gate/up published)": since(13, 3),
                "wave 4 at the barrier (shared down requested)": since(12, 3)},
            5: {"wave 0 has polled the shared h": since(17, 5)},

@@ -271,6 +271,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
   __shared__ int s_sel[MOE_MAX_TOPK];
   __shared__ float s_val[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK + 1];
+  __shared__ float s_gate_in;  // the shared gate's logit, for its sigmoid
   __shared__ int tmp_e[kWave];
   __shared__ float tmp_v[kWave];
   __shared__ uint32_t tmp_k[kWave];
@@ -540,18 +541,10 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
         wave_topk<VPL>(v, key, K, tmp_e, tmp_v, tmp_k, s_sel, s_val);
         STACK_PHASE(11);  // wave 0: top-k selected
-        // renormalised weights = softmax over the chosen logits, summed in j order
-        const float ex = lane < K ? expf(s_val[lane] - s_val[0]) : 0.f;
-        float sum = 0.f;
-#pragma unroll
-        for (int j = 0; j < K; ++j) sum += readlane_f32(ex, j);
-        if (lane < K) {
-          const float wj = ex / sum;
-          s_w[lane] = wj;
-          if (blk == 0 && a.w) a.w[(size_t)l * K + lane] = wj;
-          if (blk == 0 && a.idx) a.idx[(size_t)l * K + lane] = s_sel[lane];
-        }
-        if (lane == 0) s_w[K] = a.has_wsg ? 1.0f / (1.0f + expf(-vs)) : 0.f;
+        // the choices go out now (the host acquires a stopped layer's);
+        // their weights are formed once the routed loads are in flight
+        if (blk == 0 && a.idx && lane < K) a.idx[(size_t)l * K + lane] = s_sel[lane];
+        if (lane == 0) s_gate_in = vs;
         if (POOL) {  // pool mode: the chosen blobs, if all resident
           const uint8_t* addr = lane < K ? D.res_row[s_sel[lane]] : nullptr;
           if (lane < K) s_addr[lane] = addr;
@@ -560,7 +553,7 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
         }
       }
       if (lane == 0) s_abort = timed_out ? 1 : 0;
-      STACK_PHASE(14);  // wave 0: weights written, at the barrier
+      STACK_PHASE(14);  // wave 0: choices written, at the barrier
     } else {
       uint4 gq[S::NPS][2][CPL];
       uint32_t gsb[S::NPS][2][CPL];
@@ -631,6 +624,20 @@ __global__ __launch_bounds__(kNT, 1) void stack_decode_kernel(StackArgs a) {
       };
 #pragma unroll
       for (int n = 0; n < DEPTH; ++n) routed_load(n);
+      if (wave == 0) {
+        // renormalised weights = softmax over the chosen logits, summed in j
+        // order, and the shared gate (used by wave 0's combine at the end)
+        const float ex = lane < K ? expf(s_val[lane] - s_val[0]) : 0.f;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) sum += readlane_f32(ex, j);
+        if (lane < K) {
+          const float wj = ex / sum;
+          s_w[lane] = wj;
+          if (blk == 0 && a.w) a.w[(size_t)l * K + lane] = wj;
+        }
+        if (lane == 0) s_w[K] = a.has_wsg ? 1.0f / (1.0f + expf(-s_gate_in)) : 0.f;
+      }
 #pragma unroll
       for (int n = 0; n < S::NPR; ++n) {
         const int pr = gw + n * kNW * kG;
