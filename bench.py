@@ -59,9 +59,9 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
-    "decode80b_int8": ("stack", 974362, 79900, "e21841fb98a568a3"),
+    "decode80b_int8": ("stack", 974333, 79900, "5c31e0b40da3ec54"),
     # profiles/decode35b_stack_decode_kernel.md
-    "decode35b": ("stack", 361664, 53786, "e21841fb98a568a3"),
+    "decode35b": ("stack", 361725, 53786, "5c31e0b40da3ec54"),
     # profiles/prefill80b_grouped_gemm.md
     "prefill80b": ("prefill_gu", 615324, 45056, "ac867dac804f6665"),
     # profiles/gdn80b_step.md
