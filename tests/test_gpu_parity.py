@@ -1290,6 +1290,30 @@ def test_gdn_step_matches_oracle(torch, name, B, T):
     assert rel_err(S.cpu().numpy(), S_free) <= T * GDN_STEP_TOL
 
 
+@pytest.mark.parametrize("Hk,Hv,dk", [(8, 8, 128), (1, 8, 128), (3, 12, 64)])
+def test_gdn_step_head_grouping(torch, Hk, Hv, dk):
+    """Value heads over key heads at other ratios than the workloads' 2:
+    one key head per value head, one key head for all, and 3 key heads for
+    12 value heads (64x64 heads); 3 steps from the GPU's own state, each
+    within one step's bound of the oracle."""
+    import int4_group_quantized_router_amd as m
+    B, T = 5, 3
+    d = gdn_inputs(11, B, Hk, Hv, dk, dk, T)
+    _print("gdn grouping", Hk, Hv, dk)
+    scale = dk ** -0.5
+    S = torch.from_numpy(d["S0"].copy()).cuda()
+    for t in range(T):
+        S_prev = S.cpu().numpy().astype(np.float64)
+        q, k, v = (torch.from_numpy(d[x][t].view(np.int16)).cuda() for x in ("q", "k", "v"))
+        al, be = (torch.from_numpy(d[x][t]).cuda() for x in ("alpha", "beta"))
+        o = m.moe_gdn_step(q, k, v, al, be, S, scale=scale, eps=1e-6)
+        torch.cuda.synchronize()
+        S_ref, o_ref = G.gdn_step_bf16(S_prev, d["q"][t], d["k"][t], d["v"][t], d["alpha"][t],
+                                       d["beta"][t], scale, 1e-6)
+        assert rel_err(S.cpu().numpy(), S_ref) <= GDN_STEP_TOL, t
+        assert rel_err(o.cpu().numpy(), o_ref) <= GDN_STEP_TOL, t
+
+
 def test_gdn_step_exact_cases(torch):
     """beta = 0, and a zero key with eps > 0, write nothing: the new state is
     exactly f32(alpha * S) (one rounding, as the kernel forms it), and the
