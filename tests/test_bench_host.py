@@ -25,3 +25,35 @@ def test_traffic_withheld_for_other_shapes_and_kernels():
     assert bench.counter_traffic(cut.name, "stack", stock=cut == stock) is None
     assert bench.counter_traffic("decode80b_int8", "prefill_gu") is None
     assert bench.counter_traffic("no_such_workload", "stack") is None
+
+
+def test_bench_refuses_several_gpus():
+    """The bench runs on one GPU; asked for more it says so and exits 2
+    before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_match_the_blob_layout():
+    """The roofline's per-layer byte counts: the quantised expert bytes are
+    (k + 1) whole expert blobs as the library lays them out, and the layer
+    adds the f32 router rows (E x H, plus bias, the shared gate row and the
+    input) and the activations; pinned to the figures the profiles quote."""
+    import int4_group_quantized_router_amd as m
+    want_layer = {"decode80b_int8": 41_017_344, "decode80b": 23_715_840, "decode35b": 18_074_624}
+    for name, layer_bytes in want_layer.items():
+        cfg = CONFIGS[name]
+        ab = bench.algorithmic_bytes(cfg)
+        blob = m.moe_blob_layout_get(cfg.hidden, cfg.inter, cfg.bits)["bytes"]
+        assert cfg.shared_inter == cfg.inter
+        assert ab["expert_quantized"] == (cfg.top_k + 1) * blob
+        router = cfg.experts * cfg.hidden * 4 + cfg.experts * 4 + 2 * cfg.hidden * 4
+        assert ab["route"] == router
+        assert ab["layer"] - ab["expert_quantized"] - router < 64 * 1024  # activations
+        assert ab["layer"] == layer_bytes
