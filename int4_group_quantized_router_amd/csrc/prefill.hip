@@ -453,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void prefill_segsort_kernel(PrefillArgs a
 // * (scale, bias) words, 16 bytes (four groups) of every weight row per
 //   instruction, two-slot ring; when K is not a multiple of 256 one word per
 //   row and group instead, three-slot ring.
-// The loads of group g + 2 (int8 weights: g + 1) are in flight while group g
-// computes.  Each lane dequantises its own weights to bf16 (s * q + b, round
+// The A rows of group g + 2 and the weights of group g + 2 or beyond are in
+// flight while group g computes.  Each lane dequantises its own weights to bf16 (s * q + b, round
 // to nearest even) right before the MFMA step that uses them, overlapping
 // the matrix core's previous step.  No weight is dequantised twice within a
 // tile.
@@ -482,24 +482,10 @@ struct BRaw {  // one K group of packed weights for the lane's two weight rows
 
 // (lds_addr, dma16, dma4 and wait_vm_n: device.h.)  The loop below waits
 // for its direct-to-LDS loads itself.
-// wait until at most n of this wave's loads are outstanding (n <= 15)
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: wait_vm_n<0>(); break;
-    case 1: wait_vm_n<1>(); break;
-    case 2: wait_vm_n<2>(); break;
-    case 3: wait_vm_n<3>(); break;
-    case 4: wait_vm_n<4>(); break;
-    case 5: wait_vm_n<5>(); break;
-    case 6: wait_vm_n<6>(); break;
-    case 7: wait_vm_n<7>(); break;
-    case 8: wait_vm_n<8>(); break;
-    case 9: wait_vm_n<9>(); break;
-    case 10: wait_vm_n<10>(); break;
-    case 11: wait_vm_n<11>(); break;
-    case 12: wait_vm_n<12>(); break;
-    default: wait_vm_n<0>(); break;
-  }
+// wait until at most N of this wave's LDS operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_lgkm_n() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -529,7 +515,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = lane >> 5, l32 = lane & 31;
   // gate/up waves whose 32 columns lie past a small intermediate size load
-  // (clamped rows) but do not compute
+  // clamped rows and compute on them like the others, but store nothing
   const bool wave_live = !GU || c0 + 32 * wave < inner;
   const uint32_t lds0 = lds_addr(smem);
 
@@ -666,126 +652,162 @@ __global__ __launch_bounds__(kGemmThreads, 2) void grouped_gemm_kernel(PrefillAr
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  // One K group, operands from the LDS rings.  MFMA step s runs on
-  // operands prepared during step s-1 (A fragments read from LDS, B
-  // dequantised in registers); the scheduler is told to interleave each of
-  // the step's MFMAs with a share of the next step's dequantisation, so the
-  // VALU works while the matrix core does.  During the last step the lane
-  // reads the next group's packed weights (its own loads: a wait on its own
-  // counter, no barrier) and dequantises their step 0, so every step has
-  // VALU work and no group starts with an idle matrix core.  r / b0: the
-  // group's packed weights and step-0 operands on entry, the next group's on
-  // exit.  NRB (row blocks with any live row) is a compile-time count.
-  auto compute = [&](auto nrb_c, int kg, R& r, uint4* b0, int next_wait)
-                     __attribute__((always_inline)) {
-    constexpr int NRB = decltype(nrb_c)::value;
-    const uint8_t* st = smem + (kg % 3) * kAStage;
-    uint4 af[2][NRB], bo[2][2];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) af[0][rb] = a_frag(st, rb, 0);
-    bo[0][0] = b0[0];
-    bo[0][1] = b0[1];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int cur = s4 & 1, nxt = cur ^ 1;
-      if (s4 == 3 && next_wait >= 0 && next_wait < 16) wait_vm(next_wait);
-      __builtin_amdgcn_sched_barrier(0);
-      if (s4 < 3) {
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) af[nxt][rb] = a_frag(st, rb, s4 + 1);
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        acc[rb][0] = mfma(af[cur][rb], bo[cur][0], acc[rb][0]);
-        acc[rb][1] = mfma(af[cur][rb], bo[cur][1], acc[rb][1]);
-      }
-      if (s4 < 3 || next_wait >= 0) {
-        if (s4 < 3) {
-          bo[nxt][0] = b_operand(r, 0, s4 + 1);
-          bo[nxt][1] = b_operand(r, 1, s4 + 1);
-        } else {
-          r = read_b(kg + 1);
-          b0[0] = b_operand(r, 0, 0);
-          b0[1] = b_operand(r, 1, 0);
-        }
-        // LDS reads first, then one MFMA per share of the dequant VALU ops
-        if (s4 < 3)
-          __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
-        else
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NQ + 2, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * NRB; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, BITS == 4 ? 48 / (2 * NRB) : 40 / (2 * NRB), 0);
-        }
-      }
+  // The K pipeline.  Barrier point j opens group j: past it the A rows of
+  // group j are in LDS for every wave, and no wave reads group j - 1's A slot
+  // any more.  At point j each wave refills the ring slots whose last reader
+  // is done:
+  //   A rows of group j + 2, into group j - 1's slot;
+  //   int4, odd j: the weight slice of groups j + 3 and j + 4, into the
+  //   slice of groups j - 1 and j (both already read into registers);
+  //   int8: the weights of group j + 2, into group j's slot (already read);
+  //   (scale, bias) words, four groups per load: at j = 3 mod 4 the block
+  //   from group j + 5, into the block of groups j - 3 .. j; one word per
+  //   group: group j + 3.
+  // Point 0 sits in the prologue and point j + 1 in step 3 of group j, after
+  // that step's first MFMAs, so the matrix core works through the barrier.
+  // Group j + 1's packed weights are read into registers during step 2 of
+  // group j, after the wave waits for every load it issued up to point
+  // j - 1 (which also covers group j + 1's A rows); group j + 1's first A
+  // fragments are read right after point j + 1.  Every load is waited for
+  // before the wave exits.
+  const int nslice = (NK + C::GPC - 1) / C::GPC;
+  const int nsb = SB4 ? NK / 4 : NK;
+  auto issue_at = [&](int j) __attribute__((always_inline)) -> int {
+    int n = 0;
+    if (j + 2 < NK) {
+      issue_a(j + 2);
+      n += C::kAOps;
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (C::GPC == 2) {
+      if ((j & 1) && (j + 3) / 2 < nslice) {
+        issue_b((j + 3) / 2);
+        n += C::kBOps;
+      }
+    } else if (j + 2 < nslice) {
+      issue_b(j + 2);
+      n += C::kBOps;
+    }
+    if (SB4) {
+      if ((j & 3) == 3 && (j + 5) / 4 < nsb) {
+        issue_sb((j + 5) / 4);
+        n += 1;
+      }
+    } else if (j + 3 < NK) {
+      issue_sb(j + 3);
+      n += 1;
+    }
+    return n;
   };
 
-  // The K pipeline.  Group kg issues, right after the barrier that opens it
-  // (every wave has finished the previous group, so the ring slots being
-  // refilled are free): its B slice if kg starts a slice (the next slice),
-  // A of group kg + 2, and the (scale, bias) words ahead.  Before the
-  // barrier each wave waits until its own loads that group kg needs have
-  // landed: all but the ones issued during group kg - 1 (int8 weights: all
-  // but group kg - 1's A and (scale, bias) loads); group kg's packed
-  // weights and (scale, bias) words were already read during group kg - 1,
-  // after a wait for the wave's own loads issued since that slice.
   auto run = [&](auto nrb_c) __attribute__((always_inline)) {
-    constexpr int SBG = SB4 ? 4 : 1;  // groups per (scale, bias) load
-    const int nslice = (NK + C::GPC - 1) / C::GPC;
-    const int nsb = (NK + SBG - 1) / SBG;
-    issue_b(0);
+    constexpr int NRB = decltype(nrb_c)::value;
     issue_a(0);
-    issue_sb(0);
     if (NK > 1) issue_a(1);
-    if (!SB4 && NK > 1) issue_sb(1);
-    int younger = 0;  // loads issued during the previous group that group kg may skip
-    int since_b = 0;  // loads issued after the most recent B slice
-    R r;
-    uint4 b0[2];
-    for (int kg = 0; kg < NK; ++kg) {
-      wait_vm(younger);
-      barrier();
-      int nb = 0, na = 0, ns = 0;
-      if (kg % C::GPC == 0 && kg / C::GPC + 1 < nslice) {
-        issue_b(kg / C::GPC + 1);
-        nb = C::kBOps;
-        since_b = 0;
-      }
-      if (kg + 2 < NK) {
-        issue_a(kg + 2);
-        na = C::kAOps;
-      }
-      if (SB4) {
-        if (kg % 4 == 0 && kg / 4 + 1 < nsb) {
-          issue_sb(kg / 4 + 1);
-          ns = 1;
-        }
-      } else if (kg + 2 < NK) {
-        issue_sb(kg + 2);
-        ns = 1;
-      }
-      since_b += na + ns;
-      // group kg + 1 needs this group's B slice when a slice is one group
-      younger = C::GPC == 1 ? na + ns : nb + na + ns;
-      if (kg == 0) {  // nothing carried in: the first group reads its own weights
-        r = read_b(0);
-        b0[0] = b_operand(r, 0, 0);
-        b0[1] = b_operand(r, 1, 0);
-      }
-      // wait before reading group kg + 1's weights: for its B slice when
-      // kg + 1 starts one (the newest slice; else it is this group's,
-      // complete), for its (scale, bias) word when one is loaded per group
-      // (issued during group kg - 1, before everything issued during kg)
-      int next_wait = -1;  // -1: no next group; 16: read without waiting
-      if (kg + 1 < NK) {
-        next_wait = (kg + 1) % C::GPC == 0 ? since_b : 16;
-        if (!SB4) next_wait = min(next_wait, nb + na + ns);
-      }
-      if (wave_live) compute(nrb_c, kg, r, b0, next_wait);
+    issue_b(0);
+    if (nslice > 1) issue_b(1);
+    issue_sb(0);
+    if (SB4) {
+      if (nsb > 1) issue_sb(1);
+    } else {
+      if (NK > 1) issue_sb(1);
+      if (NK > 2) issue_sb(2);
     }
+    wait_vm_n<0>();
+    R r = read_b(0);
+    wait_lgkm_n<0>();  // point 0 may refill the slots just read
+    barrier();
+    int n_cur = issue_at(0);  // loads issued at the point that opened the current group
+    uint4 af[2][NRB], bo[2][2];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) af[0][rb] = a_frag(smem, rb, 0);
+    bo[0][0] = b_operand(r, 0, 0);
+    bo[0][1] = b_operand(r, 1, 0);
+
+    // One K group.  MFMA step s runs on operands prepared during step s - 1
+    // (A fragments read from LDS, B dequantised in registers); the scheduler
+    // is told to interleave each MFMA with a share of the next step's
+    // dequantisation.  P = kg mod 4 fixes how many loads the point that
+    // opened the group issued away from the ends of K, so every wait below
+    // is a constant (near the ends: a full wait).
+    auto group = [&](auto p_c, int kg) __attribute__((always_inline)) {
+      constexpr int P = decltype(p_c)::value;
+      constexpr int NS = C::kAOps + ((C::GPC == 1 || (P & 1)) ? C::kBOps : 0) +
+                         (SB4 ? (P == 3 ? 1 : 0) : 1);
+      const uint8_t* st = smem + (kg % 3) * kAStage;
+      const uint8_t* st1 = smem + ((kg + 1) % 3) * kAStage;
+      const bool more = kg + 1 < NK;
+      R rn;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int cur = s4 & 1, nxt = cur ^ 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (s4 < 3) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) af[nxt][rb] = a_frag(st, rb, s4 + 1);
+        }
+        if (s4 == 2 && more) {
+          if (n_cur == NS)
+            wait_vm_n<NS>();
+          else
+            wait_vm_n<0>();
+          rn = read_b(kg + 1);
+        }
+        if (s4 < 3) {
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            acc[rb][0] = mfma(af[cur][rb], bo[cur][0], acc[rb][0]);
+            acc[rb][1] = mfma(af[cur][rb], bo[cur][1], acc[rb][1]);
+          }
+          bo[nxt][0] = b_operand(r, 0, s4 + 1);
+          bo[nxt][1] = b_operand(r, 1, s4 + 1);
+          // LDS reads first, then one MFMA per share of the dequant VALU ops
+          if (s4 == 2)
+            __builtin_amdgcn_sched_group_barrier(0x100, NRB + 2 * C::NQ + 2, 0);
+          else
+            __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * NRB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, BITS == 4 ? 48 / (2 * NRB) : 40 / (2 * NRB), 0);
+          }
+        } else {
+          acc[0][0] = mfma(af[cur][0], bo[cur][0], acc[0][0]);
+          acc[0][1] = mfma(af[cur][0], bo[cur][1], acc[0][1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) {
+            wait_lgkm_n<0>();  // this wave's reads of group kg's A slot are done
+            barrier();
+            n_cur = issue_at(kg + 1);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) af[nxt][rb] = a_frag(st1, rb, 0);
+          }
+#pragma unroll
+          for (int rb = 1; rb < NRB; ++rb) {
+            acc[rb][0] = mfma(af[cur][rb], bo[cur][0], acc[rb][0]);
+            acc[rb][1] = mfma(af[cur][rb], bo[cur][1], acc[rb][1]);
+          }
+          if (more) {
+            bo[nxt][0] = b_operand(rn, 0, 0);
+            bo[nxt][1] = b_operand(rn, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * NRB - 2; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 48 / 4, 0);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) r = rn;
+    };
+    for (int k0 = 0; k0 < NK; k0 += 4) {
+      group(std::integral_constant<int, 0>{}, k0);
+      if (k0 + 1 < NK) group(std::integral_constant<int, 1>{}, k0 + 1);
+      if (k0 + 2 < NK) group(std::integral_constant<int, 2>{}, k0 + 2);
+      if (k0 + 3 < NK) group(std::integral_constant<int, 3>{}, k0 + 3);
+    }
+    wait_vm_n<0>();
   };
   static_assert(BM == 96, "row-block dispatch below");
   switch (nrb) {
