@@ -126,8 +126,9 @@ __global__ __launch_bounds__(kThreads) void split_router_kernel(const float* Wr,
 // groups: part[split][t][e] = sum over the slice of x[t] . (hi + mid + lo)[e].
 // Each 64-wide K step is staged in LDS (x rows and the three planes' rows,
 // 16-byte pieces, 8 threads per 128-byte row segment so every load
-// instruction reads whole segments), double buffered, the next step's loads
-// in flight during this step's MFMAs.  Four waves, each 64 tokens x 64
+// instruction reads whole segments), one stage per workgroup so two
+// workgroups share a CU; the next step's loads are in flight in registers
+// during this step's MFMAs and go to LDS once every wave has read the stage.  Four waves, each 64 tokens x 64
 // experts (2 x 2 MFMA 32x32x16 tiles).  Per step the products go to a fresh
 // accumulator that is then added to the running total, so every f32 sum has
 // a bounded depth.  Tokens / experts past the end read a valid row and are
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void split_router_kernel(const float* Wr,
 constexpr int RT = 128;
 constexpr int kRouterStage = 4 * RT * kLdsRow;  // x rows + three planes: 73,728 bytes
 
-__global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t* x, int T, int H,
+__global__ __launch_bounds__(kThreads, 2) void router_gemm_kernel(const uint16_t* x, int T, int H,
                                                                   const uint16_t* wr3, int E,
                                                                   int n_et, int ks, float* part) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -168,8 +169,8 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t
 #pragma unroll
       for (int i = 0; i < 4; ++i) rw[p][i] = ld16v(wr3 + p * plane + g * KG + boff[i]);
   };
-  auto store = [&](int buf) __attribute__((always_inline)) {
-    uint8_t* st = smem + buf * kRouterStage + sdst;
+  auto store = [&]() __attribute__((always_inline)) {
+    uint8_t* st = smem + sdst;
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_v*>(st + 32 * i * kLdsRow) = ra[i];
 #pragma unroll
@@ -185,12 +186,11 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t
 #pragma unroll
     for (int j = 0; j < 2; ++j) tot[i][j] = f32x16_t{};
   load(g0);
-  store(0);
+  store();
   __syncthreads();
   for (int i = 0; i < nk; ++i) {
-    const int buf = i & 1;
     if (i + 1 < nk) load(g0 + i + 1);
-    const uint8_t* st = smem + buf * kRouterStage + kh * 64;
+    const uint8_t* st = smem + kh * 64;
     f32x16_t acc[2][2];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -219,8 +219,11 @@ __global__ __launch_bounds__(kThreads, 1) void router_gemm_kernel(const uint16_t
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int c = 0; c < 2; ++c) tot[r][c] += acc[r][c];
-    if (i + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+    if (i + 1 < nk) {
+      __syncthreads();  // every wave has read the stage
+      store();
+      __syncthreads();
+    }
   }
   float* out = part + (size_t)sp * T * E;
 #pragma unroll
@@ -890,7 +893,7 @@ int pad8(int n) { return (n + 7) / 8 * 8; }
 int router_splits(int T, int E, int H) {
   const int tiles = (T + RT - 1) / RT * ((E + RT - 1) / RT);
   int ks = 1;
-  while (2 * ks <= kRouterMaxSplits && 2 * ks <= H / KG && tiles * ks < 256) ks *= 2;
+  while (2 * ks <= kRouterMaxSplits && 2 * ks <= H / KG && tiles * ks < 512) ks *= 2;
   return ks;
 }
 
@@ -907,7 +910,7 @@ hipError_t launch_router_gemm(const uint16_t* x, int T, int H, const uint16_t* w
     return hipErrorInvalidValue;
   const int ks = router_splits(T, E, H);
   const int n_et = (E + RT - 1) / RT;
-  const size_t lds = 2 * (size_t)kRouterStage;
+  const size_t lds = kRouterStage;
   hipError_t e = allow_lds(router_gemm_kernel, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(router_gemm_kernel, dim3(pad8((T + RT - 1) / RT) * n_et * ks), dim3(kThreads),
