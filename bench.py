@@ -63,7 +63,7 @@ TRAFFIC = {
     # profiles/decode35b_stack_decode_kernel.md
     "decode35b": ("stack", 361725, 53786, "5c31e0b40da3ec54"),
     # profiles/prefill80b_grouped_gemm.md
-    "prefill80b": ("prefill_gu", 581572, 45056, "fff7c862ed782cc3"),
+    "prefill80b": ("prefill_gu", 581651, 45056, "387468d250a9d31b"),
     # profiles/gdn80b_step.md
     "gdn80b": ("gdn", 66969, 132116, "51877f82619402ae"),
 }
