@@ -1087,6 +1087,17 @@ def test_prefill_shared_inter_differs(torch):
     dm.destroy()
 
 
+@pytest.mark.parametrize("name", ["prefill80b", "decode80b_int8"])
+def test_prefill_down_per_group_scales_deep_k(torch, name):
+    """Routed intermediate 512 (eight K groups in the down GEMM) with a
+    shared intermediate of 128, which is not a multiple of 256: the down
+    launch loads one (scale, bias) word per group, so its K pipeline runs
+    that layout's steady state (int4 and int8) as well as its ends."""
+    cfg = CONFIGS[name].replace(layers=1, experts=64, top_k=4, shared_inter=128, zipf=None)
+    dm, *_ = _prefill_case(torch, cfg, 150)
+    dm.destroy()
+
+
 def test_prefill_int8_small_inter(torch):
     """int8 weights with K = 128 for down (not a multiple of 256)."""
     cfg = CONFIGS["decode80b_int8"].replace(layers=1, hidden=256, experts=32, top_k=4,
