@@ -282,6 +282,10 @@ def main():
                          "OS cache)")
     ap.add_argument("--store-path", default=None,
                     help="file for --store file (default: $TMPDIR or /tmp, removed afterwards)")
+    ap.add_argument("--pool-sweep", default=None, metavar="FRACS",
+                    help="stream80b: run the same tokens at each pool size in FRACS (comma-"
+                         "separated shares of the L x E experts) over one pinned store and "
+                         "print tokens/s, hit rate, misses and evictions per size")
     ap.add_argument("--layers", type=int, default=None,
                     help="stream80b / decode80b_int8: build only this many layers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -321,6 +325,8 @@ def main():
     if cfg.batch > 8:
         return bench_prefill(args, cfg)
     if not cfg.resident:
+        if args.pool_sweep:
+            return bench_pool_sweep(args, cfg, [float(f) for f in args.pool_sweep.split(",")])
         return bench_stream(args, cfg)
     if args.phases:
         return bench_phases(args, cfg)
@@ -600,6 +606,72 @@ def _run_tokens(m, stack, X, Y, T, warmup, steps, after_warmup=None):
         m.moe_stack_forward(stack, X[i * T:(i + 1) * T], y_last=Y[i * T:(i + 1) * T], stream=stream)
     torch.cuda.synchronize()
     return time.perf_counter() - t0
+
+
+def bench_pool_sweep(args, cfg, fracs):
+    """Batch-1 streaming decode at several pool sizes over one pinned store:
+    per size a fresh (empty) pool of floor(frac * L * E) slots, the same
+    warm-up and timed tokens, and its tokens/s, warm hit rate, misses,
+    evictions and host-to-HBM rate.  The pages report that on their machine
+    the cache size barely moves the speed (the SSD absorbs the misses); here
+    a miss is a copy over the host link."""
+    import numpy as np
+    import torch
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as W
+    from moe_inputs import expert_arrays, tokens_x
+    warmup = min(64, cfg.tokens) if args.warmup is None else args.warmup
+    steps = cfg.tokens - warmup if args.steps is None else args.steps
+    torch.cuda.set_device(0)
+    dims = {"hidden": cfg.hidden, "experts": cfg.experts, "inter": cfg.inter, "bits": cfg.bits}
+    log(f"[bench] filling the pinned store: {cfg.layers} layers x {cfg.experts} experts")
+    store, stride = W.fill_store(dims, cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    n = warmup + steps
+    X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
+    Y_ref, rows = None, []
+    for f in fracs:
+        cap = int(f * cfg.layers * cfg.experts)
+        if cap < cfg.top_k:
+            raise SystemExit(f"pool share {f} gives {cap} slots, fewer than top-k {cfg.top_k}")
+        pool = m.slotpool_create(store, cap, 0)
+        layers, stack, keep = _build_stack(cfg, pool=pool)
+        Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
+        snap = {}
+        dt = _run_tokens(m, stack, X, Y, 1, warmup, steps,
+                         after_warmup=lambda: snap.update(m.slotpool_get_stats(pool)))
+        s1 = m.slotpool_get_stats(pool)
+        d = {k: s1[k] - snap[k] for k in s1}
+        acc = d["hits"] + d["misses"]
+        # every pool size must give the same outputs, bit for bit
+        same = True if Y_ref is None else bool(torch.equal(Y, Y_ref))
+        Y_ref = Y if Y_ref is None else Y_ref
+        row = {"pool_frac": f, "slots": cap, "tokens_per_s": steps / dt,
+               "ms_per_token": dt / steps * 1e3, "hit_rate": d["hits"] / max(acc, 1),
+               "misses": d["misses"], "evictions": d["evictions"],
+               "misses_per_token": d["misses"] / steps,
+               "h2d_GBps": d["bytes_h2d"] / dt / 1e9, "outputs_equal_first_size": same}
+        rows.append(row)
+        log(f"[bench] pool {f:.3f} ({cap} slots): {row['tokens_per_s']:.1f} tok/s, hit rate "
+            f"{row['hit_rate']:.4f}, {d['misses']} misses, {d['evictions']} evictions over "
+            f"{steps} tokens, {row['h2d_GBps']:.2f} GB/s host->HBM, outputs equal: {same}")
+        m.moe_stack_destroy(stack)
+        for L in layers:
+            m.moe_layer_destroy(L)
+        m.slotpool_destroy(pool)
+        del keep
+    m.expert_store_destroy(store)
+    out = {"metric": "MoE stack tokens/sec against HBM pool size, batch-1 decode with expert "
+                     "streaming, 1 GPU",
+           "value": rows[-1]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": rows[-1]["ms_per_token"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None,
+           "dtype": f"int{cfg.bits} weights, f32 accumulate, bf16 I/O",
+           "data": "synthetic (seeded; random-init weights of the stated shape)",
+           "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden "
+                                  f"{cfg.hidden}, {cfg.experts} experts top-{cfg.top_k}, "
+                                  f"int{cfg.bits}; value = the last pool size",
+                      "sweep": rows}}
+    print(json.dumps(out), flush=True)
 
 
 def bench_stream(args, cfg):
