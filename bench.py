@@ -286,6 +286,10 @@ def main():
                     help="stream80b: run the same tokens at each pool size in FRACS (comma-"
                          "separated shares of the L x E experts) over one pinned store and "
                          "print tokens/s, hit rate, misses and evictions per size")
+    ap.add_argument("--prefetch-bias", type=int, default=0, metavar="N",
+                    help="stream80b: before the first token, prefetch each layer's N experts "
+                         "of highest router bias into the empty pool (slotpool_prefetch: free "
+                         "slots only, not an access)")
     ap.add_argument("--layers", type=int, default=None,
                     help="stream80b / decode80b_int8: build only this many layers")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -608,6 +612,25 @@ def _run_tokens(m, stack, X, Y, T, warmup, steps, after_warmup=None):
     return time.perf_counter() - t0
 
 
+def prefetch_by_bias(m, pool, cfg, n):
+    """slotpool_prefetch of each layer's n experts of highest router bias
+    (the Zipf skew of the routing lives in the bias); returns (experts
+    loaded, seconds including the copies)."""
+    import numpy as np
+    import torch
+    from moe_inputs import router_arrays
+    if n <= 0:
+        return 0, 0.0
+    t0 = time.perf_counter()
+    loaded = 0
+    for l in range(cfg.layers):
+        _, rb, _ = router_arrays(cfg, l)
+        order = np.argsort(-rb, kind="stable")[:n]
+        loaded += m.slotpool_prefetch(pool, l, order)
+    torch.cuda.synchronize()
+    return loaded, time.perf_counter() - t0
+
+
 def bench_pool_sweep(args, cfg, fracs):
     """Batch-1 streaming decode at several pool sizes over one pinned store:
     per size a fresh (empty) pool of floor(frac * L * E) slots, the same
@@ -635,6 +658,7 @@ def bench_pool_sweep(args, cfg, fracs):
             raise SystemExit(f"pool share {f} gives {cap} slots, fewer than top-k {cfg.top_k}")
         pool = m.slotpool_create(store, cap, 0)
         layers, stack, keep = _build_stack(cfg, pool=pool)
+        pre, _ = prefetch_by_bias(m, pool, cfg, args.prefetch_bias)
         Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
         snap = {}
         dt = _run_tokens(m, stack, X, Y, 1, warmup, steps,
@@ -649,7 +673,8 @@ def bench_pool_sweep(args, cfg, fracs):
                "ms_per_token": dt / steps * 1e3, "hit_rate": d["hits"] / max(acc, 1),
                "misses": d["misses"], "evictions": d["evictions"],
                "misses_per_token": d["misses"] / steps,
-               "h2d_GBps": d["bytes_h2d"] / dt / 1e9, "outputs_equal_first_size": same}
+               "h2d_GBps": d["bytes_h2d"] / dt / 1e9, "prefetched": pre,
+               "outputs_equal_first_size": same}
         rows.append(row)
         log(f"[bench] pool {f:.3f} ({cap} slots): {row['tokens_per_s']:.1f} tok/s, hit rate "
             f"{row['hit_rate']:.4f}, {d['misses']} misses, {d['evictions']} evictions over "
@@ -669,7 +694,10 @@ def bench_pool_sweep(args, cfg, fracs):
            "data": "synthetic (seeded; random-init weights of the stated shape)",
            "config": {"workload": f"{cfg.name}: {cfg.layers} stacked MoE layers, hidden "
                                   f"{cfg.hidden}, {cfg.experts} experts top-{cfg.top_k}, "
-                                  f"int{cfg.bits}; value = the last pool size",
+                                  f"int{cfg.bits}; value = the last pool size"
+                                  + (f"; each pool first given its {args.prefetch_bias} experts "
+                                     f"per layer of highest router bias"
+                                     if args.prefetch_bias else ""),
                       "sweep": rows}}
     print(json.dumps(out), flush=True)
 
@@ -703,6 +731,10 @@ def bench_stream(args, cfg):
     pool = m.slotpool_create(store, cap, 0)
     layers, stack, keep = _build_stack(cfg, pool=pool)
     log(f"[bench] built in {time.perf_counter() - t_b:.1f} s; pool {cap} slots x {stride} B")
+    pre, pre_s = prefetch_by_bias(m, pool, cfg, args.prefetch_bias)
+    if args.prefetch_bias:
+        log(f"[bench] prefetched {pre} experts ({args.prefetch_bias} per layer of highest router "
+            f"bias) in {pre_s:.2f} s")
     n = warmup + steps
     X = torch.from_numpy(tokens_x(cfg, 0, n).view(np.int16)).cuda()
     Y = torch.empty((n, cfg.hidden), dtype=torch.int16, device="cuda")
@@ -754,6 +786,14 @@ def bench_stream(args, cfg):
                       "flushed_rerun_tokens": nchk,
                       "flushed_rerun_misses": s2["misses"] - sf["misses"],
                       "flushed_rerun_bitwise_equal": same}}
+    if args.prefetch_bias:
+        out["metric"] = out["metric"].replace("(30% HBM pool)",
+                                              "(30% HBM pool, prefetched by router bias)")
+        out["config"]["workload"] = out["config"]["workload"].replace(
+            "pool starts empty", f"pool starts with each layer's {args.prefetch_bias} experts "
+                                 "of highest router bias, prefetched")
+        out["config"]["prefetched"] = pre
+        out["config"]["prefetch_s"] = pre_s
     if path:
         out["metric"] = out["metric"].replace("expert streaming", "expert streaming from a file")
         out["config"]["store"] = m.STORE_KINDS[m.expert_store_kind(store)]

@@ -282,6 +282,8 @@ typedef struct slotpool_counters {
   int64_t bytes_h2d;
   int64_t bytes_read;  /* file store: bytes read from the file */
   int64_t read_ns;     /* file store: host time spent in those reads */
+  int64_t prefetched;  /* experts loaded by slotpool_prefetch (their copies
+                          count in bytes_h2d) */
 } slotpool_counters;
 
 /* capacity: number of slots (>= 1); device: HIP device ordinal.  Allocates
@@ -304,6 +306,18 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts,
  * for the previous release. */
 int32_t slotpool_release(slotpool* pool, int32_t layer, const int32_t* experts,
                          int32_t n, hipStream_t compute);
+/* Speculative load of experts[0..n) of `layer` ([lens] "結論" names expert
+ * prefetching as open room; the rule is this library's): in list order,
+ * each expert not resident is loaded into a free slot; a prefetch never
+ * evicts and stops at the first expert that finds no free slot.  It is not
+ * an access: no tick, hit or miss is counted; a loaded expert is unpinned,
+ * with use count 0 and the current tick, so one never used afterwards is
+ * the first eviction victim.  Outputs of later calls do not change, only
+ * which of their accesses hit.  `compute` is made to wait for the copies
+ * (as for slotpool_acquire).  loaded (out, nullable): experts loaded.
+ * MOE_E_RANGE for an expert or layer outside the store. */
+int32_t slotpool_prefetch(slotpool* pool, int32_t layer, const int32_t* experts,
+                          int32_t n, hipStream_t compute, int32_t* loaded);
 /* Drop (layer, expert) if resident.  MOE_E_BUSY if pinned. */
 int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert);
 /* Drop every resident expert (next accesses all miss); MOE_E_BUSY if any

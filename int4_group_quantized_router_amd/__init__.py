@@ -272,6 +272,16 @@ def slotpool_acquire(pool, layer: int, experts, stream=None):
     return [ptrs[i] for i in range(n)], [bool(m) for m in miss[:n]]
 
 
+def slotpool_prefetch(pool, layer: int, experts, stream=None) -> int:
+    """Loads the listed experts not resident into free slots (no eviction,
+    not an access); returns how many were loaded."""
+    ex = np.ascontiguousarray(experts, dtype=np.int32)
+    loaded = C.c_int32(0)
+    _check(_lib_().slotpool_prefetch(_h(pool), layer, ex.ctypes.data, ex.size, _stream(stream),
+                                      C.byref(loaded)), "slotpool_prefetch")
+    return loaded.value
+
+
 def slotpool_release(pool, layer: int, experts, stream=None) -> None:
     ex = np.ascontiguousarray(experts, dtype=np.int32)
     _check(_lib_().slotpool_release(_h(pool), layer, ex.ctypes.data, ex.size, _stream(stream)),
@@ -290,14 +300,16 @@ def slotpool_stats(pool) -> dict:
     st = PoolStats()
     _check(_lib_().slotpool_stats(_h(pool), C.byref(st)), "slotpool_stats")
     return {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
-            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns}
+            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns,
+            "prefetched": st.prefetched}
 
 
 def slotpool_get_stats(pool) -> dict:
     st = PoolStats()
     _check(_lib_().slotpool_get_stats(_h(pool), C.byref(st)), "slotpool_get_stats")
     return {"hits": st.hits, "misses": st.misses, "evictions": st.evictions,
-            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns}
+            "bytes_h2d": st.bytes_h2d, "bytes_read": st.bytes_read, "read_ns": st.read_ns,
+            "prefetched": st.prefetched}
 
 
 def slotpool_slot_of(pool, layer: int, expert: int) -> int:

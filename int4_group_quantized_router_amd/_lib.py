@@ -50,7 +50,8 @@ class QMatrixHost(C.Structure):
 class PoolStats(C.Structure):
     _fields_ = [("hits", C.c_int64), ("misses", C.c_int64),
                 ("evictions", C.c_int64), ("bytes_h2d", C.c_int64),
-                ("bytes_read", C.c_int64), ("read_ns", C.c_int64)]
+                ("bytes_read", C.c_int64), ("read_ns", C.c_int64),
+                ("prefetched", C.c_int64)]
 
 
 class LayerCfg(C.Structure):
@@ -84,6 +85,7 @@ SIGNATURES = {
     "slotpool_create": [_P, _I64, _I32, C.POINTER(_P)],
     "slotpool_acquire": [_P, _I32, _P, _I32, _P, _P, _P],
     "slotpool_release": [_P, _I32, _P, _I32, _P],
+    "slotpool_prefetch": [_P, _I32, _P, _I32, _P, C.POINTER(_I32)],
     "slotpool_evict": [_P, _I32, _I32],
     "slotpool_flush": [_P],
     "slotpool_stats": [_P, C.POINTER(PoolStats)],

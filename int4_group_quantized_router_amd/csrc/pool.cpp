@@ -530,8 +530,12 @@ int32_t slotpool_create(const expert_store* store, int64_t capacity, int32_t dev
 
 namespace {
 
+// prefetch: load only the experts not resident, into free slots, unpinned,
+// count 0, without advancing the tick; stop at the first that finds no free
+// slot (slot_ptrs and was_miss unused; *loaded counts the loads)
 int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
-                     hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss) {
+                     hipStream_t compute, const void** slot_ptrs, uint8_t* was_miss,
+                     bool prefetch = false, int32_t* loaded = nullptr) {
   for (int i = 0; i < n; ++i) {
     int32_t st = check_le(pool->store, layer, experts[i]);
     if (st != MOE_OK) return st;
@@ -618,8 +622,13 @@ int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int3
   for (int i = 0; i < n; ++i) {
     const int32_t e = experts[i];
     const int64_t k = pool->key(layer, e);
-    ++pool->tick;
     auto it = pool->where.find(k);
+    if (prefetch) {
+      if (it != pool->where.end()) continue;
+      if (pool->free_slots.empty()) break;
+    } else {
+      ++pool->tick;
+    }
     int32_t s;
     bool miss = false;
     if (it != pool->where.end()) {
@@ -660,13 +669,19 @@ int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int3
       Slot& x = pool->slots[s];
       x.layer = layer;
       x.expert = e;
-      x.count = 1;
+      x.count = prefetch ? 0 : 1;
       x.last = pool->tick;
-      x.pins = 1;
+      x.pins = prefetch ? 0 : 1;
       pool->where[k] = s;
       pool->tab_host[k] = pool->dev + (int64_t)s * stride;
       pool->tab_changed.push_back(k);
-      pool->stats.misses += 1;
+      if (prefetch) {
+        pool->victims.insert(pool->vkey(s));
+        pool->stats.prefetched += 1;
+        if (loaded) *loaded += 1;
+      } else {
+        pool->stats.misses += 1;
+      }
       miss = true;
       if (pool->store->base) {
         const int32_t st = fill(s, pool->store->base + k * stride, -1);
@@ -685,6 +700,7 @@ int32_t acquire_impl(slotpool* pool, int32_t layer, const int32_t* experts, int3
         pend.emplace_back(s, k, si);
       }
     }
+    if (prefetch) continue;
     pinned.push_back(s);
     slot_ptrs[i] = pool->dev + (int64_t)s * stride;
     if (was_miss) was_miss[i] = miss ? 1 : 0;
@@ -712,6 +728,21 @@ int32_t slotpool_acquire(slotpool* pool, int32_t layer, const int32_t* experts, 
   const int32_t st = acquire_impl(pool, layer, experts, n, compute, slot_ptrs, was_miss);
   // the table follows every admission and eviction of the call, also on
   // the error paths (entries dropped there are cleared)
+  const int32_t pt = push_table(pool, compute);
+  return st != MOE_OK ? st : pt;
+}
+
+int32_t slotpool_prefetch(slotpool* pool, int32_t layer, const int32_t* experts, int32_t n,
+                          hipStream_t compute, int32_t* loaded) {
+  clear_error();
+  MOE_REQUIRE(pool && (n == 0 || experts) && n >= 0, "bad argument");
+  if (loaded) *loaded = 0;
+  MOE_POOL_APPLY(pool);
+  for (int i = 0; i < n; ++i) {
+    const int32_t st = check_le(pool->store, layer, experts[i]);
+    if (st != MOE_OK) return st;
+  }
+  const int32_t st = acquire_impl(pool, layer, experts, n, compute, nullptr, nullptr, true, loaded);
   const int32_t pt = push_table(pool, compute);
   return st != MOE_OK ? st : pt;
 }

@@ -19,6 +19,14 @@ GPU library's pool:
   unpinned slot is "pool exhausted" (experts admitted earlier in the same
   call stay resident and unpinned).
 
+Prefetch (not in the pages, which name prefetching as open room: [lens]
+"結論"; this library's own rule): experts are loaded in the given order into
+free slots only -- a prefetch never evicts and stops at the first expert
+that finds no free slot; it is not an access (no tick, no hit or miss); a
+loaded expert enters unpinned with use count 0 and the current tick, so an
+expert prefetched and never used is the first victim.  Its copies count in
+bytes_h2d like a miss's.
+
 The policy affects which accesses hit, never the layer's output.
 """
 
@@ -46,7 +54,7 @@ class PoolReplay:
         self.last = {}         # key -> tick of the last use
         self.pins = {}         # key -> pin count
         self.tick = 0
-        self.hits = self.misses = self.evictions = 0
+        self.hits = self.misses = self.evictions = self.prefetched = 0
 
     # -- queries
     def resident(self, layer: int, expert: int) -> bool:
@@ -54,8 +62,8 @@ class PoolReplay:
 
     def stats(self) -> dict:
         return {"hits": self.hits, "misses": self.misses,
-                "evictions": self.evictions,
-                "bytes_h2d": self.misses * self.stride}
+                "evictions": self.evictions, "prefetched": self.prefetched,
+                "bytes_h2d": (self.misses + self.prefetched) * self.stride}
 
     # -- operations
     def _victim(self):
@@ -105,6 +113,23 @@ class PoolReplay:
             self.pins[key] = self.pins.get(key, 0) + 1
             pinned_now.append(key)
         return out
+
+    def prefetch(self, layer: int, experts) -> int:
+        """Load the experts not yet resident, in order, into free slots;
+        returns how many were loaded."""
+        loaded = 0
+        for e in experts:
+            key = (int(layer), int(e))
+            if key in self.slot_of:
+                continue
+            if not self.free:
+                break
+            self.slot_of[key] = heapq.heappop(self.free)
+            self.count[key] = 0
+            self.last[key] = self.tick
+            loaded += 1
+        self.prefetched += loaded
+        return loaded
 
     def release(self, layer: int, experts):
         for e in experts:

@@ -9,9 +9,10 @@
 //   file PATH L E STRIDE CAPACITY   the same store as a container file
 //   A l e1 e2 ...              acquire  -> "A ok s1 m1 s2 m2 ..." | "A err CODE"
 //   R l e1 e2 ...              release  -> "R ok" | "R err CODE"
+//   H l e1 e2 ...              prefetch -> "H ok LOADED" | "H err CODE"
 //   E l e                      evict    -> "E ok" | "E err CODE"
 //   F                          flush    -> "F ok" | "F err CODE"
-//   S                          counters -> "S hits misses evictions bytes_h2d copies"
+//   S                          counters -> "S hits misses evictions prefetched bytes_h2d copies"
 //   X l e                      slot     -> "X slot" (-1: not resident)
 //   C l e                      slot bytes equal the store's blob -> "C 1" | "C 0"
 //   P s                        slot s holds only 0xFF bytes -> "P 1" | "P 0"
@@ -61,6 +62,15 @@ int main() {
       st = slotpool_create(store, cap, 0, &pool);
       std::printf("%s %s\n", op.c_str(), st == MOE_OK ? "ok" : "err");
       if (st != MOE_OK) return 1;
+    } else if (op == "H") {
+      int l, e;
+      in >> l;
+      std::vector<int32_t> ex;
+      while (in >> e) ex.push_back(e);
+      int32_t loaded = -1;
+      const int32_t st = slotpool_prefetch(pool, l, ex.data(), (int32_t)ex.size(), nullptr, &loaded);
+      if (st == MOE_OK) std::printf("H ok %d\n", loaded);
+      else std::printf("H err %d\n", st);
     } else if (op == "A" || op == "R") {
       int l;
       in >> l;
@@ -107,8 +117,8 @@ int main() {
     } else if (op == "S") {
       slotpool_counters c{};
       slotpool_stats(pool, &c);
-      std::printf("S %lld %lld %lld %lld %lld\n", (long long)c.hits, (long long)c.misses,
-                  (long long)c.evictions, (long long)c.bytes_h2d,
+      std::printf("S %lld %lld %lld %lld %lld %lld\n", (long long)c.hits, (long long)c.misses,
+                  (long long)c.evictions, (long long)c.prefetched, (long long)c.bytes_h2d,
                   fake_hip_copies_of((size_t)stride));
     } else if (op == "X") {
       int l, e;

@@ -687,6 +687,79 @@ def test_pool_matches_resident_bitwise_and_replay(torch):
         m.expert_store_destroy(store)
 
 
+def test_pool_prefetch_is_output_neutral(torch):
+    """Experts prefetched by router-bias rank (12 per layer) into an empty
+    pool before the first token: the pooled stack's outputs and exports stay
+    bitwise the resident stack's, the pool's hits, misses, evictions, loads
+    and the slot of every expert equal the oracle's replay of the prefetch
+    and the accesses, and accesses hit prefetched experts."""
+    import int4_group_quantized_router_amd as m
+    from int4_group_quantized_router_amd import weights as Wt
+    from oracle.pool_replay import PoolReplay
+    from harness import dims_of
+    cfg = CONFIGS["stream80b"].replace(layers=3)
+    _print("pool prefetch", cfg.name)
+    dm = DeviceModel(cfg)
+    store, stride = Wt.fill_store(dims_of(cfg), cfg.layers, lambda l, e: expert_arrays(cfg, l, e))
+    cap = 40
+    pool = m.slotpool_create(store, cap, 0)
+    res_layers = dm.make_layers()
+    pool_layers = dm.make_layers(pool=pool)
+    s_res, s_pool = m.moe_stack_create(res_layers), m.moe_stack_create(pool_layers)
+    H, k, L = cfg.hidden, cfg.top_k, cfg.layers
+    replay = PoolReplay(cap, stride)
+    try:
+        fresh = set()  # prefetched and not accessed yet
+        for l in range(L):
+            _, rb, _ = router_arrays(cfg, l)
+            order = np.argsort(-rb, kind="stable")[:12].tolist()
+            n = m.slotpool_prefetch(pool, l, order)
+            assert n == replay.prefetch(l, order) == 12
+            fresh |= {(l, e) for e in order}
+        # a full pool loads nothing and evicts nothing
+        spare = [e for e in range(cfg.experts) if not replay.resident(0, e)][:cap]
+        n = m.slotpool_prefetch(pool, 0, spare)
+        assert n == replay.prefetch(0, spare) == cap - 3 * 12
+        assert m.slotpool_prefetch(pool, 1, spare) == replay.prefetch(1, spare) == 0
+        fresh |= {(0, e) for e in spare[:cap - 36]}
+        hits_on_prefetched = 0
+        for tok in range(8):
+            x0 = torch.from_numpy(token_x(cfg, tok).view(np.int16)).cuda().view(1, H)
+            outs = []
+            for st in (s_res, s_pool):
+                yl = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
+                idx = torch.empty((L, 1, k), dtype=torch.int32, device="cuda")
+                y = m.moe_stack_forward(st, x0, y_layers=yl, idx=idx)
+                torch.cuda.synchronize()
+                outs.append((y.cpu().numpy(), yl.cpu().numpy(), idx.cpu().numpy()))
+            assert np.array_equal(outs[0][0], outs[1][0]), tok
+            assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32)), tok
+            assert np.array_equal(outs[0][2], outs[1][2]), tok
+            for l in range(L):
+                ex = outs[1][2][l, 0].tolist()
+                for e in ex:
+                    if (l, e) in fresh and replay.resident(l, e):
+                        hits_on_prefetched += 1
+                    fresh.discard((l, e))
+                replay.acquire(l, ex)
+                replay.release(l, ex)
+        stats = m.slotpool_get_stats(pool)
+        assert {k_: stats[k_] for k_ in replay.stats()} == replay.stats(), (stats, replay.stats())
+        assert stats["prefetched"] == cap and stats["evictions"] > 0, stats
+        assert hits_on_prefetched > 0
+        for l in range(L):
+            for e in range(cfg.experts):
+                want = replay.slot_of[(l, e)] if replay.resident(l, e) else -1
+                assert m.slotpool_slot_of(pool, l, e) == want
+        _print("prefetch hits", hits_on_prefetched, "stats", stats)
+    finally:
+        m.moe_stack_destroy(s_res)
+        m.moe_stack_destroy(s_pool)
+        dm.destroy()
+        m.slotpool_destroy(pool)
+        m.expert_store_destroy(store)
+
+
 @pytest.mark.parametrize("cap", [24, 44])
 def test_pool_stack_persistent_equals_per_layer(torch, cap):
     """A pooled stack run through the persistent kernel (stopping at the first

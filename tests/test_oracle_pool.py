@@ -96,3 +96,24 @@ def test_lowest_free_slot_is_used():
     p.evict(0, 12)
     p.evict(0, 10)
     assert _use(p, 0, [20, 21]) == [(0, True), (2, True)]
+
+
+def test_prefetch_fills_free_slots_only_and_unused_loads_go_first():
+    """Hand-worked: a prefetch loads into free slots in list order without
+    advancing the tick or counting a hit or miss; it never evicts; a loaded
+    expert has use count 0, so one never used is the next victim."""
+    p = PoolReplay(3, stride=10)
+    assert p.prefetch(0, [5, 6]) == 2                     # slots 0 and 1
+    assert p.tick == 0 and p.hits == 0 and p.misses == 0
+    assert p.slot_of == {(0, 5): 0, (0, 6): 1}
+    assert p.acquire(0, [6, 7]) == [(1, False), (2, True)]  # a hit on a prefetched expert
+    p.release(0, [6, 7])
+    assert p.prefetch(0, [8]) == 0                        # full: nothing evicted
+    assert (0, 8) not in p.slot_of and p.evictions == 0
+    # victims by (count, last tick): (0,5) (0, 0) < (0,6) (1, 1) < (0,7) (1, 2)
+    assert p.acquire(1, [1]) == [(0, True)]
+    assert (0, 5) not in p.slot_of and p.evictions == 1
+    p.release(1, [1])
+    assert p.prefetch(1, [1, 2]) == 0                     # resident, then no free slot
+    assert p.stats() == {"hits": 1, "misses": 2, "evictions": 1, "prefetched": 2,
+                         "bytes_h2d": 40}

@@ -78,6 +78,12 @@ def random_trace(seed, L, E, cap, n_ops, k_max):
                 held.append((layer, ex))
             except PoolExhausted:
                 want.append(f"A err {E_EXHAUSTED}")
+        elif r < 0.62:
+            # prefetch a few experts, some of them maybe resident
+            layer = int(rng.integers(0, L))
+            ex = rng.choice(E, size=int(rng.integers(1, min(E, 6) + 1)), replace=False).tolist()
+            script.append("H %d %s" % (layer, " ".join(map(str, ex))))
+            want.append(f"H ok {rep.prefetch(layer, ex)}")
         elif r < 0.85:
             layer, ex = held.pop(int(rng.integers(0, len(held))))
             script.append("R %d %s" % (layer, " ".join(map(str, ex))))
@@ -107,8 +113,8 @@ def random_trace(seed, L, E, cap, n_ops, k_max):
         if rng.random() < 0.1:
             st = rep.stats()
             script.append("S")
-            want.append(f"S {st['hits']} {st['misses']} {st['evictions']} {st['bytes_h2d']} "
-                        f"{st['misses']}")  # one copy per miss
+            want.append(f"S {st['hits']} {st['misses']} {st['evictions']} {st['prefetched']} "
+                        f"{st['bytes_h2d']} {st['misses'] + st['prefetched']}")  # one copy per load
         if rng.random() < 0.1 and rep.slot_of:
             keys = sorted(rep.slot_of)
             l, e = keys[int(rng.integers(0, len(keys)))]
@@ -121,7 +127,8 @@ def random_trace(seed, L, E, cap, n_ops, k_max):
             want.append(f"X {rep.slot_of.get((l, e), -1)}")
     st = rep.stats()
     script.append("S")
-    want.append(f"S {st['hits']} {st['misses']} {st['evictions']} {st['bytes_h2d']} {st['misses']}")
+    want.append(f"S {st['hits']} {st['misses']} {st['evictions']} {st['prefetched']} "
+                f"{st['bytes_h2d']} {st['misses'] + st['prefetched']}")
     return stride, script, want
 
 
@@ -130,9 +137,10 @@ def random_trace(seed, L, E, cap, n_ops, k_max):
                                                 (2, 4, 32, 40, 10), (3, 1, 6, 6, 6)])
 def test_pool_code_matches_oracle_replay(drivers, build, seed, L, E, cap, k_max):
     """Hits, misses, slots, evictions, exhaustion (every slot pinned), busy
-    evict and flush, counters, one copy per miss, slot bytes equal the
-    store's after each fill: the pool's C++ code and the replay agree on
-    every operation of a random 400-operation script."""
+    evict and flush, prefetches (free slots only, count 0, no tick),
+    counters, one copy per load, slot bytes equal the store's after each
+    fill: the pool's C++ code and the replay agree on every operation of a
+    random 400-operation script."""
     stride, script, want = random_trace(seed, L, E, cap, 400, k_max)
     got = run(drivers[build], [f"init {L} {E} {stride} {cap}"] + script)
     assert got[0] == "init ok"
