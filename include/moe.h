@@ -323,7 +323,8 @@ int32_t slotpool_evict(slotpool* pool, int32_t layer, int32_t expert);
 /* Drop every resident expert (next accesses all miss); MOE_E_BUSY if any
  * slot is pinned.  Counters are kept. */
 int32_t slotpool_flush(slotpool* pool);
-/* The pool's counters (hits, misses, evictions, bytes copied and read). */
+/* The pool's counters (hits, misses, evictions, prefetched experts, bytes
+ * copied and read). */
 int32_t slotpool_stats(const slotpool* pool, slotpool_counters* out);
 /* The same as slotpool_stats (earlier name). */
 int32_t slotpool_get_stats(const slotpool* pool, slotpool_counters* out);
