@@ -124,15 +124,27 @@ __device__ void topk_tokens(const RouteArgs& a, int t0, int t1, int* s_sel, floa
     float v[VPL];
     uint32_t key[VPL];
     if (a.part) {
-      // partial sums of the MFMA router (earlier launch): slices in order, then rb
+      // partial sums of the MFMA router (earlier launch): every load in
+      // flight at once, then the slices added in order, then rb
+      float pv[VPL][kRouterMaxSplits], bv[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = lane + kWave * i;
+#pragma unroll
+        for (int sp = 0; sp < kRouterMaxSplits; ++sp)
+          pv[i][sp] = e < E && sp < a.ksplit ? a.part[((size_t)sp * a.T + t) * E + e] : 0.f;
+        bv[i] = e < E && a.rb ? a.rb[e] : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
         const int e = lane + kWave * i;
         float s = 0.f;
         if (e < E) {
-          s = a.part[(size_t)t * E + e];
-          for (int sp = 1; sp < a.ksplit; ++sp) s += a.part[((size_t)sp * a.T + t) * E + e];
-          s += a.rb ? a.rb[e] : 0.f;
+          s = pv[i][0];
+#pragma unroll
+          for (int sp = 1; sp < kRouterMaxSplits; ++sp)
+            if (sp < a.ksplit) s += pv[i][sp];
+          s += bv[i];
           if (a.logits) a.logits[(size_t)t * E + e] = s;
         }
         v[i] = s;
