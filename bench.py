@@ -63,7 +63,7 @@ TRAFFIC = {
     # profiles/decode35b_stack_decode_kernel.md
     "decode35b": ("stack", 361725, 53786, "5c31e0b40da3ec54"),
     # profiles/prefill80b_grouped_gemm.md
-    "prefill80b": ("prefill_gu", 581651, 45056, "387468d250a9d31b"),
+    "prefill80b": ("prefill_gu", 582346, 45056, "9b1c1bde315c56d6"),
     # profiles/gdn80b_step.md
     "gdn80b": ("gdn", 66969, 132116, "51877f82619402ae"),
 }

@@ -861,18 +861,23 @@ __global__ __launch_bounds__(kThreads) void prefill_combine_kernel(PrefillArgs a
   }
   const float sg = a.sigma[t];
   for (int c = threadIdx.x * 4; c < H; c += kThreads * 4) {
+    // every row's load in flight first, then the sum in j order
+    float4 vr[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      vr[j] = j < k ? *reinterpret_cast<const float4*>(a.yd + (size_t)rows[j] * H + c)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 v = *reinterpret_cast<const float4*>(a.yd + (size_t)shared_row * H + c);
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k) {
-        const float4 v = *reinterpret_cast<const float4*>(a.yd + (size_t)rows[j] * H + c);
-        y.x = fmaf(wj[j], v.x, y.x);
-        y.y = fmaf(wj[j], v.y, y.y);
-        y.z = fmaf(wj[j], v.z, y.z);
-        y.w = fmaf(wj[j], v.w, y.w);
+        y.x = fmaf(wj[j], vr[j].x, y.x);
+        y.y = fmaf(wj[j], vr[j].y, y.y);
+        y.z = fmaf(wj[j], vr[j].z, y.z);
+        y.w = fmaf(wj[j], vr[j].w, y.w);
       }
     }
-    const float4 v = *reinterpret_cast<const float4*>(a.yd + (size_t)shared_row * H + c);
     y.x = fmaf(sg, v.x, y.x);
     y.y = fmaf(sg, v.y, y.y);
     y.z = fmaf(sg, v.z, y.z);
