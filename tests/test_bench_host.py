@@ -57,3 +57,31 @@ def test_algorithmic_bytes_match_the_blob_layout():
         assert ab["route"] == router
         assert ab["layer"] - ab["expert_quantized"] - router < 64 * 1024  # activations
         assert ab["layer"] == layer_bytes
+
+
+def test_prefetch_by_bias_takes_each_layers_highest_router_bias(monkeypatch):
+    """The streaming bench's prefetch asks the pool, layer by layer, for the
+    n experts of highest router bias, highest first, and adds up what the
+    pool reports loaded."""
+    import numpy as np
+    import torch
+    from moe_inputs import router_arrays
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    calls = []
+
+    class Pool:
+        @staticmethod
+        def slotpool_prefetch(pool, layer, experts, stream=None):
+            calls.append((layer, [int(e) for e in experts]))
+            return len(experts) - 1
+
+    cfg = CONFIGS["stream80b"].replace(layers=3)
+    loaded, _ = bench.prefetch_by_bias(Pool, None, cfg, 5)
+    assert loaded == 3 * 4
+    assert [layer for layer, _ in calls] == [0, 1, 2]
+    for layer, ex in calls:
+        _, rb, _ = router_arrays(cfg, layer)
+        assert len(set(ex)) == 5
+        assert rb[ex].min() >= np.delete(rb, ex).max()
+        assert list(rb[ex]) == sorted(rb[ex], reverse=True)
+    assert bench.prefetch_by_bias(Pool, None, cfg, 0) == (0, 0.0)
