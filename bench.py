@@ -60,6 +60,8 @@ TRAFFIC = {
     # workload: (kernel, fetch KiB, write KiB, source digest)
     # profiles/decode80b_int8_stack_decode_kernel.md
     "decode80b_int8": ("stack", 974333, 79900, "5c31e0b40da3ec54"),
+    # profiles/decode80b_stack_decode_kernel.md
+    "decode80b": ("stack", 568405, 79900, "5c31e0b40da3ec54"),
     # profiles/decode35b_stack_decode_kernel.md
     "decode35b": ("stack", 361725, 53786, "5c31e0b40da3ec54"),
     # profiles/prefill80b_grouped_gemm.md
